@@ -1,0 +1,172 @@
+"""Benchmark of the routed-expert MoE layer (prompt ingestion) on one MI355X.
+
+Workload: 2,048 tokens x 512 experts x top-10, hidden 2048, expert intermediate 512, T1
+experts (~1.78 bits/weight), bf16 activations, seeded synthetic inputs (the reference pages
+measure one layer of a real model file, which is not available here; the synthetic layer has
+the same shapes and ~40 pairs per expert).
+
+A step is one rl_moe_prefill call (grouping, fused dequant + gate/up + SwiGLU, fused dequant +
+down, ordered combine) over the resident inputs.  Weight sets rotate over several arena
+copies at different addresses so that every step reads its weights from HBM rather than from
+the 256 MB Infinity Cache.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA (256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="t1_2048")
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--rotate", type=int, default=3, help="distinct arena copies cycled through")
+    ap.add_argument("--no-oracle", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--oracle-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the single-GPU hot path only: run it with --gpus 1 (one process, one GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import routed_experts_bit_amd as rl
+    from workload import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    wl = make_workload(args.config, seed=args.seed)
+    ex0 = wl.experts
+    T, k, E, H, I = wl.T, wl.k, ex0.E, ex0.H, ex0.I
+    counts = np.bincount(wl.ids.ravel(), minlength=E)
+    log(f"[bench] workload {args.config}: T={T} k={k} E={E} H={H} I={I} arena={ex0.arena.nbytes / 2**20:.1f} MiB "
+        f"pairs/expert min={counts.min()} mean={counts.mean():.1f} max={counts.max()} (gen {time.time() - t0:.1f}s)")
+
+    dev = rl.DeviceExperts.from_workload(ex0)
+    sets = [dev] + [dev.with_arena(dev.arena.clone()) for _ in range(max(args.rotate, 1) - 1)]
+    x = torch.from_numpy(wl.x.view(np.int16).copy()).cuda()
+    ids = torch.from_numpy(wl.ids).cuda()
+    w = torch.from_numpy(wl.w).cuda()
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = rl.alloc_workspace(T, k, dev)
+
+    flops = 6.0 * H * I * T * k
+    flops_gateup = 4.0 * H * I * T * k
+    flops_down = 2.0 * H * I * T * k
+
+    # warm-up
+    for i in range(args.warmup):
+        rl.prefill(x, ids, w, sets[i % len(sets)], out=out, ws=ws)
+    torch.cuda.synchronize()
+    assert rl.status(ws)[0] == 0
+
+    # timed region: K steps, rotating weight sets
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        rl.prefill(x, ids, w, sets[i % len(sets)], out=out, ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # same number of steps with events between the stages (on the stream the kernels run on)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        rl.prefill_timed(x, ids, w, sets[i % len(sets)], out, ws, evs[i])
+    torch.cuda.synchronize()
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+    st_ms = stage.mean(axis=0)
+
+    # warm (same weights every step) for context
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        rl.prefill(x, ids, w, dev, out=out, ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / args.steps
+
+    gpu_out = out.cpu().numpy().astype(np.float64)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gu_tflops = flops_gateup / (st_ms[1] * 1e-3) / 1e12
+    log(f"[bench] {ms_step * 1e3:.1f} us/layer = {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 "
+        f"peak); stages us: group {st_ms[0] * 1e3:.1f} gate/up {st_ms[1] * 1e3:.1f} down {st_ms[2] * 1e3:.1f} "
+        f"combine {st_ms[3] * 1e3:.1f}; warm {ms_warm * 1e3:.1f} us")
+
+    result = {
+        "metric": "routed-expert layer ms & TFLOPS (% bf16 MFMA peak), 2048 tok, 512 exp, top-10",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {T} tokens x {E} experts x top-{k}, hidden {H}, intermediate {I}, "
+                        f"{'T1' if args.config.startswith('t1') else wl.meta['types']} experts, bf16 activations",
+            "tokens": T, "experts": E, "top_k": k, "hidden": H, "intermediate": I, "pairs": T * k,
+            "seed": args.seed, "weight_sets_rotated": len(sets),
+        },
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 3),
+        "ms_per_layer_warm": round(ms_warm, 5),
+        "stage_ms": {"group": round(st_ms[0], 5), "gate_up": round(st_ms[1], 5), "down": round(st_ms[2], 5),
+                     "combine": round(st_ms[3], 5)},
+        "roofline": {
+            "kernel": "k_gateup (fused T1 decode + gate/up grouped GEMM + SwiGLU)",
+            "bound": "mfma",
+            "achieved": round(gu_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 5),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_oracle:
+        import oracle
+
+        nthr = args.oracle_threads or min(16, os.cpu_count() or 1)
+        t1 = time.time()
+        ref = oracle.moe_workload(wl, threads=nthr)
+        cpu_s = time.time() - t1
+        err = float(np.linalg.norm(gpu_out - ref) / np.linalg.norm(ref))
+        result["cpu_baseline"] = {"value": round(cpu_s * 1e3, 1), "unit": "ms per layer", "cores": nthr,
+                                  "kind": "oracle",
+                                  "sample": f"the whole {args.config} layer once (all {T * k} pairs), C, float64"}
+        result["parity_rel_l2_vs_oracle"] = err
+        log(f"[bench] oracle {cpu_s:.1f}s on {nthr} threads; GPU vs oracle rel_l2 {err:.3e}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

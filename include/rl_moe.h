@@ -1,0 +1,144 @@
+/*
+ * rl_moe -- routed-expert MoE FFN stage of prompt ingestion on 1.8-2.3-bit block-quantized
+ * experts, for AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * Operation (Red Lite dev75, "Prompt ingestion" and "Decode"; dev72, "2-row verify"):
+ * every token t was routed to k experts; column j of topk_ids/topk_w is the token's j-th
+ * selection.  For each token-expert pair (t, j) with expert e = topk_ids[t][j]:
+ *     g = Wg_e x_t,   u = Wu_e x_t,   h = silu(g) * u,   y_{t,j} = Wd_e h
+ * and the layer output is the weighted sum of the expert outputs taken in selection order:
+ *     out_t = sum_{j=0..k-1} topk_w[t][j] * y_{t,j}
+ * (the MoE tail of dev75 sums in the row's selection order; the 2-row verify of dev72 keeps
+ * every row's own selection order).  Shared experts and the residual are not part of it.
+ *
+ * Pointer kinds: [dev] device memory, [host] host memory.  Every device buffer is owned by
+ * the caller and must stay valid until the stream has passed the call.  The library keeps no
+ * mutable device state of its own between calls (per-call tables live in the caller's
+ * workspace or in kernel arguments), so calls on different streams need different workspaces.
+ * `stream` is a hipStream_t (NULL = the default stream).
+ *
+ * Errors: a negative status is returned synchronously, before anything is launched, and
+ * `out` is then untouched.  An expert id outside [0, E) is only seen on the device: it sets
+ * bit 0 of the workspace status flags (read with rl_moe_status after the stream is synced);
+ * such a token's output is then unspecified, every other token's is still correct.
+ */
+#ifndef RL_MOE_H
+#define RL_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RL_OK 0
+#define RL_EINVAL (-1)     /* a required pointer is NULL, or qtype / code unknown */
+#define RL_ESHAPE (-2)     /* a size is outside the supported set (see each call) */
+#define RL_EWORKSPACE (-3) /* workspace NULL, too small, or not 256-byte aligned */
+#define RL_EHIP (-4)       /* the HIP runtime reported an error at launch */
+#define RL_EQTYPE (-5)     /* the host descriptor copy names an unknown block type */
+
+/* Block types.  Both use 256-value blocks that tile a matrix flattened row-major; rows are
+ * output features, the input dimension is contiguous.
+ *   Q2B (74 B/block): fp16 d | 16 4-bit sub-scales (16 values each, low nibble first) |
+ *                     2-bit codes q, value = d * s * (q - 1.5)
+ *   T1  (57 B/block): fp16 d | 24-bit word of 8 3-bit sub-scales (32 values each) |
+ *                     base-3 digits five per byte, least significant first,
+ *                     value = d * s * (digit - 1); digit bytes are 0..242. */
+#define RL_QTYPE_Q2B 1
+#define RL_QTYPE_T1 2
+
+/* One expert: its block type and the byte offsets of its gate [I x H], up [I x H] and
+ * down [H x I] matrices inside the arena. */
+typedef struct rl_expert_desc {
+    int32_t qtype;
+    int32_t reserved;
+    uint64_t gate_off;
+    uint64_t up_off;
+    uint64_t down_off;
+} rl_expert_desc;
+
+/* The experts of one layer.  arena [dev]: packed blocks.  desc [dev]: E descriptors (read by
+ * the kernels).  desc_host [host]: the same E descriptors (read by the host to decide which
+ * type-specialised kernels to launch).  E in [1, 1024].  H (hidden) a multiple of 256 in
+ * [256, 8192].  I (expert intermediate) a multiple of 64 in [64, 4096] that is either a
+ * multiple of 256 or one of 64 / 128. */
+typedef struct rl_expert_blobs {
+    const void* arena;
+    const rl_expert_desc* desc;
+    const rl_expert_desc* desc_host;
+    int32_t E, H, I;
+} rl_expert_blobs;
+
+/* Bytes of workspace that rl_moe_prefill / rl_moe_decode / rl_moe_gate_up need for up to
+ * T_max tokens with k selections each.  0 if the sizes are outside the supported set. */
+size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, int32_t I);
+
+/* Routed-expert layer for T tokens (prompt ingestion).
+ *   x        [dev] bf16 bits [T][H]
+ *   topk_ids [dev] int32 [T][k], column j = j-th selection (the summation order)
+ *   topk_w   [dev] float [T][k]
+ *   experts  [host] struct, see above
+ *   out      [dev] float [T][H], overwritten
+ *   T >= 0 (T = 0 launches nothing), k in [1, 16]
+ *   workspace [dev], 256-byte aligned, ws_bytes >= rl_moe_workspace_bytes(T, k, E, H, I).
+ * Launches: pair grouping, one fused dequant + gate/up + SwiGLU kernel per block type
+ * present, one dequant + down kernel per type, the ordered combine.  Asynchronous. */
+int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                   const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Measurement hook: rl_moe_prefill with five events (events [host] array of hipEvent_t,
+ * created by the caller) recorded on `stream`: before the grouping kernel, after it, after the
+ * gate/up kernel(s), after the down kernel(s) and after the combine, so that the caller can
+ * time each stage on the stream the kernels run on.  Otherwise identical to rl_moe_prefill;
+ * RL_EINVAL if an event is NULL. */
+int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                         const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
+                         void* workspace, size_t ws_bytes, void* stream, void* const* events);
+
+/* The same layer for 1 or 2 rows (decode and 2-row verify; dev75 "Decode", dev72 "2-row
+ * verify"): matrix-vector kernels, gate/up + SwiGLU then down + the ordered combine in one
+ * dispatch.  T (= rows) must be 1 or 2.  Each row's result is bit-identical to a call with
+ * that row alone.  Arguments as rl_moe_prefill; additionally H and I must each be 256, 512 or
+ * a multiple of 1024. */
+int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                  const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Pair grouping alone (parity hook for the first step of rl_moe_prefill).  Pairs (t, j) are
+ * ordered by (expert, token, slot):
+ *   offsets  [dev] int32 [E+1], exclusive prefix sum of the per-expert pair counts
+ *   pair_src [dev] int32 [T*k], t*k + j of the pair at each sorted position
+ *   inv      [dev] int32 [T*k], sorted position of pair (t, j); -1 for an invalid id
+ *   flags    [dev] int32 [4], bit 0 of flags[0] set if an id is outside [0, E); the call
+ *            clears the flags first.
+ * T*k <= 2^24, E in [1, 1024]. */
+int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                       int32_t* pair_src, int32_t* inv, int32_t* flags, void* stream);
+
+/* Block decode alone (parity hook for the in-kernel weight decode): n_values (a multiple of
+ * 256) consecutive values of `blocks` [dev] as float d * s * c into out [dev].  Uses the same
+ * device decode routine as the matrix kernels. */
+int rl_moe_dequant(int32_t qtype, const void* blocks, int64_t n_values, float* out, void* stream);
+
+/* Grouping + fused dequant/gate/up/SwiGLU alone (parity hook): writes h as fp16 bits
+ * [T*k][I] in sorted-pair order (row = sorted position) to h_out [dev].  Arguments as
+ * rl_moe_prefill. */
+int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                   const rl_expert_blobs* experts, uint16_t* h_out, int32_t T, int32_t k,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Device status flags of the last call that used `workspace` [dev]; the caller must have
+ * synchronised the stream.  flags_out [host] int32 [4].  Blocking copy. */
+int rl_moe_status(const void* workspace, int32_t* flags_out);
+
+/* Text of a status code. */
+const char* rl_moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RL_MOE_H */

@@ -1,0 +1,27 @@
+"""MI355X routed-expert MoE layer on 1.8-2.3-bit block-quantized experts.
+
+A thin binding of the C ABI in include/rl_moe.h (librl_moe.so, HIP for gfx950).  Every
+step of the layer runs in the library's kernels; this package only marshals arguments and
+takes device memory and streams from PyTorch.  Importing it does not need a GPU; calling it
+needs the built library and fails loudly without it.
+"""
+from ._binding import (  # noqa: F401
+    RL_OK,
+    RL_QTYPE_Q2B,
+    RL_QTYPE_T1,
+    RlError,
+    DeviceExperts,
+    lib,
+    lib_path,
+    exported_symbols,
+    workspace_bytes,
+    alloc_workspace,
+    prefill,
+    prefill_timed,
+    decode,
+    gate_up,
+    group_pairs,
+    dequant,
+    status,
+    strerror,
+)

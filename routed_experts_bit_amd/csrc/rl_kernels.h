@@ -1,0 +1,615 @@
+// HIP kernels of the routed-expert MoE layer for gfx950 (wave64, MFMA 16x16x32).
+//
+//   k_group      token-expert pairs grouped per expert (stable, deterministic), plus the
+//                per-type expert work lists, longest expert first
+//   k_gateup     fused block decode + gate/up grouped GEMM (bf16 MFMA) + SwiGLU -> h (fp16)
+//   k_down       fused block decode + down grouped GEMM (fp16 MFMA) -> y per pair (fp32)
+//   k_combine    out_t = sum_j w[t][j] * y_{t,j}, j ascending (selection order)
+//   k_gv_gateup  1-2 row matrix-vector gate/up + SwiGLU (fp32 VALU, 16 lanes per row)
+//   k_gv_down    1-2 row matrix-vector down + ordered combine in one dispatch
+//   k_dequant    block decode to fp32 through the same fragment decoder
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rl_decode.h"
+#include "rl_moe.h"
+
+namespace rl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int FLAG_BAD_ID = 1;
+constexpr int FLAG_BAD_QTYPE = 2;
+constexpr int FLAGS_WORDS = 64;   // flags[0] error bits; flags[8 + q] work-list length of type q
+constexpr int MAX_E = 1024;
+constexpr int GROUP_THREADS = 512;
+constexpr int GROUP_WAVES = GROUP_THREADS / 64;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// ---------------------------------------------------------------------------------------
+// Pair grouping.  One workgroup of 8 waves.  Wave w owns a contiguous run of the flattened
+// pairs p = t*k + j; its pairs of expert e land after those of waves < w, in order, so the
+// sorted order is (expert, token, slot).  Inside a wave, lanes holding the same expert are
+// found with ballots over the bits of the id and ranked by lane number.
+struct GroupArgs {
+    const int32_t* ids;
+    const rl_expert_desc* desc;  // may be NULL: no work lists
+    int32_t* offsets;
+    int32_t* pair_src;
+    int32_t* inv;
+    int32_t* flags;
+    int32_t* worklist;  // [2][E]: experts of type q with pairs, most pairs first
+    int P, E;
+    int nflags;         // flag words to clear (4 for the grouping entry point, FLAGS_WORDS in a layer)
+};
+
+__global__ __launch_bounds__(GROUP_THREADS) void k_group(GroupArgs a) {
+    __shared__ int32_t hist[GROUP_WAVES][MAX_E];
+    __shared__ int32_t tot[MAX_E];
+    __shared__ int32_t scan[MAX_E];
+    __shared__ int32_t qt[MAX_E];
+    __shared__ int32_t wl_len[3];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int E = a.E, P = a.P;
+    if (tid < a.nflags) __hip_atomic_exchange(&a.flags[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 3) wl_len[tid] = 0;
+    for (int i = tid; i < GROUP_WAVES * MAX_E; i += GROUP_THREADS) (&hist[0][0])[i] = 0;
+    __syncthreads();
+
+    const int chunk = (P + GROUP_WAVES - 1) / GROUP_WAVES;
+    const int p_begin = min(P, wave * chunk), p_end = min(P, p_begin + chunk);
+    int bad = 0;
+    for (int base = p_begin; base < p_end; base += 64) {
+        int p = base + lane;
+        if (p < p_end) {
+            int e = a.ids[p];
+            if (e >= 0 && e < E)
+                atomicAdd(&hist[wave][e], 1);
+            else
+                bad = 1;
+        }
+    }
+    if (bad) __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+
+    // per expert: prefix over waves (in place) and the total
+    for (int e = tid; e < MAX_E; e += GROUP_THREADS) {
+        int run = 0;
+        if (e < E) {
+#pragma unroll
+            for (int w = 0; w < GROUP_WAVES; ++w) {
+                int c = hist[w][e];
+                hist[w][e] = run;
+                run += c;
+            }
+        }
+        tot[e] = run;
+        scan[e] = run;
+    }
+    __syncthreads();
+    // inclusive scan of tot over experts (Hillis-Steele, two elements per thread)
+    for (int off = 1; off < MAX_E; off <<= 1) {
+        int v0 = tid >= off ? scan[tid - off] : 0;
+        int v1 = tid + GROUP_THREADS >= off ? scan[tid + GROUP_THREADS - off] : 0;
+        __syncthreads();
+        scan[tid] += v0;
+        scan[tid + GROUP_THREADS] += v1;
+        __syncthreads();
+    }
+    for (int e = tid; e <= E; e += GROUP_THREADS) a.offsets[e] = e == 0 ? 0 : scan[e - 1];
+
+    // stable scatter
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = p_begin; base < p_end; base += 64) {
+        int p = base + lane;
+        int e = -1;
+        if (p < p_end) e = a.ids[p];
+        bool ok = (e >= 0 && e < E);
+        uint64_t peers = __ballot(ok);
+        for (int bit = 0; bit < 10; ++bit) {
+            uint64_t m = __ballot(ok && ((e >> bit) & 1));
+            peers &= ((e >> bit) & 1) ? m : ~m;
+        }
+        if (ok) {
+            int rank = __popcll(peers & lt_mask);
+            int pos = (scan[e] - tot[e]) + hist[wave][e] + rank;
+            a.pair_src[pos] = p;
+            a.inv[p] = pos;
+        } else if (p < p_end) {
+            a.inv[p] = -1;
+        }
+        // make every lane's read of hist[wave][e] happen before the leader's update
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        if (ok && (peers & lt_mask) == 0) hist[wave][e] += __popcll(peers);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // per-type work lists, experts with more pairs first (ties: lower id first)
+    if (a.desc != nullptr) {
+        for (int e = tid; e < MAX_E; e += GROUP_THREADS) qt[e] = e < E ? a.desc[e].qtype : 0;
+        __syncthreads();
+        for (int e = tid; e < E; e += GROUP_THREADS) {
+            int n = tot[e], q = qt[e];
+            if (q != QT_Q2B && q != QT_T1) {
+                if (n > 0) __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_QTYPE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
+            if (n == 0) continue;
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2) {
+                int n2 = tot[e2];
+                rank += (qt[e2] == q && n2 > 0 && (n2 > n || (n2 == n && e2 < e))) ? 1 : 0;
+            }
+            a.worklist[(q - 1) * E + rank] = e;
+            atomicAdd(&wl_len[q], 1);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            a.flags[8 + QT_Q2B] = wl_len[QT_Q2B];
+            a.flags[8 + QT_T1] = wl_len[QT_T1];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Work item -> (expert rank, column slice).  Work-groups are dispatched round-robin over the
+// 8 XCDs and a persistent work-group w only takes items i = w (mod gridDim), gridDim being a
+// multiple of 8, so i % 8 is the XCD: every slice of one expert runs on the same XCD (its
+// gathered activation rows are read through one L2), and ranks 0..7 -- the largest experts --
+// come first.
+__device__ __forceinline__ void item_to_work(int item, int ns, int& rank, int& slice) {
+    int xcd = item & 7, local = item >> 3;
+    rank = (local / ns) * 8 + xcd;
+    slice = local % ns;
+}
+
+// Decode tables of one block type, built once per (persistent) work-group.
+template <int QT, bool F16>
+struct DecodeTables {
+    uint64_t val[val_entries<QT>()];
+    uint32_t tern[QT == QT_T1 ? 256 : 1];
+    __device__ inline void build(int tid, int nthr) {
+        for (int i = tid; i < val_entries<QT>(); i += nthr) val[i] = val_entry<QT, F16>(i);
+        if constexpr (QT == QT_T1)
+            for (int i = tid; i < 256; i += nthr) tern[i] = tern_entry((uint32_t)i);
+    }
+};
+
+struct GateUpArgs {
+    const uint16_t* x;
+    const uint8_t* arena;
+    const rl_expert_desc* desc;
+    const int32_t* offsets;
+    const int32_t* pair_src;
+    const int32_t* worklist;  // this type's list
+    const int32_t* wl_len;    // this type's list length (device)
+    uint16_t* hbuf;           // [P][I] fp16, sorted-pair order
+    int H, I, k, ns, n_items;
+};
+
+// One work item = one expert x (16*NTI*NW) intermediate columns; wave w owns NTI gate tiles
+// and the NTI up tiles of the same columns, so SwiGLU is elementwise in registers.  For each
+// 64-pair chunk of the expert every weight of the slice is decoded exactly once (straight into
+// MFMA operands) and used for all of the chunk's 16-row pair tiles.  Lane (n, g) of a tile
+// decodes values 64g..64g+63 of each 256-value block of weight row n; the activation operand
+// takes the same k positions.
+template <int QT, int NW, int NTI>
+__global__ __launch_bounds__(64 * NW, 1) void k_gateup(GateUpArgs a) {
+    constexpr int NTHR = 64 * NW;
+    constexpr int NT = 2 * NTI;
+    constexpr int LDA = 256 + 8;
+    constexpr int BB = Fmt<QT>::BYTES;
+    constexpr int LOADS = 64 * 32 / NTHR;  // 16-byte pieces of the 64 x 256 activation tile
+    constexpr int ROWS_PER_PASS = NTHR / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t As[64 * LDA];
+    __shared__ DecodeTables<QT, false> tab;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    tab.build(tid, NTHR);
+    __syncthreads();
+    const int n_ranks = *a.wl_len;
+    const int nkb = a.H >> 8;
+
+    for (int item = blockIdx.x; item < a.n_items; item += gridDim.x) {
+        int rank, slice;
+        item_to_work(item, a.ns, rank, slice);
+        if (rank >= n_ranks) break;
+        const int e = a.worklist[rank];
+        const int p0 = a.offsets[e], ne = a.offsets[e + 1] - p0;
+        const rl_expert_desc dsc = a.desc[e];
+        const int colw = slice * (16 * NTI * NW) + wave * (16 * NTI);
+        const uint8_t* wrow[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            wrow[t] = a.arena + (t < NTI ? dsc.gate_off : dsc.up_off) + (size_t)(colw + 16 * (t % NTI) + n) * nkb * BB;
+
+        for (int mc = 0; mc < ne; mc += 64) {
+            const int rows = min(64, ne - mc);
+            const int mtiles = (rows + 15) >> 4;
+            int tok[LOADS];
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                int row = (tid >> 5) + ROWS_PER_PASS * i;
+                tok[i] = row < rows ? a.pair_src[p0 + mc + row] / a.k : -1;
+            }
+            f32x4 acc[4][NT];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            for (int kb = 0; kb < nkb; ++kb) {
+                Strip<QT, false, 64> st[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) st[t].load(wrow[t] + (size_t)kb * BB, 64 * g);
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    int row = (tid >> 5) + ROWS_PER_PASS * i, ch = tid & 31;
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (tok[i] >= 0) v = *(const u32x4*)(a.x + (size_t)tok[i] * a.H + kb * 256 + ch * 8);
+                    *(u32x4*)&As[row * LDA + ch * 8] = v;
+                }
+                __syncthreads();
+                float ds[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    st[t].prepare(tab.tern);
+                    ds[t] = st[t].scale();
+                }
+                f32x4 blk[4][NT];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) blk[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int f = 0; f < 8; ++f) {
+                    u32x4 b[NT];
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) b[t] = st[t].frag(f, tab.val);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        if (mt < mtiles) {
+                            u32x4 av = *(const u32x4*)&As[(mt * 16 + n) * LDA + 64 * g + 8 * f];
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) blk[mt][t] = mfma_bf16(av, b[t], blk[mt][t]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    if (mt < mtiles)
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) acc[mt][t] += ds[t] * blk[mt][t];
+            }
+            // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < mtiles) {
+#pragma unroll
+                    for (int ti = 0; ti < NTI; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            int r = mt * 16 + 4 * g + i;
+                            if (r < rows) {
+                                float hv = silu(acc[mt][ti][i]) * acc[mt][NTI + ti][i];
+                                a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(hv);
+                            }
+                        }
+                }
+            }
+        }
+    }
+}
+
+struct DownArgs {
+    const uint16_t* hbuf;  // [P][I] fp16, sorted-pair order
+    const uint8_t* arena;
+    const rl_expert_desc* desc;
+    const int32_t* offsets;
+    const int32_t* pair_src;
+    const int32_t* worklist;
+    const int32_t* wl_len;
+    float* yslot;  // [T*k][H] fp32, row t*k + j
+    int H, I, ns, n_items;
+};
+
+// One work item = one expert x (16*NTW*NW) output columns.  K runs over the intermediate
+// dimension in chunks of LCH = min(I, 256) values, each inside one block of every W_down row;
+// lane (n, g) decodes values LCH/4*g .. LCH/4*(g+1)-1 of the chunk.
+template <int QT, int LCH, int NW, int NTW>
+__global__ __launch_bounds__(64 * NW, 1) void k_down(DownArgs a) {
+    constexpr int NTHR = 64 * NW;
+    constexpr int LDA = LCH + 8;
+    constexpr int BB = Fmt<QT>::BYTES;
+    constexpr int STRIP = LCH / 4;
+    constexpr int NFRAG = STRIP / 8;
+    constexpr int CH_PER_ROW = LCH / 8;
+    constexpr int LOADS = (64 * CH_PER_ROW + NTHR - 1) / NTHR;
+    __shared__ __attribute__((aligned(16))) uint16_t As[64 * LDA];
+    __shared__ DecodeTables<QT, true> tab;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    tab.build(tid, NTHR);
+    __syncthreads();
+    const int n_ranks = *a.wl_len;
+    const int nkc = a.I / LCH;
+
+    for (int item = blockIdx.x; item < a.n_items; item += gridDim.x) {
+        int rank, slice;
+        item_to_work(item, a.ns, rank, slice);
+        if (rank >= n_ranks) break;
+        const int e = a.worklist[rank];
+        const int p0 = a.offsets[e], ne = a.offsets[e + 1] - p0;
+        const uint8_t* Wd = a.arena + a.desc[e].down_off;
+        const int col0 = slice * (16 * NTW * NW) + wave * (16 * NTW);
+
+        for (int mc = 0; mc < ne; mc += 64) {
+            const int rows = min(64, ne - mc);
+            const int mtiles = (rows + 15) >> 4;
+            f32x4 acc[4][NTW];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kc = 0; kc < nkc; ++kc) {
+                Strip<QT, true, STRIP> st[NTW];
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) {
+                    size_t flat = (size_t)(col0 + 16 * t + n) * a.I + (size_t)kc * LCH;
+                    st[t].load(Wd + (flat >> 8) * BB, (int)(flat & 255) + STRIP * g);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    int idx = tid + NTHR * i;
+                    if (idx < 64 * CH_PER_ROW) {
+                        int row = idx / CH_PER_ROW, ch = idx % CH_PER_ROW;
+                        u32x4 v = {0u, 0u, 0u, 0u};
+                        if (row < rows)
+                            v = *(const u32x4*)(a.hbuf + (size_t)(p0 + mc + row) * a.I + kc * LCH + ch * 8);
+                        *(u32x4*)&As[row * LDA + ch * 8] = v;
+                    }
+                }
+                __syncthreads();
+                float ds[NTW];
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) {
+                    st[t].prepare(tab.tern);
+                    ds[t] = st[t].scale();
+                }
+                f32x4 blk[4][NTW];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) blk[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int f = 0; f < NFRAG; ++f) {
+                    u32x4 b[NTW];
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) b[t] = st[t].frag(f, tab.val);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        if (mt < mtiles) {
+                            u32x4 av = *(const u32x4*)&As[(mt * 16 + n) * LDA + STRIP * g + 8 * f];
+#pragma unroll
+                            for (int t = 0; t < NTW; ++t) blk[mt][t] = mfma_f16(av, b[t], blk[mt][t]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    if (mt < mtiles)
+#pragma unroll
+                        for (int t = 0; t < NTW; ++t) acc[mt][t] += ds[t] * blk[mt][t];
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < mtiles) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        int r = mt * 16 + 4 * g + i;
+                        if (r < rows) {
+                            float* yrow = a.yslot + (size_t)a.pair_src[p0 + mc + r] * a.H + col0 + n;
+#pragma unroll
+                            for (int t = 0; t < NTW; ++t) yrow[16 * t] = acc[mt][t][i];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// out[t][c] = sum over j = 0..k-1 (ascending) of w[t][j] * y[t*k + j][c]
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yslot, const float* __restrict__ w,
+                                                 float* __restrict__ out, int k, int H) {
+    const int t = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= H) return;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) acc = __fmaf_rn(w[(size_t)t * k + j], yslot[((size_t)t * k + j) * H + c], acc);
+    out[(size_t)t * H + c] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// 1-2 row path (decode and 2-row verify).  Memory-bound: every weight is read once per row.
+// Types present are a template mask (1: Q2B, 2: T1, 3: both; both tables are then in LDS).
+template <int QMASK>
+struct GvTables {
+    DecodeTables<QT_Q2B, false> q2b;
+    DecodeTables<QT_T1, false> t1;
+    __device__ inline void build(int tid, int nthr) {
+        if constexpr (QMASK & 1) q2b.build(tid, nthr);
+        if constexpr (QMASK & 2) t1.build(tid, nthr);
+    }
+};
+
+// sum over the S values of one strip (inside one block) of w_i * xs[i], times the block scale;
+// xs is bf16 bits (XS_BF16) or fp32.  Fixed order: i ascending, then the scale.
+template <int QT, int S, bool XS_BF16>
+__device__ __forceinline__ float strip_dot(const uint8_t* blk, int vs, const void* xs, const DecodeTables<QT, false>& tb) {
+    Strip<QT, false, S> st;
+    st.load(blk, vs);
+    st.prepare(tb.tern);
+    float part = 0.f;
+#pragma unroll
+    for (int f = 0; f < S / 8; ++f) {
+        const u32x4 fr = st.frag(f, tb.val);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float wv = __uint_as_float(i & 1 ? (fr[i >> 1] & 0xFFFF0000u) : (fr[i >> 1] << 16));
+            const float xv = XS_BF16 ? bf16_bits_to_f32(((const uint16_t*)xs)[8 * f + i]) : ((const float*)xs)[8 * f + i];
+            part = __fmaf_rn(wv, xv, part);
+        }
+    }
+    return part * st.scale();
+}
+
+// span values of row `row` of a [rows x C] matrix starting at column c0, strips of S
+template <int QMASK, int S, bool XS_BF16>
+__device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, int C, int row, int c0, int span, const void* xs,
+                                         const GvTables<QMASK>& tb) {
+    float acc = 0.f;
+    for (int s = 0; s < span; s += S) {
+        const size_t flat = (size_t)row * C + c0 + s;
+        const void* xp = XS_BF16 ? (const void*)((const uint16_t*)xs + s) : (const void*)((const float*)xs + s);
+        if constexpr (QMASK & 2) {
+            if (QMASK == 2 || qtype == QT_T1) {
+                acc += strip_dot<QT_T1, S, XS_BF16>(W + (flat >> 8) * Fmt<QT_T1>::BYTES, (int)(flat & 255), xp, tb.t1);
+                continue;
+            }
+        }
+        if constexpr (QMASK & 1)
+            acc += strip_dot<QT_Q2B, S, XS_BF16>(W + (flat >> 8) * Fmt<QT_Q2B>::BYTES, (int)(flat & 255), xp, tb.q2b);
+    }
+    return acc;
+}
+
+struct GvArgs {
+    const uint16_t* x;
+    const int32_t* ids;
+    const float* w;
+    const uint8_t* arena;
+    const rl_expert_desc* desc;
+    float* hgv;  // [R*k][I] fp32
+    float* out;  // [R][H]
+    int32_t* flags;
+    int R, k, E, H, I;
+};
+
+// A wave computes features i0, i0+1 of one (row, slot) pair: lanes 0-15 gate row i0, 16-31
+// gate i0+1, 32-47 up i0, 48-63 up i0+1; each lane covers H/16 consecutive values (two lanes
+// per 256-value block when H = 2048), then a fixed xor tree reduces the 16 partial sums.
+template <int QMASK, int S1>
+__global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
+    __shared__ GvTables<QMASK> tb;
+    tb.build(threadIdx.x, 256);
+    if (blockIdx.x == 0 && threadIdx.x < FLAGS_WORDS) a.flags[threadIdx.x] = 0;  // k_gv_down sets them
+    __syncthreads();
+    const int lane = threadIdx.x & 63, rs = lane >> 4, q = lane & 15;
+    const int half_i = a.I >> 1;
+    const int total = a.R * a.k * half_i;
+    const int span = a.H >> 4;
+    for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < total; wv += gridDim.x * 4) {
+        const int pr = wv / half_i;
+        const int i0 = 2 * (wv % half_i);
+        const int r = pr / a.k;
+        const int e = a.ids[pr];
+        const int row = i0 + (rs & 1);
+        float part = 0.f;
+        if (e >= 0 && e < a.E) {
+            const rl_expert_desc dsc = a.desc[e];
+            const uint8_t* W = a.arena + (rs < 2 ? dsc.gate_off : dsc.up_off);
+            part = row_dot<QMASK, S1, true>(dsc.qtype, W, a.H, row, q * span, span, a.x + (size_t)r * a.H + q * span, tb);
+        }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+        const float other = __shfl_xor(part, 32, 64);  // gate lanes receive the up sum of their feature
+        if (rs < 2 && q == 0) a.hgv[(size_t)pr * a.I + row] = (e >= 0 && e < a.E) ? silu(part) * other : 0.f;
+    }
+}
+
+// One wave per (row r, output column c): lane group gq = lane/16 takes slot j = 4*round + gq,
+// each lane I/16 values of row c of that expert's W_down; after the 16-lane reduction the slot
+// outputs are added to the accumulator in selection order j = 0..k-1.
+template <int QMASK, int S2>
+__global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
+    __shared__ GvTables<QMASK> tb;
+    tb.build(threadIdx.x, 256);
+    __syncthreads();
+    const int lane = threadIdx.x & 63, gq = lane >> 4, q = lane & 15;
+    const int span = a.I >> 4;
+    for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < a.R * a.H; wv += gridDim.x * 4) {
+        const int r = wv / a.H, c = wv % a.H;
+        float acc = 0.f;
+        for (int j0 = 0; j0 < a.k; j0 += 4) {
+            const int j = j0 + gq;
+            float part = 0.f;
+            if (j < a.k) {
+                const int e = a.ids[r * a.k + j];
+                if ((e < 0 || e >= a.E) && q == 0)
+                    __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (e >= 0 && e < a.E) {
+                    const rl_expert_desc dsc = a.desc[e];
+                    part = row_dot<QMASK, S2, false>(dsc.qtype, a.arena + dsc.down_off, a.I, c, q * span, span,
+                                                     a.hgv + (size_t)(r * a.k + j) * a.I + q * span, tb);
+                }
+            }
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const float y = __shfl(part, 16 * s2, 64);
+                if (j0 + s2 < a.k) acc = __fmaf_rn(a.w[r * a.k + j0 + s2], y, acc);
+            }
+        }
+        if (lane == 0) a.out[(size_t)r * a.H + c] = acc;
+    }
+}
+
+// Four threads per block, each decoding a 64-value strip through the same decoder as the
+// matrix kernels: out = (s*c) * block scale, exact in fp32.
+template <int QT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blocks, int64_t n_blocks,
+                                                 float* __restrict__ out) {
+    __shared__ DecodeTables<QT, false> tab;
+    tab.build(threadIdx.x, 256);
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_blocks * 4) return;
+    const int64_t b = t >> 2;
+    const int g = (int)(t & 3);
+    Strip<QT, false, 64> st;
+    st.load(blocks + b * Fmt<QT>::BYTES, 64 * g);
+    st.prepare(tab.tern);
+    const float d = st.scale();
+    float* o = out + b * 256 + 64 * g;
+    for (int f = 0; f < 8; ++f) {
+        const u32x4 fr = st.frag(f, tab.val);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[8 * f + 2 * i] = __uint_as_float(fr[i] << 16) * d;
+            o[8 * f + 2 * i + 1] = __uint_as_float(fr[i] & 0xFFFF0000u) * d;
+        }
+    }
+}
+
+}  // namespace rl

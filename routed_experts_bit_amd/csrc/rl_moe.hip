@@ -1,0 +1,369 @@
+// C ABI of the routed-expert MoE layer (declarations and contracts: include/rl_moe.h).
+//
+// Host side: argument validation (synchronous, before any launch), workspace carving and
+// stream-ordered launches.  No device allocation, no host synchronisation inside a call, no
+// library-global device buffers: every per-call table lives in the caller's workspace (Red
+// Lite dev72, "2-row verify": tables written into shared buffers at encode time let one
+// in-flight row read another row's tables).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "rl_kernels.h"
+#include "rl_moe.h"
+
+namespace {
+
+using namespace rl;
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+    size_t flags, offsets, pair_src, inv, worklist, hbuf, yslot, total;
+};
+
+bool shape_ok(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+    if (T < 0 || k < 1 || k > 16) return false;
+    if (E < 1 || E > MAX_E) return false;
+    if (H < 256 || H > 8192 || H % 256) return false;
+    if (I < 64 || I > 4096 || I % 64) return false;
+    if (!(I % 256 == 0 || I == 64 || I == 128)) return false;
+    if (T * (int64_t)k > (1 << 24)) return false;
+    return true;
+}
+
+Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+    Layout L;
+    const size_t P = (size_t)T * (size_t)k;
+    size_t off = 0;
+    L.flags = off;
+    off = align_up(off + FLAGS_WORDS * sizeof(int32_t));
+    L.offsets = off;
+    off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
+    L.pair_src = off;
+    off = align_up(off + P * sizeof(int32_t));
+    L.inv = off;
+    off = align_up(off + P * sizeof(int32_t));
+    L.worklist = off;
+    off = align_up(off + 2 * (size_t)E * sizeof(int32_t));
+    L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
+    off = align_up(off + P * (size_t)I * sizeof(float));
+    L.yslot = off;
+    off = align_up(off + P * (size_t)H * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+int hip_status() { return hipGetLastError() == hipSuccess ? RL_OK : RL_EHIP; }
+
+template <typename P>
+P* at(void* ws, size_t off) {
+    return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+// Common validation of the layer entry points.  Fills `present[q]` with the number of
+// experts of type q (from the host copy of the descriptors).
+int check_layer(const void* x, const void* ids, const void* w, const rl_expert_blobs* ex, const void* out, int32_t T,
+                int32_t k, const void* ws, size_t ws_bytes, int present[3]) {
+    if (!ex) return RL_EINVAL;
+    if (!shape_ok(T, k, ex->E, ex->H, ex->I)) return RL_ESHAPE;
+    if (T == 0) return RL_OK;
+    if (!x || !ids || !w || !out || !ex->arena || !ex->desc || !ex->desc_host) return RL_EINVAL;
+    if (!ws || ((uintptr_t)ws % ALIGN)) return RL_EWORKSPACE;
+    if (ws_bytes < layout(T, k, ex->E, ex->H, ex->I).total) return RL_EWORKSPACE;
+    present[0] = present[1] = present[2] = 0;
+    for (int e = 0; e < ex->E; ++e) {
+        int q = ex->desc_host[e].qtype;
+        if (q != QT_Q2B && q != QT_T1) return RL_EQTYPE;
+        present[q] += 1;
+    }
+    return RL_OK;
+}
+
+void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
+                  int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, hipStream_t s) {
+    GroupArgs g;
+    g.ids = ids;
+    g.desc = desc;
+    g.offsets = offsets;
+    g.pair_src = pair_src;
+    g.inv = inv;
+    g.flags = flags;
+    g.worklist = worklist;
+    g.P = T * k;
+    g.E = E;
+    g.nflags = desc ? FLAGS_WORDS : 4;
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, s, g);
+}
+
+// Persistent grids: at most two work-groups per CU (256 CUs), a multiple of 8 so that a
+// work-group always stays on one XCD's share of the items.
+constexpr int MAX_GRID = 512;
+int items_for(int n_experts, int ns) { return ((n_experts + 7) / 8) * 8 * ns; }
+int grid_for(int n_items) { return n_items < MAX_GRID ? n_items : MAX_GRID; }
+
+template <int QT>
+void launch_gateup_t(const GateUpArgs& a, int n_experts, hipStream_t s) {
+    GateUpArgs b = a;
+    if (a.I % 128 == 0) {
+        b.ns = a.I / 128;
+        b.n_items = items_for(n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup<QT, 4, 2>), dim3(grid_for(b.n_items)), dim3(256), 0, s, b);
+    } else {
+        b.ns = a.I / 64;
+        b.n_items = items_for(n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup<QT, 4, 1>), dim3(grid_for(b.n_items)), dim3(256), 0, s, b);
+    }
+}
+
+template <int QT>
+void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
+    DownArgs b = a;
+    b.ns = a.H / 256;
+    b.n_items = items_for(n_experts, b.ns);
+    dim3 grid(grid_for(b.n_items));
+    if (a.I % 256 == 0)
+        hipLaunchKernelGGL((k_down<QT, 256, 4, 4>), grid, dim3(256), 0, s, b);
+    else if (a.I == 128)
+        hipLaunchKernelGGL((k_down<QT, 128, 4, 4>), grid, dim3(256), 0, s, b);
+    else
+        hipLaunchKernelGGL((k_down<QT, 64, 4, 4>), grid, dim3(256), 0, s, b);
+}
+
+bool gv_dim_ok(int d) { return d == 256 || d == 512 || (d % 1024 == 0); }
+
+template <int QMASK>
+void launch_gv(const GvArgs& a, hipStream_t s) {
+    const int waves1 = a.R * a.k * (a.I / 2);
+    const int waves2 = a.R * a.H;
+    dim3 g1((waves1 + 3) / 4 < 1024 ? (waves1 + 3) / 4 : 1024);
+    dim3 g2((waves2 + 3) / 4 < 1024 ? (waves2 + 3) / 4 : 1024);
+    const int s1 = a.H >= 1024 ? 64 : a.H / 16;
+    const int s2 = a.I >= 1024 ? 64 : a.I / 16;
+    if (s1 == 64)
+        hipLaunchKernelGGL((k_gv_gateup<QMASK, 64>), g1, dim3(256), 0, s, a);
+    else if (s1 == 32)
+        hipLaunchKernelGGL((k_gv_gateup<QMASK, 32>), g1, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gv_gateup<QMASK, 16>), g1, dim3(256), 0, s, a);
+    if (s2 == 64)
+        hipLaunchKernelGGL((k_gv_down<QMASK, 64>), g2, dim3(256), 0, s, a);
+    else if (s2 == 32)
+        hipLaunchKernelGGL((k_gv_down<QMASK, 32>), g2, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gv_down<QMASK, 16>), g2, dim3(256), 0, s, a);
+}
+
+// grouping + gate/up for every present type; returns the layout used
+void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blobs* ex, int32_t T, int32_t k,
+                      void* ws, const int present[3], uint16_t* hdst, hipStream_t s, Layout& L) {
+    L = layout(T, k, ex->E, ex->H, ex->I);
+    int32_t* flags = at<int32_t>(ws, L.flags);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* pair_src = at<int32_t>(ws, L.pair_src);
+    int32_t* worklist = at<int32_t>(ws, L.worklist);
+    launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist, s);
+    GateUpArgs a;
+    a.x = x;
+    a.arena = static_cast<const uint8_t*>(ex->arena);
+    a.desc = ex->desc;
+    a.offsets = offsets;
+    a.pair_src = pair_src;
+    a.hbuf = hdst;
+    a.H = ex->H;
+    a.I = ex->I;
+    a.k = k;
+    a.ns = 1;
+    a.n_items = 0;
+    if (present[QT_Q2B]) {
+        a.worklist = worklist + (QT_Q2B - 1) * ex->E;
+        a.wl_len = flags + 8 + QT_Q2B;
+        launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
+    }
+    if (present[QT_T1]) {
+        a.worklist = worklist + (QT_T1 - 1) * ex->E;
+        a.wl_len = flags + 8 + QT_T1;
+        launch_gateup_t<QT_T1>(a, present[QT_T1], s);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, int32_t I) {
+    if (!shape_ok(T_max, k, E, H, I)) return 0;
+    return layout(T_max, k, E, H, I).total;
+}
+
+static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                        const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* workspace,
+                        size_t ws_bytes, void* stream, void* const* events) {
+    int present[3] = {0, 0, 0};
+    int rc = check_layer(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, present);
+    if (rc != RL_OK || T == 0) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+        if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    };
+    const Layout L = layout(T, k, experts->E, experts->H, experts->I);
+    uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
+    int32_t* flags = at<int32_t>(workspace, L.flags);
+    int32_t* offsets = at<int32_t>(workspace, L.offsets);
+    int32_t* pair_src = at<int32_t>(workspace, L.pair_src);
+    int32_t* worklist = at<int32_t>(workspace, L.worklist);
+    float* yslot = at<float>(workspace, L.yslot);
+    mark(0);
+    launch_group(topk_ids, T, k, experts->E, experts->desc, offsets, pair_src, at<int32_t>(workspace, L.inv), flags,
+                 worklist, s);
+    mark(1);
+    GateUpArgs a;
+    a.x = x;
+    a.arena = static_cast<const uint8_t*>(experts->arena);
+    a.desc = experts->desc;
+    a.offsets = offsets;
+    a.pair_src = pair_src;
+    a.hbuf = hbuf;
+    a.H = experts->H;
+    a.I = experts->I;
+    a.k = k;
+    a.ns = 1;
+    a.n_items = 0;
+    DownArgs d;
+    d.hbuf = hbuf;
+    d.arena = a.arena;
+    d.desc = experts->desc;
+    d.offsets = offsets;
+    d.pair_src = pair_src;
+    d.yslot = yslot;
+    d.H = experts->H;
+    d.I = experts->I;
+    d.ns = 1;
+    d.n_items = 0;
+    if (present[QT_Q2B]) {
+        a.worklist = worklist + (QT_Q2B - 1) * experts->E;
+        a.wl_len = flags + 8 + QT_Q2B;
+        launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
+    }
+    if (present[QT_T1]) {
+        a.worklist = worklist + (QT_T1 - 1) * experts->E;
+        a.wl_len = flags + 8 + QT_T1;
+        launch_gateup_t<QT_T1>(a, present[QT_T1], s);
+    }
+    mark(2);
+    if (present[QT_Q2B]) {
+        d.worklist = worklist + (QT_Q2B - 1) * experts->E;
+        d.wl_len = flags + 8 + QT_Q2B;
+        launch_down_t<QT_Q2B>(d, present[QT_Q2B], s);
+    }
+    if (present[QT_T1]) {
+        d.worklist = worklist + (QT_T1 - 1) * experts->E;
+        d.wl_len = flags + 8 + QT_T1;
+        launch_down_t<QT_T1>(d, present[QT_T1], s);
+    }
+    mark(3);
+    hipLaunchKernelGGL(k_combine, dim3(experts->H / 256, T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
+    mark(4);
+    return hip_status();
+}
+
+int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
+                   float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
+    return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, stream, nullptr);
+}
+
+int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                         const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* workspace,
+                         size_t ws_bytes, void* stream, void* const* events) {
+    if (!events) return RL_EINVAL;
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return RL_EINVAL;
+    return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, stream, events);
+}
+
+int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
+                   uint16_t* h_out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
+    int present[3] = {0, 0, 0};
+    int rc = check_layer(x, topk_ids, topk_w, experts, h_out, T, k, workspace, ws_bytes, present);
+    if (rc != RL_OK || T == 0) return rc;
+    Layout L;
+    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, h_out, static_cast<hipStream_t>(stream), L);
+    return hip_status();
+}
+
+int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
+                  float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
+    int present[3] = {0, 0, 0};
+    if (experts && (T < 1 || T > 2 || !gv_dim_ok(experts->H) || !gv_dim_ok(experts->I))) return RL_ESHAPE;
+    int rc = check_layer(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, present);
+    if (rc != RL_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Layout L = layout(T, k, experts->E, experts->H, experts->I);
+    GvArgs a;
+    a.x = x;
+    a.ids = topk_ids;
+    a.w = topk_w;
+    a.arena = static_cast<const uint8_t*>(experts->arena);
+    a.desc = experts->desc;
+    a.hgv = at<float>(workspace, L.hbuf);
+    a.out = out;
+    a.flags = at<int32_t>(workspace, L.flags);
+    a.R = T;
+    a.k = k;
+    a.E = experts->E;
+    a.H = experts->H;
+    a.I = experts->I;
+    const int mask = (present[QT_Q2B] ? 1 : 0) | (present[QT_T1] ? 2 : 0);
+    if (mask == 1)
+        launch_gv<1>(a, s);
+    else if (mask == 2)
+        launch_gv<2>(a, s);
+    else
+        launch_gv<3>(a, s);
+    return hip_status();
+}
+
+int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets, int32_t* pair_src,
+                       int32_t* inv, int32_t* flags, void* stream) {
+    if (T < 0 || k < 1 || k > 16 || E < 1 || E > MAX_E || (int64_t)T * k > (1 << 24)) return RL_ESHAPE;
+    if (!offsets || !flags || (T > 0 && (!topk_ids || !pair_src || !inv))) return RL_EINVAL;
+    launch_group(topk_ids, T, k, E, nullptr, offsets, pair_src, inv, flags, nullptr, static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int rl_moe_dequant(int32_t qtype, const void* blocks, int64_t n_values, float* out, void* stream) {
+    if (qtype != QT_Q2B && qtype != QT_T1) return RL_EINVAL;
+    if (n_values < 0 || n_values % 256) return RL_ESHAPE;
+    if (n_values == 0) return RL_OK;
+    if (!blocks || !out) return RL_EINVAL;
+    const int64_t n_blocks = n_values / 256;
+    dim3 grid((unsigned)((n_blocks * 4 + 255) / 256));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* b = static_cast<const uint8_t*>(blocks);
+    if (qtype == QT_Q2B)
+        hipLaunchKernelGGL(k_dequant<QT_Q2B>, grid, dim3(256), 0, s, b, n_blocks, out);
+    else
+        hipLaunchKernelGGL(k_dequant<QT_T1>, grid, dim3(256), 0, s, b, n_blocks, out);
+    return hip_status();
+}
+
+int rl_moe_status(const void* workspace, int32_t* flags_out) {
+    if (!workspace || !flags_out) return RL_EINVAL;
+    return hipMemcpy(flags_out, workspace, 4 * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess ? RL_OK
+                                                                                                     : RL_EHIP;
+}
+
+const char* rl_moe_strerror(int status) {
+    switch (status) {
+        case RL_OK: return "ok";
+        case RL_EINVAL: return "invalid argument (NULL pointer or unknown code)";
+        case RL_ESHAPE: return "size outside the supported set";
+        case RL_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case RL_EHIP: return "HIP runtime error at launch";
+        case RL_EQTYPE: return "unknown block type in the expert descriptors";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: bit-exact for the block decode and the pair grouping; relative L2 <= 2e-3 (float64,
+over the whole output) for the fp16 h of the gate/up stage and for the layer output.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import log, rel_l2, to_device
+from workload import QTYPE_Q2B, QTYPE_T1, BLOCK_BYTES, make_experts, make_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def rl():
+    import torch
+
+    import routed_experts_bit_amd as rl
+
+    assert torch.cuda.is_available()
+    rl.lib()
+    return rl
+
+
+# ----------------------------------------------------------------------------- decode
+@pytest.mark.parametrize("qtype", [QTYPE_Q2B, QTYPE_T1])
+def test_dequant_bit_exact(orc, rl, qtype):
+    import torch
+
+    rng = np.random.default_rng(qtype)
+    nb = 3000
+    bb = BLOCK_BYTES[qtype]
+    blk = rng.integers(0, 256, size=(nb, bb)).astype(np.uint8)
+    blk[:, 0:2] = np.frombuffer((rng.standard_normal(nb) * 0.01).astype(np.float16).tobytes(), np.uint8).reshape(nb, 2)
+    if qtype == QTYPE_T1:
+        blk[:, 5:56] = rng.integers(0, 243, size=(nb, 51))
+        blk[:, 56] = rng.integers(0, 3, size=nb)
+    flat = blk.reshape(-1)
+    log(f"dequant qtype={qtype} blocks={nb}")
+    dev = torch.from_numpy(np.concatenate([flat, np.zeros(4, np.uint8)])).cuda()
+    got = rl.dequant(qtype, dev, nb * 256).cpu().numpy()
+    ref = orc.dequant(qtype, flat, nb * 256)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("qtype", [QTYPE_Q2B, QTYPE_T1])
+def test_dequant_real_matrix(orc, rl, qtype):
+    ex = make_experts(2, 2048, 512, qtype, seed=3)
+    import torch
+
+    arena = torch.from_numpy(ex.arena).cuda()
+    for which in ("gate", "down"):
+        off = int(ex.desc[which + "_off"][1])
+        n = 2048 * 512
+        got = rl.dequant(qtype, arena[off:], n).cpu().numpy()
+        ref = orc.dequant(qtype, ex.matrix(1, which), n)
+        assert np.array_equal(got.astype(np.float64), ref)
+
+
+# ----------------------------------------------------------------------------- grouping
+@pytest.mark.parametrize(
+    "T,k,E,kind",
+    [(1, 1, 1, "uniform"), (64, 2, 8, "uniform"), (2048, 10, 512, "uniform"), (1090, 10, 512, "skewed"),
+     (300, 16, 1024, "dup"), (4096, 8, 64, "uniform"), (5, 3, 1024, "uniform")],
+)
+def test_group_pairs_bit_exact(orc, rl, T, k, E, kind):
+    import torch
+
+    rng = np.random.default_rng(T * 31 + k)
+    if kind == "skewed":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        ids = rng.choice(E, size=(T, k), p=p / p.sum()).astype(np.int32)
+    elif kind == "dup":
+        ids = rng.integers(0, 7, size=(T, k)).astype(np.int32)  # duplicates inside rows, most experts empty
+    else:
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    log(f"group T={T} k={k} E={E} {kind}")
+    offsets, src, inv, flags = rl.group_pairs(torch.from_numpy(ids).cuda(), E)
+    o2, s2, i2 = orc.group_pairs(ids, E)
+    assert np.array_equal(offsets.cpu().numpy(), o2)
+    assert np.array_equal(src.cpu().numpy(), s2)
+    assert np.array_equal(inv.cpu().numpy(), i2)
+    assert flags.cpu().numpy()[0] == 0
+
+
+def test_group_pairs_flags_bad_id(rl):
+    import torch
+
+    ids = np.array([[0, 1], [5, 2], [3, -1]], np.int32)
+    offsets, src, inv, flags = rl.group_pairs(torch.from_numpy(ids).cuda(), 4)
+    assert flags.cpu().numpy()[0] & 1
+    inv = inv.cpu().numpy()
+    assert inv[2] == -1 and inv[5] == -1
+    good = [0, 1, 3, 4]
+    assert sorted(inv[good].tolist()) == [0, 1, 2, 3]
+    assert offsets.cpu().numpy()[-1] == 4
+
+
+# ----------------------------------------------------------------------------- layer
+def _medium(name, seed, T=256, E=32, H=2048, I=512, k=10, types=None):
+    over = dict(E=E, H=H, I=I, k=k)
+    if types:
+        over["types"] = types
+    return make_workload(name, seed=seed, T=T, **over)
+
+
+CASES = {
+    "tiny_q2b": lambda: make_workload("tiny", seed=21),
+    "tiny_t1": lambda: make_workload("tiny", seed=22, types="t1"),
+    "med_q2b": lambda: _medium("q2b_1090", 23, types="q2b"),
+    "med_t1": lambda: _medium("t1_2048", 24),
+    "med_mixed": lambda: _medium("mixed_2048", 25),
+    "i128_t1": lambda: _medium("t1_2048", 26, T=96, E=16, H=1024, I=128, k=4),
+    "i64_q2b": lambda: _medium("q2b_1090", 27, T=80, E=12, H=512, I=64, k=3),
+    "i256_mixed_k1": lambda: _medium("mixed_2048", 28, T=130, E=8, H=768, I=256, k=1),
+}
+
+
+@pytest.fixture(scope="module")
+def cases():
+    return {}
+
+
+def _case(cases, name):
+    if name not in cases:
+        cases[name] = CASES[name]()
+    return cases[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_parity(orc, rl, cases, name):
+    wl = _case(cases, name)
+    log(f"prefill {name} T={wl.T} k={wl.k} E={wl.experts.E} H={wl.experts.H} I={wl.experts.I}")
+    x, ids, w, ex = to_device(wl)
+    ws = rl.alloc_workspace(wl.T, wl.k, ex)
+    out = rl.prefill(x, ids, w, ex, ws=ws).cpu().numpy()
+    assert rl.status(ws)[0] == 0
+    ref = orc.moe_workload(wl)
+    err = rel_l2(out, ref)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name", ["tiny_q2b", "med_t1", "med_mixed", "i64_q2b"])
+def test_gate_up_h_parity(orc, rl, cases, name):
+    wl = _case(cases, name)
+    x, ids, w, ex = to_device(wl)
+    h = rl.gate_up(x, ids, w, ex).cpu().numpy().view(np.float16).astype(np.float64)
+    _, ref_h = orc.moe_workload(wl, want_h=True)  # [T, k, I]
+    _, src, _ = orc.group_pairs(wl.ids, wl.experts.E)
+    ref_sorted = ref_h.reshape(wl.T * wl.k, -1)[src]
+    err = rel_l2(h, ref_sorted)
+    log(f"gate_up {name} rel_l2={err:.3e}")
+    assert err <= TOL
+
+
+def test_prefill_deterministic_and_invariants(orc, rl, cases):
+    import torch
+
+    wl = _case(cases, "med_mixed")
+    x, ids, w, ex = to_device(wl)
+    a = rl.prefill(x, ids, w, ex)
+    b = rl.prefill(x, ids, w, ex)
+    assert torch.equal(a, b)
+    # doubling all weights doubles the output exactly
+    c = rl.prefill(x, ids, w * 2, ex)
+    assert torch.equal(c, 2 * a)
+    # a zero-weight pair contributes nothing, whichever expert it names
+    w0 = w.clone()
+    w0[:, 3] = 0
+    d1 = rl.prefill(x, ids, w0, ex)
+    ids2 = ids.clone()
+    ids2[:, 3] = (ids2[:, 3] + 5) % wl.experts.E
+    d2 = rl.prefill(x, ids2, w0, ex)
+    assert torch.equal(d1, d2)
+    # x = 0 gives exactly 0
+    z = rl.prefill(torch.zeros_like(x), ids, w, ex)
+    assert torch.count_nonzero(z).item() == 0
+
+
+def test_back_to_back_calls_no_sync(orc, rl, cases):
+    """Two calls with different routing, different workspaces, one stream, no host sync in
+    between: both correct (per-call tables never live in shared library buffers)."""
+    import torch
+
+    wl = _case(cases, "med_t1")
+    x, ids, w, ex = to_device(wl)
+    ids_b = torch.flip(ids, dims=[1]).contiguous()
+    w_b = torch.flip(w, dims=[1]).contiguous()
+    ws1 = rl.alloc_workspace(wl.T, wl.k, ex)
+    ws2 = rl.alloc_workspace(wl.T, wl.k, ex)
+    o1 = rl.prefill(x, ids, w, ex, ws=ws1)
+    o2 = rl.prefill(x, ids_b, w_b, ex, ws=ws2)
+    o3 = rl.prefill(x, ids, w, ex, ws=ws1)
+    torch.cuda.synchronize()
+    ref = orc.moe_workload(wl)
+    assert rel_l2(o1.cpu().numpy(), ref) <= TOL
+    ex_np = wl.experts
+    ref_b = orc.moe_prefill(wl.x, wl.ids[:, ::-1].copy(), wl.w[:, ::-1].copy(), ex_np.arena, ex_np.desc, ex_np.E,
+                            ex_np.H, ex_np.I)
+    assert rel_l2(o2.cpu().numpy(), ref_b) <= TOL
+    assert torch.equal(o1, o3)
+
+
+def test_empty_input(rl, cases):
+    import torch
+
+    wl = _case(cases, "tiny_q2b")
+    _, _, _, ex = to_device(wl)
+    ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.zeros((0, 2), dtype=torch.float32, device="cuda")
+    x = torch.zeros((0, 256), dtype=torch.int16, device="cuda")
+    out = rl.prefill(x, ids, w, ex)
+    assert out.shape == (0, 256)
+
+
+def test_bad_expert_id_flagged(orc, rl, cases):
+    wl = _case(cases, "tiny_q2b")
+    x, ids, w, ex = to_device(wl)
+    ids[5, 1] = wl.experts.E + 3
+    ws = rl.alloc_workspace(wl.T, wl.k, ex)
+    out = rl.prefill(x, ids, w, ex, ws=ws).cpu().numpy()
+    assert rl.status(ws)[0] & 1
+    ref = orc.moe_workload(wl)
+    keep = np.ones(wl.T, bool)
+    keep[5] = False
+    assert rel_l2(out[keep], ref[keep]) <= TOL
+
+
+# ----------------------------------------------------------------------------- 1-2 rows
+@pytest.mark.parametrize("types", ["t1", "q2b", "mixed"])
+def test_decode_rows_parity_and_bit_identity(orc, rl, types):
+    import torch
+
+    ex_np = make_experts(64, 2048, 512, {"t1": QTYPE_T1, "q2b": QTYPE_Q2B, "mixed": [QTYPE_Q2B] * 32 + [QTYPE_T1] * 32}[types], seed=40)
+    wl = make_workload("decode_t1", seed=41, T=2, experts=ex_np, E=64)
+    wl.ids[1, :3] = wl.ids[0, :3]  # the two rows share some experts
+    x, ids, w, ex = to_device(wl)
+    log(f"decode {types}")
+    two = rl.decode(x, ids, w, ex)
+    one0 = rl.decode(x[:1], ids[:1], w[:1], ex)
+    one1 = rl.decode(x[1:], ids[1:], w[1:], ex)
+    assert torch.equal(two[0], one0[0])
+    assert torch.equal(two[1], one1[0])
+    ref = orc.moe_workload(wl)
+    err = rel_l2(two.cpu().numpy(), ref)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
+    # the matrix-vector path and the prefill path agree within the same bar
+    pre = rl.prefill(x, ids, w, ex)
+    assert rel_l2(two.cpu().numpy(), pre.cpu().numpy()) <= TOL
+
+
+# ----------------------------------------------------------------------------- full size
+FULL = {
+    "q2b_1090": dict(),
+    "t1_2048": dict(),
+    "mixed_2048": dict(),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_parity(orc, rl, name):
+    """Full-size layer on the GPU (the bench's launch configuration); the oracle recomputes a
+    seeded sample of 48 tokens one by one."""
+    wl = make_workload(name, seed=7)
+    log(f"full {name} T={wl.T} pairs/expert min={np.bincount(wl.ids.ravel(), minlength=wl.experts.E).min()} "
+        f"max={np.bincount(wl.ids.ravel(), minlength=wl.experts.E).max()}")
+    x, ids, w, ex = to_device(wl)
+    out = rl.prefill(x, ids, w, ex).cpu().numpy()
+    tok = np.sort(np.random.default_rng(5).choice(wl.T, size=48, replace=False)).astype(np.int32)
+    ref = orc.moe_workload(wl, tokens=tok)
+    err = rel_l2(out[tok], ref)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
+    assert np.all(np.isfinite(out))
