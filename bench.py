@@ -95,6 +95,9 @@ def main():
 
     # same number of steps with events between the stages (on the stream the kernels run on)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for row in evs:  # torch creates the HIP event on its first record
+        for e in row:
+            e.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
         rl.prefill_timed(x, ids, w, sets[i % len(sets)], out, ws, evs[i])
