@@ -59,8 +59,9 @@ typedef struct rl_expert_desc {
     uint64_t down_off;
 } rl_expert_desc;
 
-/* The experts of one layer.  arena [dev]: packed blocks.  desc [dev]: E descriptors (read by
- * the kernels).  desc_host [host]: the same E descriptors (read by the host to decide which
+/* The experts of one layer.  arena [dev]: packed blocks, 4-byte aligned, its allocation a
+ * whole number of dwords; every matrix offset a multiple of 4 (RL_EINVAL otherwise).  desc
+ * [dev]: E descriptors (read by the kernels).  desc_host [host]: the same E descriptors (read by the host to decide which
  * type-specialised kernels to launch).  E in [1, 1024].  H (hidden) a multiple of 256 in
  * [256, 8192].  I (expert intermediate) a multiple of 64 in [64, 4096] that is either a
  * multiple of 256 or one of 64 / 128. */

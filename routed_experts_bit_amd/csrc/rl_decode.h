@@ -1,5 +1,5 @@
-// Decode of the Q2B and T1 expert blocks (host + device code, no intrinsics, so the same
-// routine is exercised by a CPU unit test and runs inside the gfx950 kernels).
+// Decode of the Q2B and T1 expert blocks (host + device code, so the same routine is
+// exercised by a CPU unit test and runs inside the gfx950 kernels).
 //
 // The matrix kernels never materialise decoded weights in memory (Red Lite dev75, "Prompt
 // ingestion": dequantising whole experts per chunk would write gigabytes per layer).  Each
@@ -17,9 +17,16 @@
 // A T1 strip first turns its (up to 14) digit bytes into one 2-bit digit stream through
 // `tern`, shifted so that the strip's first value is digit 0; the stream (and a Q2B strip's
 // code bytes directly) is then read 8 bits = 4 values at a time through `val`.
+//
+// A strip is handled in two phases so that kernels can issue the loads of the next block
+// long before decoding it: StripRaw::load issues aligned dword loads only (block header and
+// the strip's byte window), Strip::prepare turns them into code words, Strip::frag returns
+// operands.  Loads never touch a dword that holds no byte of the matrix: reads go through a
+// source whose device form is a buffer resource over the matrix (out-of-range dwords read 0).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 namespace rl {
 
@@ -32,14 +39,17 @@ template <>
 struct Fmt<QT_Q2B> {
     static constexpr int BYTES = 74;
     static constexpr int NSCALE = 16;
+    static constexpr int HDR_DW = 4;  // bytes 0..9 of a block at any alignment
 };
 template <>
 struct Fmt<QT_T1> {
     static constexpr int BYTES = 57;
     static constexpr int NSCALE = 8;
+    static constexpr int HDR_DW = 2;  // bytes 0..4 of a block at any alignment
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ scalar helpers
 __host__ __device__ inline float half_bits_to_float(uint32_t h) {
@@ -55,6 +65,10 @@ __host__ __device__ inline uint32_t int_to_op16(int v) {
     } else {
         return __builtin_bit_cast(uint32_t, f) >> 16;  // low 16 bits are zero for these values
     }
+}
+
+__host__ __device__ inline uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t bytes) {
+    return (uint32_t)((((uint64_t)hi << 32) | lo) >> (8 * bytes));
 }
 
 // ------------------------------------------------------------------ tables
@@ -87,108 +101,154 @@ __host__ __device__ constexpr int val_entries() {
     return Fmt<QT>::NSCALE * 256;
 }
 
-// ------------------------------------------------------------------ byte windows
-// Bytes p[0..nb) as little-endian dwords out[0..(nb+3)/4), loading only the aligned dwords
-// that contain at least one requested byte (so a window never reads past the dword that
-// holds the last byte of the arena).
-template <int MAXW>
-__host__ __device__ inline void load_window(const uint8_t* p, int nb, uint32_t out[MAXW]) {
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t* base = (const uint32_t*)(a & ~(uintptr_t)3);
-    const int m = (int)(a & 3);
-    const int ndw = (m + nb + 3) >> 2;
-    uint32_t dw[MAXW + 1];
-#pragma unroll
-    for (int i = 0; i <= MAXW; ++i) dw[i] = i < ndw ? base[i] : 0u;
-#pragma unroll
-    for (int i = 0; i < MAXW; ++i) {
-        uint64_t pair = ((uint64_t)dw[i + 1] << 32) | dw[i];
-        out[i] = (uint32_t)(pair >> (8 * m));
+// ------------------------------------------------------------------ memory sources
+// Plain pointer (host tests; device code with a padded buffer).
+struct PtrSrc {
+    const uint8_t* p;
+    __host__ __device__ inline uint32_t dw(uint32_t off) const {
+        uint32_t v;
+        memcpy(&v, p + off, 4);
+        return v;
     }
-}
+    __host__ __device__ inline void dw4(uint32_t off, uint32_t o[4]) const {
+        for (int i = 0; i < 4; ++i) o[i] = dw(off + 4 * i);
+    }
+    __host__ __device__ inline void dw2(uint32_t off, uint32_t o[2]) const {
+        o[0] = dw(off);
+        o[1] = dw(off + 4);
+    }
+};
 
-__host__ __device__ inline uint32_t byte_of(const uint32_t* w, int i) { return (w[i >> 2] >> (8 * (i & 3))) & 255u; }
+// Buffer resource over one matrix of the arena (offsets are bytes from the matrix start; the
+// base is 4-byte aligned and the range is rounded up to whole dwords).
+struct BufSrc {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ inline BufSrc(const void* base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)((bytes + 3u) & ~3u), 0x00020000)) {}
+    __device__ inline uint32_t dw(uint32_t off) const { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ inline void dw4(uint32_t off, uint32_t o[4]) const {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        o[0] = v[0];
+        o[1] = v[1];
+        o[2] = v[2];
+        o[3] = v[3];
+    }
+    __device__ inline void dw2(uint32_t off, uint32_t o[2]) const {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        o[0] = v[0];
+        o[1] = v[1];
+    }
+};
 
-// ------------------------------------------------------------------ strip decoder
-// A strip: STRIP consecutive values (STRIP in {16, 32, 64}) of one row inside one block,
-// starting at value vs (a multiple of 8).  After `load` and `prepare`, frag(f) returns the
-// operand of values vs+8f .. vs+8f+7 (value vs+8f+i in 16-bit element i).
-template <int QT, bool F16, int STRIP>
+// ------------------------------------------------------------------ strips
+// STRIP consecutive values (16, 32 or 64) of one row inside one block, starting at value vs
+// (a multiple of 8).  Raw dwords: the aligned dwords of the block header and of the strip's
+// byte window.
+template <int QT, int STRIP>
+struct StripRaw {
+    static constexpr int HW = Fmt<QT>::HDR_DW;
+    static constexpr int WB = QT == QT_Q2B ? STRIP / 4 : (STRIP + 4 + 4) / 5;  // window bytes
+    static constexpr int WW = (WB + 3 + 3) / 4;                                // window dwords
+    uint32_t h[HW];
+    uint32_t w[WW];
+    uint32_t hm, wm;  // misalignment (bytes) of header and window
+    int vs;
+
+    template <class Src>
+    __host__ __device__ inline void load(const Src& src, uint32_t blk_off, int v) {
+        vs = v;
+        hm = blk_off & 3u;
+        const uint32_t ha = blk_off - hm;
+        if constexpr (HW == 4)
+            src.dw4(ha, h);
+        else
+            src.dw2(ha, h);
+        uint32_t woff;
+        if constexpr (QT == QT_Q2B)
+            woff = blk_off + 10u + (uint32_t)(v >> 2);
+        else
+            woff = blk_off + 5u + (uint32_t)(v / 5);
+        wm = woff & 3u;
+        const uint32_t wa = woff - wm;
+        if constexpr (WW >= 4) {
+            src.dw4(wa, w);
+            if constexpr (WW == 5) w[4] = src.dw(wa + 16);
+        } else if constexpr (WW == 3) {
+            src.dw2(wa, w);
+            w[2] = src.dw(wa + 8);
+        } else {
+            src.dw2(wa, w);
+        }
+    }
+};
+
+template <int QT, int STRIP>
 struct Strip {
     static constexpr int NFRAG = STRIP / 8;
-    static constexpr int TB = (STRIP + 4 + 4) / 5 + 1;  // T1 digit bytes loaded (>= needed)
-    static constexpr int TW = (TB + 3) / 4 + 1;         // their dwords
-    static constexpr int SW = (STRIP * 2 + 31) / 32;    // dwords of the shifted digit stream
-    const uint8_t* blk;
-    int vs;
-    uint32_t hdr[3];    // block bytes 0..9 (Q2B: d + 16 scales; T1: d + scale word)
-    uint32_t raw[TW];   // T1 digit bytes / Q2B code bytes of the strip
-    uint32_t code[SW];  // 2-bit codes of values vs.. (T1 after the stream shift)
+    static constexpr int SW = (STRIP * 2 + 31) / 32;      // dwords of 2-bit codes
+    static constexpr int FPS = QT == QT_T1 ? 4 : 2;       // fragments per sub-scale
+    static constexpr int NSB = (NFRAG + FPS - 1) / FPS;   // sub-scales the strip touches
+    uint32_t code[SW];  // 2-bit codes of values vs..vs+STRIP-1
+    uint32_t sb[NSB];   // value-table row (s * 256) of each sub-scale; 0 everywhere when d = 0
+    float d;            // block scale applied to the integer dot product
 
-    __host__ __device__ inline void load(const uint8_t* b, int v) {
-        blk = b;
-        vs = v;
+    // vs must be a multiple of min(STRIP, sub-scale span): strips never straddle a sub-scale
+    // boundary except at fragment-group boundaries (true for every strip the kernels use).
+    __host__ __device__ inline void prepare(const StripRaw<QT, STRIP>& raw, const uint32_t* tern) {
+        const int vs = raw.vs;
+        const uint32_t h0 = funnel(raw.h[1], raw.h[0], raw.hm);
         if constexpr (QT == QT_Q2B) {
-            load_window<3>(b, 10, hdr);
-            load_window<TW>(b + 10 + (v >> 2), STRIP / 4, raw);
+            const uint32_t h1 = funnel(raw.h[2], raw.h[1], raw.hm);
+            const uint32_t h2 = funnel(raw.h[3], raw.h[2], raw.hm);
+            d = half_bits_to_float(h0 & 0xFFFFu) * 0.5f;
+            // scale bytes 2..9 as one 64-bit word: nibble j = sub-scale of values 16j..16j+15
+            const uint64_t sw = ((uint64_t)h2 << 48) | ((uint64_t)h1 << 16) | (h0 >> 16);
+#pragma unroll
+            for (int i = 0; i < NSB; ++i) sb[i] = (uint32_t)((sw >> (4 * ((vs >> 4) + i))) & 15u) << 8;
         } else {
-            load_window<3>(b, 5, hdr);
-            const int b0 = v / 5;
-            const int last = (v + STRIP - 1) / 5;
-            load_window<TW>(b + 5 + b0, last - b0 + 1, raw);
+            const uint32_t h1 = funnel(0u, raw.h[1], raw.hm);
+            d = half_bits_to_float(h0 & 0xFFFFu);
+            const uint32_t sw = (h0 >> 16) | ((h1 & 255u) << 16);
+#pragma unroll
+            for (int i = 0; i < NSB; ++i) sb[i] = ((sw >> (3 * ((vs >> 5) + i))) & 7u) << 8;
         }
-    }
-
-    __host__ __device__ inline float scale() const {
-        float d = half_bits_to_float(hdr[0] & 0xFFFFu);
-        return QT == QT_Q2B ? d * 0.5f : d;
-    }
-
-    __host__ __device__ inline int subscale(int f) const {
-        const int v = vs + 8 * f;
-        if constexpr (QT == QT_Q2B) {
-            const int j = v >> 4;
-            return (int)((byte_of(hdr, 2 + (j >> 1)) >> (4 * (j & 1))) & 15u);
-        } else {
-            const uint32_t sc = (hdr[0] >> 16) | ((hdr[1] & 255u) << 16);
-            return (int)((sc >> (3 * (v >> 5))) & 7u);
+        if (d == 0.0f) {
+#pragma unroll
+            for (int i = 0; i < NSB; ++i) sb[i] = 0u;  // s = 0 rows of the value table are zero
         }
-    }
-
-    // T1: digit stream through the tern table; Q2B: the code bytes are the stream.
-    __host__ __device__ inline void prepare(const uint32_t* tern) {
+        constexpr int AW = StripRaw<QT, STRIP>::WW - 1;
+        uint32_t a[AW];
+#pragma unroll
+        for (int i = 0; i < AW; ++i) a[i] = funnel(raw.w[i + 1], raw.w[i], raw.wm);
         if constexpr (QT == QT_Q2B) {
 #pragma unroll
-            for (int i = 0; i < SW; ++i) code[i] = raw[i];
+            for (int i = 0; i < SW; ++i) code[i] = a[i];
         } else {
             const int b0 = vs / 5;
             const int r = vs - 5 * b0;
-            const int nb = (vs + STRIP - 1) / 5 - b0 + 1;
+            constexpr int NB = StripRaw<QT, STRIP>::WB;
             uint32_t st[SW + 1];
 #pragma unroll
             for (int i = 0; i <= SW; ++i) st[i] = 0u;
 #pragma unroll
-            for (int i = 0; i < TB; ++i) {
-                if (i < nb) {
-                    const uint32_t c = tern[byte_of(raw, i)];
-                    const int bit = 10 * i;
-                    if (bit / 32 <= SW) st[bit / 32] |= c << (bit % 32);
-                    if ((bit % 32) > 22 && bit / 32 + 1 <= SW) st[bit / 32 + 1] |= c >> (32 - bit % 32);
-                }
+            for (int i = 0; i < NB; ++i) {
+                const uint32_t c = tern[(a[i >> 2] >> (8 * (i & 3))) & 255u];
+                const int bit = 10 * i;
+                if (bit / 32 <= SW) st[bit / 32] |= c << (bit % 32);
+                if ((bit % 32) > 22 && bit / 32 + 1 <= SW) st[bit / 32 + 1] |= c >> (32 - bit % 32);
             }
 #pragma unroll
-            for (int i = 0; i < SW; ++i) {
-                uint64_t pair = ((uint64_t)st[i + 1] << 32) | st[i];
-                code[i] = (uint32_t)(pair >> (2 * r));
-            }
+            for (int i = 0; i < SW; ++i) code[i] = (uint32_t)((((uint64_t)st[i + 1] << 32) | st[i]) >> (2 * r));
         }
     }
 
+    // operand of fragment f (values vs+8f..vs+8f+7); f must be a compile-time constant in
+    // kernels so that the code words stay in registers
     __host__ __device__ inline u32x4 frag(int f, const uint64_t* val) const {
         const uint32_t w = code[f >> 1] >> (16 * (f & 1));
-        const int sbase = subscale(f) << 8;
-        const uint64_t lo = val[sbase + (int)(w & 255u)];
-        const uint64_t hi = val[sbase + (int)((w >> 8) & 255u)];
+        const uint32_t base = sb[f / FPS];
+        const uint64_t lo = val[base + (w & 255u)];
+        const uint64_t hi = val[base + ((w >> 8) & 255u)];
         u32x4 r;
         r[0] = (uint32_t)lo;
         r[1] = (uint32_t)(lo >> 32);

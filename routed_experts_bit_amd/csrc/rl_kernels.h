@@ -171,15 +171,30 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(GroupArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Work item -> (expert rank, column slice).  Work-groups are dispatched round-robin over the
-// 8 XCDs and a persistent work-group w only takes items i = w (mod gridDim), gridDim being a
-// multiple of 8, so i % 8 is the XCD: every slice of one expert runs on the same XCD (its
-// gathered activation rows are read through one L2), and ranks 0..7 -- the largest experts --
-// come first.
-__device__ __forceinline__ void item_to_work(int item, int ns, int& rank, int& slice) {
-    int xcd = item & 7, local = item >> 3;
+// Scheduling of the expert GEMMs.  Work item = (expert rank, column slice); ranks come from the
+// per-type work list, longest expert first.  Work-groups are dispatched round-robin over the 8
+// XCDs, so blockIdx % 8 is the XCD; every XCD owns the ranks r = xcd (mod 8) and hands them out
+// in order through its own counter (zeroed by k_group), so all slices of one expert run on the
+// same XCD (its gathered activation rows are read through one L2) and the XCD's work-groups
+// balance themselves.
+// flags[16 + 8*(2*stage + type - 1) + xcd]: per-XCD item counters, one set per stage and type
+constexpr int CNT_BASE = 16;
+__host__ __device__ constexpr int counter_set(int stage, int qtype) { return CNT_BASE + 8 * (2 * stage + qtype - 1); }
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+    return ((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) | (uint32_t)uni((int)(uint32_t)v);
+}
+
+__device__ __forceinline__ bool next_item(int32_t* counters, int ns, int n_ranks, int* sh, int& rank, int& slice) {
+    const int xcd = blockIdx.x & 7;
+    if (threadIdx.x == 0) *sh = atomicAdd(&counters[xcd], 1);
+    __syncthreads();
+    const int local = uni(*sh);  // the same for the whole work-group
+    __syncthreads();
     rank = (local / ns) * 8 + xcd;
     slice = local % ns;
+    return rank < n_ranks;
 }
 
 // Decode tables of one block type, built once per (persistent) work-group.
@@ -194,6 +209,56 @@ struct DecodeTables {
     }
 };
 
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// Running block scale: the accumulator holds sum_b (d_b / d_cur) * S_b, so each new block only
+// rescales it by d_prev/d_cur and the MFMA adds the integer dot product S_b directly.  A block
+// with d = 0 contributes nothing (its operands are zero, see Strip::prepare) and keeps the scale.
+struct RunScale {
+    float dprev = 1.0f;
+    __device__ __forceinline__ float step(float d) {
+        const float eff = d == 0.0f ? dprev : d;
+        const float r = dprev * __builtin_amdgcn_rcpf(eff);
+        dprev = eff;
+        return r;
+    }
+};
+
+// Activation chunk of the K loop: for each of the 4 lane groups, CS*8 consecutive k of its
+// strip; staged as [64 rows][4 groups][CS*8] halfwords (+8 pad per row), 16-byte pieces.
+template <int CS, int NTHR>
+struct ChunkShape {
+    static constexpr int SEG = CS * 8;          // k values per group per chunk
+    static constexpr int LDA = 4 * SEG + 8;     // halfwords per staged row
+    static constexpr int PIECES = 4 * SEG / 8;  // 16-byte pieces per row
+    static constexpr int TOTAL = 64 * PIECES;   // pieces per chunk
+    static constexpr int PER_THREAD = (TOTAL + NTHR - 1) / NTHR;
+};
+
+// Staging of one activation chunk by the NTHR threads of a work-group: thread tid owns pieces
+// tid + NTHR*i (row = piece / PIECES); `off` are byte offsets of the pieces' sources (row,
+// group, position) without the chunk's own k offset.
+template <int CS, int NTHR>
+struct Stager {
+    using CH = ChunkShape<CS, NTHR>;
+    uint32_t off[CH::PER_THREAD];
+    u32x4 v[CH::PER_THREAD];
+    __device__ __forceinline__ void load(const BufSrc& src, uint32_t koff, int tid) {
+#pragma unroll
+        for (int i = 0; i < CH::PER_THREAD; ++i)
+            if (CH::TOTAL % NTHR == 0 || tid + NTHR * i < CH::TOTAL)
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(src.r, off[i] + koff, 0, 0);
+    }
+    __device__ __forceinline__ void store(uint16_t* As, int tid) const {
+#pragma unroll
+        for (int i = 0; i < CH::PER_THREAD; ++i) {
+            const int idx = tid + NTHR * i;
+            if (CH::TOTAL % NTHR == 0 || idx < CH::TOTAL)
+                *(u32x4*)&As[(idx / CH::PIECES) * CH::LDA + 8 * (idx % CH::PIECES)] = v[i];
+        }
+    }
+};
+
 struct GateUpArgs {
     const uint16_t* x;
     const uint8_t* arena;
@@ -202,103 +267,128 @@ struct GateUpArgs {
     const int32_t* pair_src;
     const int32_t* worklist;  // this type's list
     const int32_t* wl_len;    // this type's list length (device)
+    int32_t* counters;        // 8 per-XCD item counters
     uint16_t* hbuf;           // [P][I] fp16, sorted-pair order
-    int H, I, k, ns, n_items;
+    int H, I, k, ns;
 };
 
-// One work item = one expert x (16*NTI*NW) intermediate columns; wave w owns NTI gate tiles
-// and the NTI up tiles of the same columns, so SwiGLU is elementwise in registers.  For each
+// K loop of one 64-pair chunk with MT 16-row tiles, NT weight tiles per wave (NTI gate + NTI
+// up), 256-value blocks in two chunks of 4 MFMA steps.
+template <int QT, int NW, int NTI, int MT>
+__device__ __forceinline__ void gateup_chunk(const GateUpArgs& a, const DecodeTables<QT, false>& tab,
+                                             uint16_t (*As)[64 * ChunkShape<4, 64 * NW>::LDA], const BufSrc& srcx,
+                                             const BufSrc& srcg, const BufSrc& srcu, Stager<4, 64 * NW>& sx,
+                                             const uint32_t* roff, int nkb, f32x4 (&acc)[4][2 * NTI],
+                                             RunScale* rs) {
+    constexpr int NT = 2 * NTI;
+    constexpr int BB = Fmt<QT>::BYTES;
+    using CH = ChunkShape<4, 64 * NW>;
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    StripRaw<QT, 64> raw[NT];
+    Strip<QT, 64> st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], 64 * g);
+    sx.load(srcx, 0u, tid);
+    __syncthreads();  // the previous chunk's readers are done with As
+    sx.store(As[0], tid);
+    sx.load(srcx, 64u, tid);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            st[t].prepare(raw[t], tab.tern);
+            const float r = rs[t].step(st[t].d);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
+            __builtin_amdgcn_sched_barrier(0);  // one tile's table lookups in flight at a time
+        }
+        if (kb + 1 < nkb) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                raw[t].load(t < NTI ? srcg : srcu, roff[t] + (uint32_t)(kb + 1) * BB, 64 * g);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint16_t* Ab = As[half];
+#pragma unroll
+            for (int f4 = 0; f4 < 4; ++f4) {
+                u32x4 b[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) b[t] = st[t].frag(4 * half + f4, tab.val);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const u32x4 av = *(const u32x4*)&Ab[(mt * 16 + n) * CH::LDA + 32 * g + 8 * f4];
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[mt][t] = mfma_bf16(av, b[t], acc[mt][t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight to one step
+            }
+            // chunk c = 2kb + half is done: stage c+1 into the other buffer, fetch c+2
+            const int c = 2 * kb + half;
+            if (c + 1 < 2 * nkb) sx.store(As[half ^ 1], tid);
+            if (c + 2 < 2 * nkb) sx.load(srcx, 2u * (uint32_t)(((c + 2) >> 1) * 256 + ((c + 2) & 1) * 32), tid);
+            __syncthreads();
+        }
+    }
+}
+
+// One work item = one expert x (16*NTI*NW) intermediate columns; wave w owns NTI gate tiles and
+// the NTI up tiles of the same columns, so SwiGLU is elementwise in registers.  For each
 // 64-pair chunk of the expert every weight of the slice is decoded exactly once (straight into
 // MFMA operands) and used for all of the chunk's 16-row pair tiles.  Lane (n, g) of a tile
 // decodes values 64g..64g+63 of each 256-value block of weight row n; the activation operand
-// takes the same k positions.
+// of step f takes the same k positions (64g + 8f .. +7).  The next block's strips and the next
+// activation chunk are loaded into registers one stage ahead.
 template <int QT, int NW, int NTI>
-__global__ __launch_bounds__(64 * NW, 1) void k_gateup(GateUpArgs a) {
+__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup(GateUpArgs a) {
     constexpr int NTHR = 64 * NW;
     constexpr int NT = 2 * NTI;
-    constexpr int LDA = 256 + 8;
     constexpr int BB = Fmt<QT>::BYTES;
-    constexpr int LOADS = 64 * 32 / NTHR;  // 16-byte pieces of the 64 x 256 activation tile
-    constexpr int ROWS_PER_PASS = NTHR / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t As[64 * LDA];
+    using CH = ChunkShape<4, NTHR>;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * CH::LDA];
     __shared__ DecodeTables<QT, false> tab;
+    __shared__ int item_sh;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
     tab.build(tid, NTHR);
     __syncthreads();
-    const int n_ranks = *a.wl_len;
+    const int n_ranks = uni(*a.wl_len);
     const int nkb = a.H >> 8;
-
-    for (int item = blockIdx.x; item < a.n_items; item += gridDim.x) {
-        int rank, slice;
-        item_to_work(item, a.ns, rank, slice);
-        if (rank >= n_ranks) break;
-        const int e = a.worklist[rank];
-        const int p0 = a.offsets[e], ne = a.offsets[e + 1] - p0;
-        const rl_expert_desc dsc = a.desc[e];
+    const uint32_t row_bytes = (uint32_t)nkb * BB;
+    const uint32_t mat_bytes = (uint32_t)a.I * row_bytes;
+    const BufSrc srcx(a.x, 0x7FFFFFF0u);
+    int rank, slice;
+    while (next_item(a.counters, a.ns, n_ranks, &item_sh, rank, slice)) {
+        const int e = uni(a.worklist[rank]);
+        const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
+        const BufSrc srcg(a.arena + uni64(a.desc[e].gate_off), mat_bytes);
+        const BufSrc srcu(a.arena + uni64(a.desc[e].up_off), mat_bytes);
         const int colw = slice * (16 * NTI * NW) + wave * (16 * NTI);
-        const uint8_t* wrow[NT];
+        uint32_t roff[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            wrow[t] = a.arena + (t < NTI ? dsc.gate_off : dsc.up_off) + (size_t)(colw + 16 * (t % NTI) + n) * nkb * BB;
+        for (int t = 0; t < NT; ++t) roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
 
         for (int mc = 0; mc < ne; mc += 64) {
             const int rows = min(64, ne - mc);
             const int mtiles = (rows + 15) >> 4;
-            int tok[LOADS];
+            Stager<4, NTHR> sx;
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                int row = (tid >> 5) + ROWS_PER_PASS * i;
-                tok[i] = row < rows ? a.pair_src[p0 + mc + row] / a.k : -1;
+            for (int i = 0; i < CH::PER_THREAD; ++i) {
+                const int idx = tid + NTHR * i;
+                const int row = idx / CH::PIECES, pc = idx % CH::PIECES;
+                const int tok = a.pair_src[p0 + mc + (row < rows ? row : 0)] / a.k;
+                sx.off[i] = 2u * ((uint32_t)tok * (uint32_t)a.H + 64u * (pc >> 2) + 8u * (pc & 3));
             }
             f32x4 acc[4][NT];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-            for (int kb = 0; kb < nkb; ++kb) {
-                Strip<QT, false, 64> st[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) st[t].load(wrow[t] + (size_t)kb * BB, 64 * g);
-                __syncthreads();
-#pragma unroll
-                for (int i = 0; i < LOADS; ++i) {
-                    int row = (tid >> 5) + ROWS_PER_PASS * i, ch = tid & 31;
-                    u32x4 v = {0u, 0u, 0u, 0u};
-                    if (tok[i] >= 0) v = *(const u32x4*)(a.x + (size_t)tok[i] * a.H + kb * 256 + ch * 8);
-                    *(u32x4*)&As[row * LDA + ch * 8] = v;
-                }
-                __syncthreads();
-                float ds[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    st[t].prepare(tab.tern);
-                    ds[t] = st[t].scale();
-                }
-                f32x4 blk[4][NT];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) blk[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int f = 0; f < 8; ++f) {
-                    u32x4 b[NT];
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) b[t] = st[t].frag(f, tab.val);
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        if (mt < mtiles) {
-                            u32x4 av = *(const u32x4*)&As[(mt * 16 + n) * LDA + 64 * g + 8 * f];
-#pragma unroll
-                            for (int t = 0; t < NT; ++t) blk[mt][t] = mfma_bf16(av, b[t], blk[mt][t]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    if (mt < mtiles)
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) acc[mt][t] += ds[t] * blk[mt][t];
+            RunScale rs[NT];
+            switch (mtiles) {
+                case 1: gateup_chunk<QT, NW, NTI, 1>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
+                case 2: gateup_chunk<QT, NW, NTI, 2>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
+                case 3: gateup_chunk<QT, NW, NTI, 3>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
+                default: gateup_chunk<QT, NW, NTI, 4>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
             }
             // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
 #pragma unroll
@@ -308,10 +398,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gateup(GateUpArgs a) {
                     for (int ti = 0; ti < NTI; ++ti)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            int r = mt * 16 + 4 * g + i;
+                            const int r = mt * 16 + 4 * g + i;
                             if (r < rows) {
-                                float hv = silu(acc[mt][ti][i]) * acc[mt][NTI + ti][i];
-                                a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(hv);
+                                const float gv = acc[mt][ti][i] * rs[ti].dprev;
+                                const float uv = acc[mt][NTI + ti][i] * rs[NTI + ti].dprev;
+                                a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] =
+                                    f32_to_f16_bits(silu_fast(gv) * uv);
                             }
                         }
                 }
@@ -328,108 +420,136 @@ struct DownArgs {
     const int32_t* pair_src;
     const int32_t* worklist;
     const int32_t* wl_len;
+    int32_t* counters;
     float* yslot;  // [T*k][H] fp32, row t*k + j
-    int H, I, ns, n_items;
+    int H, I, ns;
 };
 
-// One work item = one expert x (16*NTW*NW) output columns.  K runs over the intermediate
-// dimension in chunks of LCH = min(I, 256) values, each inside one block of every W_down row;
-// lane (n, g) decodes values LCH/4*g .. LCH/4*(g+1)-1 of the chunk.
-template <int QT, int LCH, int NW, int NTW>
-__global__ __launch_bounds__(64 * NW, 1) void k_down(DownArgs a) {
-    constexpr int NTHR = 64 * NW;
-    constexpr int LDA = LCH + 8;
+template <int QT, int LCH, int NW, int NTW, int MT>
+__device__ __forceinline__ void down_chunk(const DownArgs& a, const DecodeTables<QT, true>& tab,
+                                           uint16_t (*As)[64 * ChunkShape<(LCH / 32 < 4 ? LCH / 32 : 4), 64 * NW>::LDA],
+                                           const BufSrc& srch, const BufSrc& src,
+                                           Stager<(LCH / 32 < 4 ? LCH / 32 : 4), 64 * NW>& sx, int col0,
+                                           f32x4 (&acc)[4][NTW], RunScale* rs) {
     constexpr int BB = Fmt<QT>::BYTES;
     constexpr int STRIP = LCH / 4;
     constexpr int NFRAG = STRIP / 8;
-    constexpr int CH_PER_ROW = LCH / 8;
-    constexpr int LOADS = (64 * CH_PER_ROW + NTHR - 1) / NTHR;
-    __shared__ __attribute__((aligned(16))) uint16_t As[64 * LDA];
+    constexpr int CS = NFRAG < 4 ? NFRAG : 4;  // steps per chunk
+    constexpr int CPB = NFRAG / CS;            // chunks per K block
+    using CH = ChunkShape<CS, 64 * NW>;
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int nkc = a.I / LCH;
+    StripRaw<QT, STRIP> raw[NTW];
+    Strip<QT, STRIP> st[NTW];
+    auto rload = [&](int kc) {
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const uint32_t flat = (uint32_t)(col0 + 16 * t + n) * (uint32_t)a.I + (uint32_t)kc * LCH;
+            raw[t].load(src, (flat >> 8) * BB, (int)(flat & 255) + STRIP * g);
+        }
+    };
+    auto koff = [&](int c) { return 2u * (uint32_t)((c / CPB) * LCH + (c % CPB) * CH::SEG); };
+    const int nch = CPB * nkc;
+    rload(0);
+    sx.load(srch, 0u, tid);
+    __syncthreads();
+    sx.store(As[0], tid);
+    if (nch > 1) sx.load(srch, koff(1), tid);
+    __syncthreads();
+    for (int kc = 0; kc < nkc; ++kc) {
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            st[t].prepare(raw[t], tab.tern);
+            const float r = rs[t].step(st[t].d);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
+            __builtin_amdgcn_sched_barrier(0);  // one tile's table lookups in flight at a time
+        }
+        if (kc + 1 < nkc) rload(kc + 1);
+#pragma unroll
+        for (int part = 0; part < CPB; ++part) {
+            const int c = CPB * kc + part;
+            const uint16_t* Ab = As[c & 1];
+#pragma unroll
+            for (int f4 = 0; f4 < CS; ++f4) {
+                u32x4 b[NTW];
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) b[t] = st[t].frag(CS * part + f4, tab.val);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const u32x4 av = *(const u32x4*)&Ab[(mt * 16 + n) * CH::LDA + CH::SEG * g + 8 * f4];
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) acc[mt][t] = mfma_f16(av, b[t], acc[mt][t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight to one step
+            }
+            if (c + 1 < nch) sx.store(As[(c + 1) & 1], tid);
+            if (c + 2 < nch) sx.load(srch, koff(c + 2), tid);
+            __syncthreads();
+        }
+    }
+}
+
+// One work item = one expert x (16*NTW*NW) output columns.  K runs over the intermediate
+// dimension in blocks of LCH = min(I, 256) values (each inside one block of every W_down row);
+// lane (n, g) decodes values LCH/4*g .. LCH/4*(g+1)-1 of each; activation chunks as k_gateup.
+template <int QT, int LCH, int NW, int NTW>
+__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
+    constexpr int NTHR = 64 * NW;
+    constexpr int BB = Fmt<QT>::BYTES;
+    constexpr int STRIP = LCH / 4;
+    constexpr int NFRAG = STRIP / 8;
+    constexpr int CS = NFRAG < 4 ? NFRAG : 4;
+    using CH = ChunkShape<CS, NTHR>;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * CH::LDA];
     __shared__ DecodeTables<QT, true> tab;
+    __shared__ int item_sh;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
     tab.build(tid, NTHR);
     __syncthreads();
-    const int n_ranks = *a.wl_len;
-    const int nkc = a.I / LCH;
-
-    for (int item = blockIdx.x; item < a.n_items; item += gridDim.x) {
-        int rank, slice;
-        item_to_work(item, a.ns, rank, slice);
-        if (rank >= n_ranks) break;
-        const int e = a.worklist[rank];
-        const int p0 = a.offsets[e], ne = a.offsets[e + 1] - p0;
-        const uint8_t* Wd = a.arena + a.desc[e].down_off;
+    const int n_ranks = uni(*a.wl_len);
+    const uint32_t mat_bytes = (uint32_t)((size_t)a.H * a.I / 256 * BB);
+    const BufSrc srch(a.hbuf, 0x7FFFFFF0u);
+    int rank, slice;
+    while (next_item(a.counters, a.ns, n_ranks, &item_sh, rank, slice)) {
+        const int e = uni(a.worklist[rank]);
+        const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
+        const BufSrc src(a.arena + uni64(a.desc[e].down_off), mat_bytes);
         const int col0 = slice * (16 * NTW * NW) + wave * (16 * NTW);
 
         for (int mc = 0; mc < ne; mc += 64) {
             const int rows = min(64, ne - mc);
             const int mtiles = (rows + 15) >> 4;
+            Stager<CS, NTHR> sx;
+#pragma unroll
+            for (int i = 0; i < CH::PER_THREAD; ++i) {
+                const int idx = tid + NTHR * i;
+                const int row = idx / CH::PIECES, pc = idx % CH::PIECES;
+                sx.off[i] = 2u * ((uint32_t)(p0 + mc + (row < rows ? row : 0)) * (uint32_t)a.I +
+                                  (uint32_t)(STRIP * (pc / (CH::PIECES / 4)) + 8 * (pc % (CH::PIECES / 4))));
+            }
             f32x4 acc[4][NTW];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int kc = 0; kc < nkc; ++kc) {
-                Strip<QT, true, STRIP> st[NTW];
-#pragma unroll
-                for (int t = 0; t < NTW; ++t) {
-                    size_t flat = (size_t)(col0 + 16 * t + n) * a.I + (size_t)kc * LCH;
-                    st[t].load(Wd + (flat >> 8) * BB, (int)(flat & 255) + STRIP * g);
-                }
-                __syncthreads();
-#pragma unroll
-                for (int i = 0; i < LOADS; ++i) {
-                    int idx = tid + NTHR * i;
-                    if (idx < 64 * CH_PER_ROW) {
-                        int row = idx / CH_PER_ROW, ch = idx % CH_PER_ROW;
-                        u32x4 v = {0u, 0u, 0u, 0u};
-                        if (row < rows)
-                            v = *(const u32x4*)(a.hbuf + (size_t)(p0 + mc + row) * a.I + kc * LCH + ch * 8);
-                        *(u32x4*)&As[row * LDA + ch * 8] = v;
-                    }
-                }
-                __syncthreads();
-                float ds[NTW];
-#pragma unroll
-                for (int t = 0; t < NTW; ++t) {
-                    st[t].prepare(tab.tern);
-                    ds[t] = st[t].scale();
-                }
-                f32x4 blk[4][NTW];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int t = 0; t < NTW; ++t) blk[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int f = 0; f < NFRAG; ++f) {
-                    u32x4 b[NTW];
-#pragma unroll
-                    for (int t = 0; t < NTW; ++t) b[t] = st[t].frag(f, tab.val);
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        if (mt < mtiles) {
-                            u32x4 av = *(const u32x4*)&As[(mt * 16 + n) * LDA + STRIP * g + 8 * f];
-#pragma unroll
-                            for (int t = 0; t < NTW; ++t) blk[mt][t] = mfma_f16(av, b[t], blk[mt][t]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    if (mt < mtiles)
-#pragma unroll
-                        for (int t = 0; t < NTW; ++t) acc[mt][t] += ds[t] * blk[mt][t];
+            RunScale rs[NTW];
+            switch (mtiles) {
+                case 1: down_chunk<QT, LCH, NW, NTW, 1>(a, tab, As, srch, src, sx, col0, acc, rs); break;
+                case 2: down_chunk<QT, LCH, NW, NTW, 2>(a, tab, As, srch, src, sx, col0, acc, rs); break;
+                case 3: down_chunk<QT, LCH, NW, NTW, 3>(a, tab, As, srch, src, sx, col0, acc, rs); break;
+                default: down_chunk<QT, LCH, NW, NTW, 4>(a, tab, As, srch, src, sx, col0, acc, rs); break;
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (mt < mtiles) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        int r = mt * 16 + 4 * g + i;
+                        const int r = mt * 16 + 4 * g + i;
                         if (r < rows) {
                             float* yrow = a.yslot + (size_t)a.pair_src[p0 + mc + r] * a.H + col0 + n;
 #pragma unroll
-                            for (int t = 0; t < NTW; ++t) yrow[16 * t] = acc[mt][t][i];
+                            for (int t = 0; t < NTW; ++t) yrow[16 * t] = acc[mt][t][i] * rs[t].dprev;
                         }
                     }
                 }
@@ -465,10 +585,12 @@ struct GvTables {
 // sum over the S values of one strip (inside one block) of w_i * xs[i], times the block scale;
 // xs is bf16 bits (XS_BF16) or fp32.  Fixed order: i ascending, then the scale.
 template <int QT, int S, bool XS_BF16>
-__device__ __forceinline__ float strip_dot(const uint8_t* blk, int vs, const void* xs, const DecodeTables<QT, false>& tb) {
-    Strip<QT, false, S> st;
-    st.load(blk, vs);
-    st.prepare(tb.tern);
+__device__ __forceinline__ float strip_dot(const BufSrc& src, uint32_t blk_off, int vs, const void* xs,
+                                           const DecodeTables<QT, false>& tb) {
+    StripRaw<QT, S> raw;
+    raw.load(src, blk_off, vs);
+    Strip<QT, S> st;
+    st.prepare(raw, tb.tern);
     float part = 0.f;
 #pragma unroll
     for (int f = 0; f < S / 8; ++f) {
@@ -480,25 +602,27 @@ __device__ __forceinline__ float strip_dot(const uint8_t* blk, int vs, const voi
             part = __fmaf_rn(wv, xv, part);
         }
     }
-    return part * st.scale();
+    return part * st.d;
 }
 
-// span values of row `row` of a [rows x C] matrix starting at column c0, strips of S
+// span values of row `row` of a [rows x C] matrix (mat_bytes long) starting at column c0,
+// strips of S
 template <int QMASK, int S, bool XS_BF16>
-__device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, int C, int row, int c0, int span, const void* xs,
-                                         const GvTables<QMASK>& tb) {
+__device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, uint32_t mat_bytes, int C, int row, int c0,
+                                         int span, const void* xs, const GvTables<QMASK>& tb) {
+    const BufSrc src(W, mat_bytes);
     float acc = 0.f;
     for (int s = 0; s < span; s += S) {
-        const size_t flat = (size_t)row * C + c0 + s;
+        const uint32_t flat = (uint32_t)row * (uint32_t)C + (uint32_t)(c0 + s);
         const void* xp = XS_BF16 ? (const void*)((const uint16_t*)xs + s) : (const void*)((const float*)xs + s);
         if constexpr (QMASK & 2) {
             if (QMASK == 2 || qtype == QT_T1) {
-                acc += strip_dot<QT_T1, S, XS_BF16>(W + (flat >> 8) * Fmt<QT_T1>::BYTES, (int)(flat & 255), xp, tb.t1);
+                acc += strip_dot<QT_T1, S, XS_BF16>(src, (flat >> 8) * Fmt<QT_T1>::BYTES, (int)(flat & 255), xp, tb.t1);
                 continue;
             }
         }
         if constexpr (QMASK & 1)
-            acc += strip_dot<QT_Q2B, S, XS_BF16>(W + (flat >> 8) * Fmt<QT_Q2B>::BYTES, (int)(flat & 255), xp, tb.q2b);
+            acc += strip_dot<QT_Q2B, S, XS_BF16>(src, (flat >> 8) * Fmt<QT_Q2B>::BYTES, (int)(flat & 255), xp, tb.q2b);
     }
     return acc;
 }
@@ -538,7 +662,8 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
         if (e >= 0 && e < a.E) {
             const rl_expert_desc dsc = a.desc[e];
             const uint8_t* W = a.arena + (rs < 2 ? dsc.gate_off : dsc.up_off);
-            part = row_dot<QMASK, S1, true>(dsc.qtype, W, a.H, row, q * span, span, a.x + (size_t)r * a.H + q * span, tb);
+            const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 * (dsc.qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
+            part = row_dot<QMASK, S1, true>(dsc.qtype, W, mb, a.H, row, q * span, span, a.x + (size_t)r * a.H + q * span, tb);
         }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
@@ -569,7 +694,9 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
                     __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (e >= 0 && e < a.E) {
                     const rl_expert_desc dsc = a.desc[e];
-                    part = row_dot<QMASK, S2, false>(dsc.qtype, a.arena + dsc.down_off, a.I, c, q * span, span,
+                    const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 *
+                                                   (dsc.qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
+                    part = row_dot<QMASK, S2, false>(dsc.qtype, a.arena + dsc.down_off, mb, a.I, c, q * span, span,
                                                      a.hgv + (size_t)(r * a.k + j) * a.I + q * span, tb);
                 }
             }
@@ -597,17 +724,22 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blo
     if (t >= n_blocks * 4) return;
     const int64_t b = t >> 2;
     const int g = (int)(t & 3);
-    Strip<QT, false, 64> st;
-    st.load(blocks + b * Fmt<QT>::BYTES, 64 * g);
-    st.prepare(tab.tern);
-    const float d = st.scale();
+    // a buffer window of the single block (with its alignment preserved) keeps loads in bounds
+    const uintptr_t base = (uintptr_t)(blocks + b * Fmt<QT>::BYTES);
+    const uint32_t mis = (uint32_t)(base & 3);
+    const uint8_t* b4 = (const uint8_t*)(base - mis);
+    const BufSrc src(b4, mis + Fmt<QT>::BYTES);
+    StripRaw<QT, 64> raw;
+    raw.load(src, mis, 64 * g);
+    Strip<QT, 64> st;
+    st.prepare(raw, tab.tern);
     float* o = out + b * 256 + 64 * g;
     for (int f = 0; f < 8; ++f) {
         const u32x4 fr = st.frag(f, tab.val);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            o[8 * f + 2 * i] = __uint_as_float(fr[i] << 16) * d;
-            o[8 * f + 2 * i + 1] = __uint_as_float(fr[i] & 0xFFFF0000u) * d;
+            o[8 * f + 2 * i] = __uint_as_float(fr[i] << 16) * st.d;
+            o[8 * f + 2 * i + 1] = __uint_as_float(fr[i] & 0xFFFF0000u) * st.d;
         }
     }
 }

@@ -72,10 +72,13 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
     if (!x || !ids || !w || !out || !ex->arena || !ex->desc || !ex->desc_host) return RL_EINVAL;
     if (!ws || ((uintptr_t)ws % ALIGN)) return RL_EWORKSPACE;
     if (ws_bytes < layout(T, k, ex->E, ex->H, ex->I).total) return RL_EWORKSPACE;
+    if ((uintptr_t)ex->arena & 3) return RL_EINVAL;
     present[0] = present[1] = present[2] = 0;
     for (int e = 0; e < ex->E; ++e) {
-        int q = ex->desc_host[e].qtype;
+        const rl_expert_desc& dd = ex->desc_host[e];
+        int q = dd.qtype;
         if (q != QT_Q2B && q != QT_T1) return RL_EQTYPE;
+        if ((dd.gate_off | dd.up_off | dd.down_off) & 3) return RL_EINVAL;
         present[q] += 1;
     }
     return RL_OK;
@@ -97,23 +100,38 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
     hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, s, g);
 }
 
-// Persistent grids: at most two work-groups per CU (256 CUs), a multiple of 8 so that a
-// work-group always stays on one XCD's share of the items.
-constexpr int MAX_GRID = 512;
-int items_for(int n_experts, int ns) { return ((n_experts + 7) / 8) * 8 * ns; }
-int grid_for(int n_items) { return n_items < MAX_GRID ? n_items : MAX_GRID; }
+// Persistent grids: as many work-groups as fit on the device at once (occupancy query, cached
+// per kernel), a multiple of 8 so that every XCD gets the same number.
+template <typename K>
+int resident_grid(K kernel, int block) {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, cus = 256, per_cu = 1;
+        if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+        cached = ((cus * per_cu + 7) / 8) * 8;
+    }
+    return cached;
+}
 
+int grid_cap(int grid, int n_experts, int ns) {
+    const int items = ((n_experts + 7) / 8) * 8 * ns;
+    return grid < items ? grid : items;
+}
+
+// Gate/up: 8 waves x (1 gate + 1 up tile) = 128 intermediate columns per work item when
+// I % 128 == 0, else 4 waves (64 columns).  Down: 8 waves x 2 tiles = 256 output columns.
 template <int QT>
 void launch_gateup_t(const GateUpArgs& a, int n_experts, hipStream_t s) {
     GateUpArgs b = a;
     if (a.I % 128 == 0) {
         b.ns = a.I / 128;
-        b.n_items = items_for(n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup<QT, 4, 2>), dim3(grid_for(b.n_items)), dim3(256), 0, s, b);
+        const int grid = grid_cap(resident_grid(k_gateup<QT, 8, 1>, 512), n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup<QT, 8, 1>), dim3(grid), dim3(512), 0, s, b);
     } else {
         b.ns = a.I / 64;
-        b.n_items = items_for(n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup<QT, 4, 1>), dim3(grid_for(b.n_items)), dim3(256), 0, s, b);
+        const int grid = grid_cap(resident_grid(k_gateup<QT, 4, 1>, 256), n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup<QT, 4, 1>), dim3(grid), dim3(256), 0, s, b);
     }
 }
 
@@ -121,14 +139,16 @@ template <int QT>
 void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
     DownArgs b = a;
     b.ns = a.H / 256;
-    b.n_items = items_for(n_experts, b.ns);
-    dim3 grid(grid_for(b.n_items));
-    if (a.I % 256 == 0)
-        hipLaunchKernelGGL((k_down<QT, 256, 4, 4>), grid, dim3(256), 0, s, b);
-    else if (a.I == 128)
-        hipLaunchKernelGGL((k_down<QT, 128, 4, 4>), grid, dim3(256), 0, s, b);
-    else
-        hipLaunchKernelGGL((k_down<QT, 64, 4, 4>), grid, dim3(256), 0, s, b);
+    if (a.I % 256 == 0) {
+        const int grid = grid_cap(resident_grid(k_down<QT, 256, 8, 2>, 512), n_experts, b.ns);
+        hipLaunchKernelGGL((k_down<QT, 256, 8, 2>), dim3(grid), dim3(512), 0, s, b);
+    } else if (a.I == 128) {
+        const int grid = grid_cap(resident_grid(k_down<QT, 128, 8, 2>, 512), n_experts, b.ns);
+        hipLaunchKernelGGL((k_down<QT, 128, 8, 2>), dim3(grid), dim3(512), 0, s, b);
+    } else {
+        const int grid = grid_cap(resident_grid(k_down<QT, 64, 8, 2>, 512), n_experts, b.ns);
+        hipLaunchKernelGGL((k_down<QT, 64, 8, 2>), dim3(grid), dim3(512), 0, s, b);
+    }
 }
 
 bool gv_dim_ok(int d) { return d == 256 || d == 512 || (d % 1024 == 0); }
@@ -157,13 +177,15 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
 
 // grouping + gate/up for every present type; returns the layout used
 void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blobs* ex, int32_t T, int32_t k,
-                      void* ws, const int present[3], uint16_t* hdst, hipStream_t s, Layout& L) {
+                      void* ws, const int present[3], uint16_t* hdst, hipStream_t s, Layout& L,
+                      void* ev_after_group = nullptr) {
     L = layout(T, k, ex->E, ex->H, ex->I);
     int32_t* flags = at<int32_t>(ws, L.flags);
     int32_t* offsets = at<int32_t>(ws, L.offsets);
     int32_t* pair_src = at<int32_t>(ws, L.pair_src);
     int32_t* worklist = at<int32_t>(ws, L.worklist);
     launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist, s);
+    if (ev_after_group) (void)hipEventRecord(static_cast<hipEvent_t>(ev_after_group), s);
     GateUpArgs a;
     a.x = x;
     a.arena = static_cast<const uint8_t*>(ex->arena);
@@ -175,16 +197,15 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     a.I = ex->I;
     a.k = k;
     a.ns = 1;
-    a.n_items = 0;
-    if (present[QT_Q2B]) {
-        a.worklist = worklist + (QT_Q2B - 1) * ex->E;
-        a.wl_len = flags + 8 + QT_Q2B;
-        launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
-    }
-    if (present[QT_T1]) {
-        a.worklist = worklist + (QT_T1 - 1) * ex->E;
-        a.wl_len = flags + 8 + QT_T1;
-        launch_gateup_t<QT_T1>(a, present[QT_T1], s);
+    for (int q = QT_Q2B; q <= QT_T1; ++q) {
+        if (!present[q]) continue;
+        a.worklist = worklist + (q - 1) * ex->E;
+        a.wl_len = flags + 8 + q;
+        a.counters = flags + counter_set(0, q);
+        if (q == QT_Q2B)
+            launch_gateup_t<QT_Q2B>(a, present[q], s);
+        else
+            launch_gateup_t<QT_T1>(a, present[q], s);
     }
 }
 
@@ -215,24 +236,12 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     int32_t* worklist = at<int32_t>(workspace, L.worklist);
     float* yslot = at<float>(workspace, L.yslot);
     mark(0);
-    launch_group(topk_ids, T, k, experts->E, experts->desc, offsets, pair_src, at<int32_t>(workspace, L.inv), flags,
-                 worklist, s);
-    mark(1);
-    GateUpArgs a;
-    a.x = x;
-    a.arena = static_cast<const uint8_t*>(experts->arena);
-    a.desc = experts->desc;
-    a.offsets = offsets;
-    a.pair_src = pair_src;
-    a.hbuf = hbuf;
-    a.H = experts->H;
-    a.I = experts->I;
-    a.k = k;
-    a.ns = 1;
-    a.n_items = 0;
+    Layout L2;  // same layout as L
+    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events ? events[1] : nullptr);
+    mark(2);
     DownArgs d;
     d.hbuf = hbuf;
-    d.arena = a.arena;
+    d.arena = static_cast<const uint8_t*>(experts->arena);
     d.desc = experts->desc;
     d.offsets = offsets;
     d.pair_src = pair_src;
@@ -240,27 +249,15 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     d.H = experts->H;
     d.I = experts->I;
     d.ns = 1;
-    d.n_items = 0;
-    if (present[QT_Q2B]) {
-        a.worklist = worklist + (QT_Q2B - 1) * experts->E;
-        a.wl_len = flags + 8 + QT_Q2B;
-        launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
-    }
-    if (present[QT_T1]) {
-        a.worklist = worklist + (QT_T1 - 1) * experts->E;
-        a.wl_len = flags + 8 + QT_T1;
-        launch_gateup_t<QT_T1>(a, present[QT_T1], s);
-    }
-    mark(2);
-    if (present[QT_Q2B]) {
-        d.worklist = worklist + (QT_Q2B - 1) * experts->E;
-        d.wl_len = flags + 8 + QT_Q2B;
-        launch_down_t<QT_Q2B>(d, present[QT_Q2B], s);
-    }
-    if (present[QT_T1]) {
-        d.worklist = worklist + (QT_T1 - 1) * experts->E;
-        d.wl_len = flags + 8 + QT_T1;
-        launch_down_t<QT_T1>(d, present[QT_T1], s);
+    for (int q = QT_Q2B; q <= QT_T1; ++q) {
+        if (!present[q]) continue;
+        d.worklist = worklist + (q - 1) * experts->E;
+        d.wl_len = flags + 8 + q;
+        d.counters = flags + counter_set(1, q);
+        if (q == QT_Q2B)
+            launch_down_t<QT_Q2B>(d, present[q], s);
+        else
+            launch_down_t<QT_T1>(d, present[q], s);
     }
     mark(3);
     hipLaunchKernelGGL(k_combine, dim3(experts->H / 256, T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);

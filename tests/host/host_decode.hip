@@ -16,12 +16,13 @@ static void run(const uint8_t* blocks, int64_t nblocks, float* out) {
     for (int i = 0; i < val_entries<QT>(); ++i) val[i] = val_entry<QT, F16>(i);
     uint32_t tern[256];
     for (int i = 0; i < 256; ++i) tern[i] = tern_entry((uint32_t)i);
+    const PtrSrc src{blocks};
     for (int64_t b = 0; b < nblocks; ++b) {
         for (int vs = 0; vs < 256; vs += STRIP) {
-            Strip<QT, F16, STRIP> st;
-            st.load(blocks + b * Fmt<QT>::BYTES, vs);
-            st.prepare(tern);
-            const float d = st.scale();
+            StripRaw<QT, STRIP> raw;
+            raw.load(src, (uint32_t)(b * Fmt<QT>::BYTES), vs);
+            Strip<QT, STRIP> st;
+            st.prepare(raw, tern);
             for (int f = 0; f < STRIP / 8; ++f) {
                 u32x4 fr = st.frag(f, val.data());
                 for (int i = 0; i < 8; ++i) {
@@ -33,7 +34,7 @@ static void run(const uint8_t* blocks, int64_t nblocks, float* out) {
                         uint32_t u = h << 16;
                         memcpy(&v, &u, 4);
                     }
-                    out[b * 256 + vs + 8 * f + i] = v * d;
+                    out[b * 256 + vs + 8 * f + i] = v * st.d;
                 }
             }
         }

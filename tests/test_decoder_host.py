@@ -54,10 +54,13 @@ def _blocks(qtype, nb, seed):
 @pytest.mark.parametrize("mis", [0, 1, 2, 3])
 def test_strip_decoder_matches_oracle(orc, harness, qtype, f16, strip, mis):
     blk, nb = _blocks(qtype, 40, seed=100 + qtype)
-    buf = np.zeros(blk.size + 16, np.uint8)
+    # the decoder reads whole aligned dwords around each block: keep the buffer 4-aligned and
+    # padded, and place the blocks at every misalignment
+    buf = np.zeros(blk.size + 32, np.uint8)
     buf[mis : mis + blk.size] = blk
     out = np.empty(nb * 256, np.float32)
-    rc = harness.hd_decode(qtype, f16, strip, buf.ctypes.data + mis, nb, out.ctypes.data)
+    base = buf.ctypes.data
+    rc = harness.hd_decode(qtype, f16, strip, base + mis, nb, out.ctypes.data)
     assert rc == 0
     ref = orc.dequant(qtype, blk, nb * 256)
     assert np.array_equal(out.astype(np.float64), ref), np.nonzero(out != ref)[0][:10]
