@@ -113,11 +113,11 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
  *   offsets  [dev] int32 [E+1], exclusive prefix sum of the per-expert pair counts
  *   pair_src [dev] int32 [T*k], t*k + j of the pair at each sorted position
  *   inv      [dev] int32 [T*k], sorted position of pair (t, j); -1 for an invalid id
- *   flags    [dev] int32 [4], bit 0 of flags[0] set if an id is outside [0, E); the call
- *            clears the flags first.
+ *   workspace [dev], 256-byte aligned, at least rl_moe_workspace_bytes(T, k, E, 256, 64)
+ *            bytes; an id outside [0, E) sets bit 0 of the status flags (rl_moe_status).
  * T*k <= 2^24, E in [1, 1024]. */
 int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,
-                       int32_t* pair_src, int32_t* inv, int32_t* flags, void* stream);
+                       int32_t* pair_src, int32_t* inv, void* workspace, size_t ws_bytes, void* stream);
 
 /* Block decode alone (parity hook for the in-kernel weight decode): n_values (a multiple of
  * 256) consecutive values of `blocks` [dev] as float d * s * c into out [dev].  Uses the same

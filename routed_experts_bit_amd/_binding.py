@@ -66,7 +66,7 @@ def lib():
         getattr(L, name).restype = C.c_int
     L.rl_moe_prefill_timed.argtypes = layer + [C.POINTER(C.c_void_p)]
     L.rl_moe_prefill_timed.restype = C.c_int
-    L.rl_moe_group_pairs.argtypes = [P, I32, I32, I32, P, P, P, P, P]
+    L.rl_moe_group_pairs.argtypes = [P, I32, I32, I32, P, P, P, P, SZ, P]
     L.rl_moe_group_pairs.restype = C.c_int
     L.rl_moe_dequant.argtypes = [I32, P, C.c_int64, P, P]
     L.rl_moe_dequant.restype = C.c_int
@@ -209,16 +209,19 @@ def gate_up(x, ids, w, ex: DeviceExperts, h=None, ws=None):
 
 
 def group_pairs(ids, E: int):
+    """Returns (offsets[E+1], pair_src[T*k], inv[T*k], workspace) as device tensors; the
+    workspace holds the status flags (see status())."""
     torch = _torch()
     T, k = ids.shape
     dev = ids.device
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     pair_src = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
     inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
-    flags = torch.empty(64, dtype=torch.int32, device=dev)
-    rc = lib().rl_moe_group_pairs(_ptr(ids), T, k, E, _ptr(offsets), _ptr(pair_src), _ptr(inv), _ptr(flags), _stream())
+    ws = torch.empty(workspace_bytes(max(T, 1), k, E, 256, 64), dtype=torch.uint8, device=dev)
+    rc = lib().rl_moe_group_pairs(_ptr(ids), T, k, E, _ptr(offsets), _ptr(pair_src), _ptr(inv), _ptr(ws), ws.numel(),
+                                  _stream())
     _check(rc, "rl_moe_group_pairs")
-    return offsets, pair_src[: T * k], inv[: T * k], flags
+    return offsets, pair_src[: T * k], inv[: T * k], ws
 
 
 def dequant(qtype: int, blocks_u8, n_values: int, out=None):

@@ -1,6 +1,6 @@
 // HIP kernels of the routed-expert MoE layer for gfx950 (wave64, MFMA 16x16x32).
 //
-//   k_group      token-expert pairs grouped per expert (stable, deterministic), plus the
+//   k_group_*    token-expert pairs grouped per expert (stable, deterministic), plus the
 //                per-type expert work lists, longest expert first
 //   k_gateup     fused block decode + gate/up grouped GEMM (bf16 MFMA) + SwiGLU -> h (fp16)
 //   k_down       fused block decode + down grouped GEMM (fp16 MFMA) -> y per pair (fp32)
@@ -25,8 +25,6 @@ constexpr int FLAG_BAD_ID = 1;
 constexpr int FLAG_BAD_QTYPE = 2;
 constexpr int FLAGS_WORDS = 64;   // flags[0] error bits; flags[8 + q] work-list length of type q
 constexpr int MAX_E = 1024;
-constexpr int GROUP_THREADS = 512;
-constexpr int GROUP_WAVES = GROUP_THREADS / 64;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -44,10 +42,20 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return __builtin_
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // ---------------------------------------------------------------------------------------
-// Pair grouping.  One workgroup of 8 waves.  Wave w owns a contiguous run of the flattened
-// pairs p = t*k + j; its pairs of expert e land after those of waves < w, in order, so the
-// sorted order is (expert, token, slot).  Inside a wave, lanes holding the same expert are
-// found with ballots over the bits of the id and ranked by lane number.
+// Pair grouping: two kernels over tiles of GT consecutive flattened pairs p = t*k + j.
+//   k_group_count    per-tile expert histograms (and the clearing of the status words);
+//   k_group_scatter  per tile: the pairs of expert e in earlier tiles (sum of their
+//                    histograms) plus the exclusive scan of all counts place the tile's pairs;
+//                    inside the tile wave w owns a contiguous run and lanes holding the same
+//                    expert are found with ballots over the bits of the id and ranked by lane.
+// The sorted order is (expert, token, slot), identical to a sequential stable sort.  Tile 0
+// also writes the offsets and the per-type work lists (experts with pairs, more pairs first;
+// ties and experts above 255 pairs come in no particular order: the lists only steer
+// scheduling).
+constexpr int GT = 1024;           // pairs per tile
+constexpr int GROUP_NTHR = 256;    // threads per grouping work-group
+constexpr int NBIN = 256;
+
 struct GroupArgs {
     const int32_t* ids;
     const rl_expert_desc* desc;  // may be NULL: no work lists
@@ -55,118 +63,156 @@ struct GroupArgs {
     int32_t* pair_src;
     int32_t* inv;
     int32_t* flags;
-    int32_t* worklist;  // [2][E]: experts of type q with pairs, most pairs first
-    int P, E;
-    int nflags;         // flag words to clear (4 for the grouping entry point, FLAGS_WORDS in a layer)
+    int32_t* worklist;  // [2][E]
+    int32_t* tile_hist; // [ntiles][E]
+    int P, E, ntiles;
+    int nflags;         // status words to clear
 };
 
-__global__ __launch_bounds__(GROUP_THREADS) void k_group(GroupArgs a) {
-    __shared__ int32_t hist[GROUP_WAVES][MAX_E];
+__global__ __launch_bounds__(GROUP_NTHR) void k_group_count(GroupArgs a) {
+    __shared__ int32_t h[MAX_E];
+    const int tid = threadIdx.x, tile = blockIdx.x;
+    if (tile == 0 && tid < a.nflags) a.flags[tid] = 0;
+    for (int e = tid; e < a.E; e += GROUP_NTHR) h[e] = 0;
+    __syncthreads();
+    const int p0 = tile * GT, p1 = min(a.P, p0 + GT);
+    for (int p = p0 + tid; p < p1; p += GROUP_NTHR) {
+        const int e = a.ids[p];
+        if (e >= 0 && e < a.E) atomicAdd(&h[e], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < a.E; e += GROUP_NTHR) a.tile_hist[(size_t)tile * a.E + e] = h[e];
+}
+
+__global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
+    constexpr int NW = GROUP_NTHR / 64;
+    constexpr int SUB = GT / NW;
+    __shared__ int32_t ids_sh[GT];
+    __shared__ int32_t before[MAX_E];  // pairs of e in earlier tiles
     __shared__ int32_t tot[MAX_E];
     __shared__ int32_t scan[MAX_E];
-    __shared__ int32_t qt[MAX_E];
-    __shared__ int32_t wl_len[3];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int E = a.E, P = a.P;
-    if (tid < a.nflags) __hip_atomic_exchange(&a.flags[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < 3) wl_len[tid] = 0;
-    for (int i = tid; i < GROUP_WAVES * MAX_E; i += GROUP_THREADS) (&hist[0][0])[i] = 0;
-    __syncthreads();
-
-    const int chunk = (P + GROUP_WAVES - 1) / GROUP_WAVES;
-    const int p_begin = min(P, wave * chunk), p_end = min(P, p_begin + chunk);
-    int bad = 0;
-    for (int base = p_begin; base < p_end; base += 64) {
-        int p = base + lane;
-        if (p < p_end) {
-            int e = a.ids[p];
-            if (e >= 0 && e < E)
-                atomicAdd(&hist[wave][e], 1);
-            else
-                bad = 1;
-        }
-    }
-    if (bad) __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-
-    // per expert: prefix over waves (in place) and the total
-    for (int e = tid; e < MAX_E; e += GROUP_THREADS) {
-        int run = 0;
+    __shared__ int32_t whist[NW][MAX_E];
+    __shared__ int32_t bins[2][NBIN];
+    __shared__ int32_t bad_sh;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tile = blockIdx.x;
+    const int E = a.E;
+    const int p0 = tile * GT, n = min(a.P - p0, GT);
+    if (tid == 0) bad_sh = 0;
+    for (int i = tid; i < GT; i += GROUP_NTHR) ids_sh[i] = i < n ? a.ids[p0 + i] : -1;
+    for (int e = tid; e < MAX_E; e += GROUP_NTHR) {
+        int b = 0, t = 0;
         if (e < E) {
-#pragma unroll
-            for (int w = 0; w < GROUP_WAVES; ++w) {
-                int c = hist[w][e];
-                hist[w][e] = run;
-                run += c;
+            for (int tl = 0; tl < a.ntiles; ++tl) {
+                const int c = a.tile_hist[(size_t)tl * E + e];
+                b += tl < tile ? c : 0;
+                t += c;
             }
         }
-        tot[e] = run;
-        scan[e] = run;
+        before[e] = b;
+        tot[e] = t;
+        scan[e] = t;
     }
+    for (int i = tid; i < NW * MAX_E; i += GROUP_NTHR) (&whist[0][0])[i] = 0;
     __syncthreads();
-    // inclusive scan of tot over experts (Hillis-Steele, two elements per thread)
+    // inclusive scan of the totals (Hillis-Steele, four elements per thread)
     for (int off = 1; off < MAX_E; off <<= 1) {
-        int v0 = tid >= off ? scan[tid - off] : 0;
-        int v1 = tid + GROUP_THREADS >= off ? scan[tid + GROUP_THREADS - off] : 0;
+        int v[MAX_E / GROUP_NTHR];
+#pragma unroll
+        for (int i = 0; i < MAX_E / GROUP_NTHR; ++i) {
+            const int e = tid + GROUP_NTHR * i;
+            v[i] = e >= off ? scan[e - off] : 0;
+        }
         __syncthreads();
-        scan[tid] += v0;
-        scan[tid + GROUP_THREADS] += v1;
+#pragma unroll
+        for (int i = 0; i < MAX_E / GROUP_NTHR; ++i) scan[tid + GROUP_NTHR * i] += v[i];
         __syncthreads();
     }
-    for (int e = tid; e <= E; e += GROUP_THREADS) a.offsets[e] = e == 0 ? 0 : scan[e - 1];
-
-    // stable scatter
+    // wave-local counts of the tile
+    const int r_begin = wave * SUB, r_end = min(r_begin + SUB, n);
+    int bad = 0;
+    for (int i = r_begin + lane; i < r_end; i += 64) {
+        const int e = ids_sh[i];
+        if (e >= 0 && e < E)
+            atomicAdd(&whist[wave][e], 1);
+        else
+            bad = 1;
+    }
+    if (bad) atomicOr(&bad_sh, 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += GROUP_NTHR) {
+        int run = scan[e] - tot[e] + before[e];  // exclusive offset of e + pairs of e in earlier tiles
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int c = whist[w][e];
+            whist[w][e] = run;
+            run += c;
+        }
+    }
+    if (tile == 0)
+        for (int e = tid; e <= E; e += GROUP_NTHR) a.offsets[e] = e == 0 ? 0 : scan[e - 1];
+    __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = p_begin; base < p_end; base += 64) {
-        int p = base + lane;
-        int e = -1;
-        if (p < p_end) e = a.ids[p];
-        bool ok = (e >= 0 && e < E);
+    for (int i0 = r_begin; i0 < r_end; i0 += 64) {
+        const int i = i0 + lane;
+        const int e = i < r_end ? ids_sh[i] : -1;
+        const bool ok = (e >= 0 && e < E);
         uint64_t peers = __ballot(ok);
         for (int bit = 0; bit < 10; ++bit) {
-            uint64_t m = __ballot(ok && ((e >> bit) & 1));
+            const uint64_t m = __ballot(ok && ((e >> bit) & 1));
             peers &= ((e >> bit) & 1) ? m : ~m;
         }
         if (ok) {
-            int rank = __popcll(peers & lt_mask);
-            int pos = (scan[e] - tot[e]) + hist[wave][e] + rank;
-            a.pair_src[pos] = p;
-            a.inv[p] = pos;
-        } else if (p < p_end) {
-            a.inv[p] = -1;
+            const int pos = whist[wave][e] + __popcll(peers & lt_mask);
+            a.pair_src[pos] = p0 + i;
+            a.inv[p0 + i] = pos;
+        } else if (i < r_end) {
+            a.inv[p0 + i] = -1;
         }
-        // make every lane's read of hist[wave][e] happen before the leader's update
+        // every lane's read of whist[wave][e] happens before the leaders' updates
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
-        if (ok && (peers & lt_mask) == 0) hist[wave][e] += __popcll(peers);
+        if (ok && (peers & lt_mask) == 0) whist[wave][e] += __popcll(peers);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
     }
+    __syncthreads();
+    if (tid == 0 && bad_sh) atomicOr(&a.flags[0], FLAG_BAD_ID);
 
-    // per-type work lists, experts with more pairs first (ties: lower id first)
-    if (a.desc != nullptr) {
-        for (int e = tid; e < MAX_E; e += GROUP_THREADS) qt[e] = e < E ? a.desc[e].qtype : 0;
+    // tile 0: per-type work lists, binned by pair count
+    if (tile == 0 && a.desc != nullptr) {
+        for (int i = tid; i < 2 * NBIN; i += GROUP_NTHR) (&bins[0][0])[i] = 0;
         __syncthreads();
-        for (int e = tid; e < E; e += GROUP_THREADS) {
-            int n = tot[e], q = qt[e];
+        for (int e = tid; e < E; e += GROUP_NTHR) {
+            const int q = a.desc[e].qtype, c = tot[e];
+            before[e] = -1;  // reused: list bin of e
+            if (c == 0) continue;
             if (q != QT_Q2B && q != QT_T1) {
-                if (n > 0) __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_QTYPE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                atomicOr(&bad_sh, 2);
                 continue;
             }
-            if (n == 0) continue;
-            int rank = 0;
-            for (int e2 = 0; e2 < E; ++e2) {
-                int n2 = tot[e2];
-                rank += (qt[e2] == q && n2 > 0 && (n2 > n || (n2 == n && e2 < e))) ? 1 : 0;
-            }
-            a.worklist[(q - 1) * E + rank] = e;
-            atomicAdd(&wl_len[q], 1);
+            const int b = c < NBIN - 1 ? c : NBIN - 1;
+            before[e] = (q - 1) * NBIN + b;
+            atomicAdd(&bins[q - 1][b], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-            a.flags[8 + QT_Q2B] = wl_len[QT_Q2B];
-            a.flags[8 + QT_T1] = wl_len[QT_T1];
+        if (tid < 2) {  // start of each bin in the type's list, high counts first
+            int run = 0;
+            for (int b = NBIN - 1; b >= 0; --b) {
+                const int c = bins[tid][b];
+                bins[tid][b] = run;
+                run += c;
+            }
+            a.flags[8 + QT_Q2B + tid] = run;
         }
+        __syncthreads();
+        for (int e = tid; e < E; e += GROUP_NTHR) {
+            const int key = before[e];
+            if (key < 0) continue;
+            const int q0 = key / NBIN, b = key % NBIN;
+            a.worklist[q0 * E + atomicAdd(&bins[q0][b], 1)] = e;
+        }
+        __syncthreads();
+        if (tid == 0 && (bad_sh & 2)) atomicOr(&a.flags[0], FLAG_BAD_QTYPE);
     }
 }
 
@@ -174,7 +220,7 @@ __global__ __launch_bounds__(GROUP_THREADS) void k_group(GroupArgs a) {
 // Scheduling of the expert GEMMs.  Work item = (expert rank, column slice); ranks come from the
 // per-type work list, longest expert first.  Work-groups are dispatched round-robin over the 8
 // XCDs, so blockIdx % 8 is the XCD; every XCD owns the ranks r = xcd (mod 8) and hands them out
-// in order through its own counter (zeroed by k_group), so all slices of one expert run on the
+// in order through its own counter (zeroed by k_group_count), so all slices of one expert run on the
 // same XCD (its gathered activation rows are read through one L2) and the XCD's work-groups
 // balance themselves.
 // flags[16 + 8*(2*stage + type - 1) + xcd]: per-XCD item counters, one set per stage and type
@@ -558,15 +604,22 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
     }
 }
 
-// out[t][c] = sum over j = 0..k-1 (ascending) of w[t][j] * y[t*k + j][c]
+// out[t][c] = sum over j = 0..k-1 (ascending) of w[t][j] * y[t*k + j][c]; one work-group per
+// token, four columns per thread (16-byte loads).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yslot, const float* __restrict__ w,
                                                  float* __restrict__ out, int k, int H) {
-    const int t = blockIdx.y;
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= H) return;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) acc = __fmaf_rn(w[(size_t)t * k + j], yslot[((size_t)t * k + j) * H + c], acc);
-    out[(size_t)t * H + c] = acc;
+    const int t = blockIdx.x;
+    const float* wt = w + (size_t)t * k;
+    for (int c = 4 * threadIdx.x; c < H; c += 4 * 256) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+            const float wj = wt[j];
+            const f32x4 y = *(const f32x4*)(yslot + ((size_t)t * k + j) * H + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __fmaf_rn(wj, y[i], acc[i]);
+        }
+        *(f32x4*)(out + (size_t)t * H + c) = acc;
+    }
 }
 
 // ---------------------------------------------------------------------------------------

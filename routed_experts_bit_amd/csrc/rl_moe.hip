@@ -20,8 +20,10 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, hbuf, yslot, total;
+    size_t flags, offsets, pair_src, inv, worklist, tile_hist, hbuf, yslot, total;
 };
+
+int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
 
 bool shape_ok(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     if (T < 0 || k < 1 || k > 16) return false;
@@ -47,6 +49,8 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + P * sizeof(int32_t));
     L.worklist = off;
     off = align_up(off + 2 * (size_t)E * sizeof(int32_t));
+    L.tile_hist = off;
+    off = align_up(off + (size_t)(group_tiles((int64_t)P) > 0 ? group_tiles((int64_t)P) : 1) * E * sizeof(int32_t));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
     L.yslot = off;
@@ -85,7 +89,8 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
 }
 
 void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
-                  int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, hipStream_t s) {
+                  int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, int32_t* tile_hist,
+                  hipStream_t s) {
     GroupArgs g;
     g.ids = ids;
     g.desc = desc;
@@ -94,10 +99,13 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
     g.inv = inv;
     g.flags = flags;
     g.worklist = worklist;
+    g.tile_hist = tile_hist;
     g.P = T * k;
     g.E = E;
-    g.nflags = desc ? FLAGS_WORDS : 4;
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, s, g);
+    g.ntiles = group_tiles(g.P) > 0 ? group_tiles(g.P) : 1;
+    g.nflags = FLAGS_WORDS;
+    hipLaunchKernelGGL(k_group_count, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
+    hipLaunchKernelGGL(k_group_scatter, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
 }
 
 // Persistent grids: as many work-groups as fit on the device at once (occupancy query, cached
@@ -184,7 +192,8 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     int32_t* offsets = at<int32_t>(ws, L.offsets);
     int32_t* pair_src = at<int32_t>(ws, L.pair_src);
     int32_t* worklist = at<int32_t>(ws, L.worklist);
-    launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist, s);
+    launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
+                 at<int32_t>(ws, L.tile_hist), s);
     if (ev_after_group) (void)hipEventRecord(static_cast<hipEvent_t>(ev_after_group), s);
     GateUpArgs a;
     a.x = x;
@@ -260,7 +269,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
             launch_down_t<QT_T1>(d, present[q], s);
     }
     mark(3);
-    hipLaunchKernelGGL(k_combine, dim3(experts->H / 256, T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
     mark(4);
     return hip_status();
 }
@@ -322,10 +331,16 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
 }
 
 int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets, int32_t* pair_src,
-                       int32_t* inv, int32_t* flags, void* stream) {
+                       int32_t* inv, void* workspace, size_t ws_bytes, void* stream) {
     if (T < 0 || k < 1 || k > 16 || E < 1 || E > MAX_E || (int64_t)T * k > (1 << 24)) return RL_ESHAPE;
-    if (!offsets || !flags || (T > 0 && (!topk_ids || !pair_src || !inv))) return RL_EINVAL;
-    launch_group(topk_ids, T, k, E, nullptr, offsets, pair_src, inv, flags, nullptr, static_cast<hipStream_t>(stream));
+    if (!offsets || (T > 0 && (!topk_ids || !pair_src || !inv))) return RL_EINVAL;
+    if (!workspace || ((uintptr_t)workspace % ALIGN)) return RL_EWORKSPACE;
+    const Layout L = layout(T, k, E, 256, 64);
+    if (ws_bytes < L.tile_hist + (size_t)(group_tiles((int64_t)T * k) > 0 ? group_tiles((int64_t)T * k) : 1) * E * 4)
+        return RL_EWORKSPACE;
+    launch_group(topk_ids, T, k, E, nullptr, offsets, pair_src, inv, at<int32_t>(workspace, L.flags),
+                 at<int32_t>(workspace, L.worklist), at<int32_t>(workspace, L.tile_hist),
+                 static_cast<hipStream_t>(stream));
     return hip_status();
 }
 

@@ -93,9 +93,12 @@ def test_dequant_and_group_codes(L):
     assert L.rl_moe_dequant(2, None, 0, None, None) == 0
     assert L.rl_moe_dequant(2, None, 256, None, None) == -1
     p = C.c_void_p(0x100)
-    assert L.rl_moe_group_pairs(p, 4, 17, 8, p, p, p, p, None) == -2
-    assert L.rl_moe_group_pairs(p, 4, 2, 1025, p, p, p, p, None) == -2
-    assert L.rl_moe_group_pairs(p, 4, 2, 8, None, p, p, p, None) == -1
+    ws = C.c_void_p(0x10000)
+    assert L.rl_moe_group_pairs(p, 4, 17, 8, p, p, p, ws, 1 << 20, None) == -2
+    assert L.rl_moe_group_pairs(p, 4, 2, 1025, p, p, p, ws, 1 << 20, None) == -2
+    assert L.rl_moe_group_pairs(p, 4, 2, 8, None, p, p, ws, 1 << 20, None) == -1
+    assert L.rl_moe_group_pairs(p, 4, 2, 8, p, p, p, None, 1 << 20, None) == -3
+    assert L.rl_moe_group_pairs(p, 4, 2, 8, p, p, p, ws, 16, None) == -3
 
 
 def test_strerror(L):

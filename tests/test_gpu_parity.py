@@ -64,7 +64,8 @@ def test_dequant_real_matrix(orc, rl, qtype):
 @pytest.mark.parametrize(
     "T,k,E,kind",
     [(1, 1, 1, "uniform"), (64, 2, 8, "uniform"), (2048, 10, 512, "uniform"), (1090, 10, 512, "skewed"),
-     (300, 16, 1024, "dup"), (4096, 8, 64, "uniform"), (5, 3, 1024, "uniform")],
+     (300, 16, 1024, "dup"), (4096, 8, 64, "uniform"), (5, 3, 1024, "uniform"), (8192, 10, 512, "skewed"),
+     (777, 13, 3, "uniform")],
 )
 def test_group_pairs_bit_exact(orc, rl, T, k, E, kind):
     import torch
@@ -78,20 +79,20 @@ def test_group_pairs_bit_exact(orc, rl, T, k, E, kind):
     else:
         ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
     log(f"group T={T} k={k} E={E} {kind}")
-    offsets, src, inv, flags = rl.group_pairs(torch.from_numpy(ids).cuda(), E)
+    offsets, src, inv, ws = rl.group_pairs(torch.from_numpy(ids).cuda(), E)
     o2, s2, i2 = orc.group_pairs(ids, E)
     assert np.array_equal(offsets.cpu().numpy(), o2)
     assert np.array_equal(src.cpu().numpy(), s2)
     assert np.array_equal(inv.cpu().numpy(), i2)
-    assert flags.cpu().numpy()[0] == 0
+    assert rl.status(ws)[0] == 0
 
 
 def test_group_pairs_flags_bad_id(rl):
     import torch
 
     ids = np.array([[0, 1], [5, 2], [3, -1]], np.int32)
-    offsets, src, inv, flags = rl.group_pairs(torch.from_numpy(ids).cuda(), 4)
-    assert flags.cpu().numpy()[0] & 1
+    offsets, src, inv, ws = rl.group_pairs(torch.from_numpy(ids).cuda(), 4)
+    assert rl.status(ws)[0] & 1
     inv = inv.cpu().numpy()
     assert inv[2] == -1 and inv[5] == -1
     good = [0, 1, 3, 4]
