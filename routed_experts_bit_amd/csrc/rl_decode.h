@@ -71,6 +71,17 @@ __host__ __device__ inline uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t by
     return (uint32_t)((((uint64_t)hi << 32) | lo) >> (8 * bytes));
 }
 
+// Bytes of `tbl` picked by the four selector bytes of `sel` (each 0..3).
+__host__ __device__ inline uint32_t byte_select(uint32_t tbl, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_perm(0u, tbl, sel);
+#else
+    uint32_t r = 0;
+    for (int b = 0; b < 4; ++b) r |= ((tbl >> (8 * ((sel >> (8 * b)) & 3u))) & 255u) << (8 * b);
+    return r;
+#endif
+}
+
 // ------------------------------------------------------------------ tables
 __host__ __device__ inline uint32_t tern_entry(uint32_t b) {
     if (b > 242) return 0x155u;  // five 1-digits
@@ -239,6 +250,20 @@ struct Strip {
             }
 #pragma unroll
             for (int i = 0; i < SW; ++i) code[i] = (uint32_t)((((uint64_t)st[i + 1] << 32) | st[i]) >> (2 * r));
+        }
+    }
+
+    // fp8 operand (32 bytes) of the 32 values vs+32h .. vs+32h+31 of a 64-value T1 strip for the
+    // 16x16x128 MFMA: byte p of the operand holds value vs + 32h + pi(p) with
+    //   pi(p) = 16*(p/16) + 4*(p%4) + (p/4)%4      (a 4x4 transpose inside each 16-value group),
+    // so that dword q is one shift-and-mask of a code word (digits q%4, q%4+4, q%4+8, q%4+12 of
+    // word 2h + q/4 as byte selectors) and one byte-select from `tbl` = [e(-s), e(0), e(+s), 0]
+    // (e = the fp8 encoding).  The activation operand must use the same order.
+    __host__ __device__ inline void frag8(int h, uint32_t tbl, uint32_t out[8]) const {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t sel = (code[2 * h + (q >> 2)] >> (2 * (q & 3))) & 0x03030303u;
+            out[q] = byte_select(tbl, sel);
         }
     }
 

@@ -458,6 +458,255 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup(GateUpArgs 
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// T1 gate/up on the fp8 MFMA (16x16x128).  T1 operands s*t (|s*t| <= 7) are exact in fp8
+// e4m3, and each is produced by one byte-select per four weights (Strip::frag8).  The bf16
+// activations become an exact pair hi + lo of fp8 values after a per-token power-of-two
+// scaling 2^sigma (max |x| * 2^sigma in [128, 256)): hi = fp8(v), lo = fp8(v - hi) keeps all 8
+// significant bits of v except for elements below ~2^-10 of the row's maximum.  Two fp8
+// MFMAs (hi, lo) take the same MFMA time as one bf16 MFMA over the same k, and the weights
+// need no 16-bit value table.
+
+// x [T][H] bf16 -> xq [T][2H] fp8 bytes, per token ordered [kb][h][g][hi 32 | lo 32] where
+// byte p of a 32-byte group holds k = 256*kb + 64*g + 32*h + pi(p) (pi as in Strip::frag8);
+// xinv[t] = 2^-sigma.
+__global__ __launch_bounds__(256) void k_xsplit(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
+                                                float* __restrict__ xinv, int H) {
+    __shared__ __attribute__((aligned(16))) uint8_t row[2 * 8192];
+    __shared__ float red[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* xr = x + (size_t)t * H;
+    float amax = 0.f;
+    for (int k = 8 * tid; k < H; k += 8 * 256) {
+        const u32x4 v = *(const u32x4*)(xr + k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 255u) - 127 : 7;  // floor(log2(amax))
+    int sigma = 7 - ex;
+    sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
+    const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
+    if (tid == 0) xinv[t] = __uint_as_float((uint32_t)(127 - sigma) << 23);
+    for (int k = 8 * tid; k < H; k += 8 * 256) {
+        const u32x4 v = *(const u32x4*)(xr + k);
+        const int kb = k >> 8, g = (k >> 6) & 3, h = (k >> 5) & 1, v0 = k & 31;
+        uint8_t* grp = row + kb * 512 + h * 256 + g * 64;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float xv = __uint_as_float(i & 1 ? (v[i >> 1] & 0xFFFF0000u) : (v[i >> 1] << 16)) * sc;
+            const uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv, 0.f, 0, false) & 255u;
+            const float hv = __builtin_amdgcn_cvt_f32_fp8((int)hb, 0);
+            const uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv - hv, 0.f, 0, false) & 255u;
+            const int vv = v0 + i, rem = vv & 15;
+            const int p = 16 * (vv >> 4) + 4 * (rem & 3) + (rem >> 2);
+            grp[p] = (uint8_t)hb;
+            grp[32 + p] = (uint8_t)lb;
+        }
+    }
+    __syncthreads();
+    uint8_t* dst = xq + (size_t)t * 2 * H;
+    for (int i = 16 * tid; i < 2 * H; i += 16 * 256) *(u32x4*)(dst + i) = *(const u32x4*)(row + i);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f32x4 c) {
+    i32x8 av, bv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        av[i] = (int)a[i];
+        bv[i] = (int)b[i];
+    }
+    // formats 0/0 = fp8 e4m3 for both operands; unit E8M0 scales (127)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+}
+
+struct GateUpF8Args {
+    const uint8_t* xq;   // [T][2H] split activations
+    const float* xinv;   // [T]
+    const uint8_t* arena;
+    const rl_expert_desc* desc;
+    const int32_t* offsets;
+    const int32_t* pair_src;
+    const int32_t* worklist;
+    const int32_t* wl_len;
+    int32_t* counters;
+    uint16_t* hbuf;
+    int H, I, k, ns;
+};
+
+// staged activation chunk = one MFMA step (kb, h): [64 rows][4 groups][hi 32 | lo 32] bytes
+constexpr int F8_ROW = 256;
+constexpr int F8_LDA = F8_ROW + 16;
+
+template <int NW, int NTI, int MT>
+__device__ __forceinline__ void gateup_f8_chunk(const GateUpF8Args& a, const uint32_t* tern, const uint32_t* tbl8,
+                                                uint8_t (*As)[64 * F8_LDA], const BufSrc& srcx, const BufSrc& srcg,
+                                                const BufSrc& srcu, const uint32_t* xoff, const uint32_t* roff,
+                                                int nkb, f32x4 (&acc)[4][2 * NTI], RunScale* rs) {
+    constexpr int NTHR = 64 * NW;
+    constexpr int NT = 2 * NTI;
+    constexpr int BB = Fmt<QT_T1>::BYTES;
+    constexpr int PIECES = 64 * F8_ROW / 16;
+    constexpr int XL = PIECES / NTHR;
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    StripRaw<QT_T1, 64> raw[NT];
+    Strip<QT_T1, 64> st[NT];
+    u32x4 xv[XL];
+    auto xload = [&](int c) {  // step c = 2*kb + h
+#pragma unroll
+        for (int i = 0; i < XL; ++i)
+            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(srcx.r, xoff[i] + (uint32_t)c * F8_ROW, 0, 0);
+    };
+    auto xstore = [&](uint8_t* buf) {
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int idx = tid + NTHR * i;
+            *(u32x4*)&buf[(idx >> 4) * F8_LDA + 16 * (idx & 15)] = xv[i];
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], 64 * g);
+    xload(0);
+    __syncthreads();  // the previous chunk's readers are done with As
+    xstore(As[0]);
+    xload(1);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            st[t].prepare(raw[t], tern);
+            const float r = rs[t].step(st[t].d);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kb + 1 < nkb) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t] + (uint32_t)(kb + 1) * BB, 64 * g);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint8_t* Ab = As[h];
+            uint32_t b[NT][8];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) st[t].frag8(h, tbl8[st[t].sb[h] >> 8], b[t]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t* ar = Ab + (mt * 16 + n) * F8_LDA + 64 * g;
+                uint32_t ahi[8], alo[8];
+                *(u32x4*)&ahi[0] = *(const u32x4*)(ar);
+                *(u32x4*)&ahi[4] = *(const u32x4*)(ar + 16);
+                *(u32x4*)&alo[0] = *(const u32x4*)(ar + 32);
+                *(u32x4*)&alo[4] = *(const u32x4*)(ar + 48);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
+                    acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one M tile's activation operands at a time
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int c = 2 * kb + h;
+            if (c + 1 < 2 * nkb) xstore(As[h ^ 1]);
+            if (c + 2 < 2 * nkb) xload(c + 2);
+            __syncthreads();
+        }
+    }
+}
+
+template <int NW, int NTI>
+__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup_f8(GateUpF8Args a) {
+    constexpr int NTHR = 64 * NW;
+    constexpr int NT = 2 * NTI;
+    constexpr int BB = Fmt<QT_T1>::BYTES;
+    constexpr int XL = 64 * F8_ROW / 16 / NTHR;
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][64 * F8_LDA];
+    __shared__ uint32_t tern[256];
+    __shared__ uint32_t tbl8[8];
+    __shared__ float rscale[64];
+    __shared__ int item_sh;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    for (int i = tid; i < 256; i += NTHR) tern[i] = tern_entry((uint32_t)i);
+    if (tid < 8) {  // [e(-s), e(0), e(+s), 0] with the hardware's fp8 encoding; s = 0 -> all zero
+        const float sv = (float)tid;
+        const uint32_t pos = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv, 0.f, 0, false) & 255u;
+        const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
+        tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
+    }
+    __syncthreads();
+    const int n_ranks = uni(*a.wl_len);
+    const int nkb = a.H >> 8;
+    const uint32_t row_bytes = (uint32_t)nkb * BB;
+    const uint32_t mat_bytes = (uint32_t)a.I * row_bytes;
+    const BufSrc srcx(a.xq, 0x7FFFFFF0u);
+    int rank, slice;
+    while (next_item(a.counters, a.ns, n_ranks, &item_sh, rank, slice)) {
+        const int e = uni(a.worklist[rank]);
+        const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
+        const BufSrc srcg(a.arena + uni64(a.desc[e].gate_off), mat_bytes);
+        const BufSrc srcu(a.arena + uni64(a.desc[e].up_off), mat_bytes);
+        const int colw = slice * (16 * NTI * NW) + wave * (16 * NTI);
+        uint32_t roff[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
+
+        for (int mc = 0; mc < ne; mc += 64) {
+            const int rows = min(64, ne - mc);
+            const int mtiles = (rows + 15) >> 4;
+            uint32_t xoff[XL];
+#pragma unroll
+            for (int i = 0; i < XL; ++i) {
+                const int idx = tid + NTHR * i;
+                const int row = idx >> 4;
+                const int tok = a.pair_src[p0 + mc + (row < rows ? row : 0)] / a.k;
+                xoff[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (idx & 15);
+            }
+            f32x4 acc[4][NT];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            RunScale rs[NT];
+            switch (mtiles) {
+                case 1: gateup_f8_chunk<NW, NTI, 1>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
+                case 2: gateup_f8_chunk<NW, NTI, 2>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
+                case 3: gateup_f8_chunk<NW, NTI, 3>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
+                default: gateup_f8_chunk<NW, NTI, 4>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
+            }
+            if (tid < 64) rscale[tid] = tid < rows ? a.xinv[a.pair_src[p0 + mc + tid] / a.k] : 0.f;
+            __syncthreads();
+            // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < mtiles) {
+#pragma unroll
+                    for (int ti = 0; ti < NTI; ++ti)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = mt * 16 + 4 * g + i;
+                            if (r < rows) {
+                                const float xs = rscale[r];
+                                const float gv = acc[mt][ti][i] * rs[ti].dprev * xs;
+                                const float uv = acc[mt][NTI + ti][i] * rs[NTI + ti].dprev * xs;
+                                a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] =
+                                    f32_to_f16_bits(silu_fast(gv) * uv);
+                            }
+                        }
+                }
+            }
+        }
+    }
+}
+
 struct DownArgs {
     const uint16_t* hbuf;  // [P][I] fp16, sorted-pair order
     const uint8_t* arena;

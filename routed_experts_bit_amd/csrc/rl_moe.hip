@@ -20,7 +20,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, tile_hist, hbuf, yslot, total;
+    size_t flags, offsets, pair_src, inv, worklist, tile_hist, xq, xinv, hbuf, yslot, total;
 };
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
@@ -51,6 +51,10 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + 2 * (size_t)E * sizeof(int32_t));
     L.tile_hist = off;
     off = align_up(off + (size_t)(group_tiles((int64_t)P) > 0 ? group_tiles((int64_t)P) : 1) * E * sizeof(int32_t));
+    L.xq = off;  // fp8 hi/lo activations of the T1 path
+    off = align_up(off + (size_t)T * 2 * H);
+    L.xinv = off;
+    off = align_up(off + (size_t)T * sizeof(float));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
     L.yslot = off;
@@ -143,6 +147,19 @@ void launch_gateup_t(const GateUpArgs& a, int n_experts, hipStream_t s) {
     }
 }
 
+void launch_gateup_f8(const GateUpF8Args& a, int n_experts, hipStream_t s) {
+    GateUpF8Args b = a;
+    if (a.I % 128 == 0) {
+        b.ns = a.I / 128;
+        const int grid = grid_cap(resident_grid(k_gateup_f8<8, 1>, 512), n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup_f8<8, 1>), dim3(grid), dim3(512), 0, s, b);
+    } else {
+        b.ns = a.I / 64;
+        const int grid = grid_cap(resident_grid(k_gateup_f8<4, 1>, 256), n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup_f8<4, 1>), dim3(grid), dim3(256), 0, s, b);
+    }
+}
+
 template <int QT>
 void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
     DownArgs b = a;
@@ -206,15 +223,32 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     a.I = ex->I;
     a.k = k;
     a.ns = 1;
-    for (int q = QT_Q2B; q <= QT_T1; ++q) {
-        if (!present[q]) continue;
-        a.worklist = worklist + (q - 1) * ex->E;
-        a.wl_len = flags + 8 + q;
-        a.counters = flags + counter_set(0, q);
-        if (q == QT_Q2B)
-            launch_gateup_t<QT_Q2B>(a, present[q], s);
-        else
-            launch_gateup_t<QT_T1>(a, present[q], s);
+    if (present[QT_Q2B]) {
+        a.worklist = worklist + (QT_Q2B - 1) * ex->E;
+        a.wl_len = flags + 8 + QT_Q2B;
+        a.counters = flags + counter_set(0, QT_Q2B);
+        launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
+    }
+    if (present[QT_T1]) {
+        uint8_t* xq = at<uint8_t>(ws, L.xq);
+        float* xinv = at<float>(ws, L.xinv);
+        hipLaunchKernelGGL(k_xsplit, dim3(T), dim3(256), 0, s, x, xq, xinv, ex->H);
+        GateUpF8Args b;
+        b.xq = xq;
+        b.xinv = xinv;
+        b.arena = a.arena;
+        b.desc = a.desc;
+        b.offsets = offsets;
+        b.pair_src = pair_src;
+        b.worklist = worklist + (QT_T1 - 1) * ex->E;
+        b.wl_len = flags + 8 + QT_T1;
+        b.counters = flags + counter_set(0, QT_T1);
+        b.hbuf = hdst;
+        b.H = ex->H;
+        b.I = ex->I;
+        b.k = k;
+        b.ns = 1;
+        launch_gateup_f8(b, present[QT_T1], s);
     }
 }
 

@@ -25,6 +25,8 @@ def harness(tmp_path_factory):
     L = C.CDLL(out)
     L.hd_decode.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int64, C.c_void_p]
     L.hd_decode.restype = C.c_int
+    L.hd_frag8_t1.argtypes = [C.c_void_p, C.c_int64, C.c_void_p]
+    L.hd_frag8_t1.restype = C.c_int
     return L
 
 
@@ -64,3 +66,14 @@ def test_strip_decoder_matches_oracle(orc, harness, qtype, f16, strip, mis):
     assert rc == 0
     ref = orc.dequant(qtype, blk, nb * 256)
     assert np.array_equal(out.astype(np.float64), ref), np.nonzero(out != ref)[0][:10]
+
+
+def test_t1_fp8_step_operands(orc, harness):
+    """The fp8 operands of the T1 path: digit placement (byte order pi) and sub-scale per step."""
+    blk, nb = _blocks(QTYPE_T1, 40, seed=77)
+    buf = np.zeros(blk.size + 32, np.uint8)
+    buf[: blk.size] = blk
+    out = np.full(nb * 256, np.nan, np.float32)
+    assert harness.hd_frag8_t1(buf.ctypes.data, nb, out.ctypes.data) == 0
+    ref = orc.dequant(QTYPE_T1, blk, nb * 256)
+    assert np.array_equal(out.astype(np.float64), ref)
