@@ -41,6 +41,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="distinct arena copies cycled through")
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--oracle-threads", type=int, default=0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size reference for HBM byte "
+                         "counters under a profiler)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -74,6 +77,14 @@ def main():
     flops = 6.0 * H * I * T * k
     flops_gateup = 4.0 * H * I * T * k
     flops_down = 2.0 * H * I * T * k
+
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # warm-up
     for i in range(args.warmup):

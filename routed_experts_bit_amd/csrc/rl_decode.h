@@ -50,6 +50,7 @@ struct Fmt<QT_T1> {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // ------------------------------------------------------------------ scalar helpers
 __host__ __device__ inline float half_bits_to_float(uint32_t h) {
@@ -78,6 +79,18 @@ __host__ __device__ inline uint32_t byte_select(uint32_t tbl, uint32_t sel) {
 #else
     uint32_t r = 0;
     for (int b = 0; b < 4; ++b) r |= ((tbl >> (8 * ((sel >> (8 * b)) & 3u))) & 255u) << (8 * b);
+    return r;
+#endif
+}
+
+// Bytes of the pair (hi:lo) picked by the four selector bytes of `sel` (0..3 from lo, 4..7 from hi).
+__host__ __device__ inline uint32_t perm2(uint32_t hi, uint32_t lo, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_perm(hi, lo, sel);
+#else
+    const uint64_t v = ((uint64_t)hi << 32) | lo;
+    uint32_t r = 0;
+    for (int b = 0; b < 4; ++b) r |= (uint32_t)((v >> (8 * ((sel >> (8 * b)) & 7u))) & 255u) << (8 * b);
     return r;
 #endif
 }
@@ -128,10 +141,18 @@ struct PtrSrc {
         o[0] = dw(off);
         o[1] = dw(off + 4);
     }
+    __host__ __device__ inline void dw3(uint32_t off, uint32_t o[3]) const {
+        for (int i = 0; i < 3; ++i) o[i] = dw(off + 4 * i);
+    }
+    // offset split into a per-lane part and a uniform part (same bytes as dw*(off + soff))
+    __host__ __device__ inline uint32_t dw(uint32_t off, uint32_t soff) const { return dw(off + soff); }
+    __host__ __device__ inline void dw2(uint32_t off, uint32_t soff, uint32_t o[2]) const { dw2(off + soff, o); }
+    __host__ __device__ inline void dw3(uint32_t off, uint32_t soff, uint32_t o[3]) const { dw3(off + soff, o); }
 };
 
 // Buffer resource over one matrix of the arena (offsets are bytes from the matrix start; the
-// base is 4-byte aligned and the range is rounded up to whole dwords).
+// base is 4-byte aligned and the range is rounded up to whole dwords).  Buffer loads at any byte
+// offset return the bytes at that offset (gfx950 runs in unaligned access mode).
 struct BufSrc {
     __amdgpu_buffer_rsrc_t r;
     __device__ inline BufSrc(const void* base, uint32_t bytes)
@@ -148,6 +169,22 @@ struct BufSrc {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
         o[0] = v[0];
         o[1] = v[1];
+    }
+    __device__ inline void dw3(uint32_t off, uint32_t o[3]) const { dw3(off, 0u, o); }
+    // per-lane offset `off` plus a wave-uniform offset `soff` (kept in a scalar register)
+    __device__ inline uint32_t dw(uint32_t off, uint32_t soff) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+    }
+    __device__ inline void dw2(uint32_t off, uint32_t soff, uint32_t o[2]) const {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+        o[0] = v[0];
+        o[1] = v[1];
+    }
+    __device__ inline void dw3(uint32_t off, uint32_t soff, uint32_t o[3]) const {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, soff, 0);
+        o[0] = v[0];
+        o[1] = v[1];
+        o[2] = v[2];
     }
 };
 
@@ -253,20 +290,6 @@ struct Strip {
         }
     }
 
-    // fp8 operand (32 bytes) of the 32 values vs+32h .. vs+32h+31 of a 64-value T1 strip for the
-    // 16x16x128 MFMA: byte p of the operand holds value vs + 32h + pi(p) with
-    //   pi(p) = 16*(p/16) + 4*(p%4) + (p/4)%4      (a 4x4 transpose inside each 16-value group),
-    // so that dword q is one shift-and-mask of a code word (digits q%4, q%4+4, q%4+8, q%4+12 of
-    // word 2h + q/4 as byte selectors) and one byte-select from `tbl` = [e(-s), e(0), e(+s), 0]
-    // (e = the fp8 encoding).  The activation operand must use the same order.
-    __host__ __device__ inline void frag8(int h, uint32_t tbl, uint32_t out[8]) const {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t sel = (code[2 * h + (q >> 2)] >> (2 * (q & 3))) & 0x03030303u;
-            out[q] = byte_select(tbl, sel);
-        }
-    }
-
     // operand of fragment f (values vs+8f..vs+8f+7); f must be a compile-time constant in
     // kernels so that the code words stay in registers
     __host__ __device__ inline u32x4 frag(int f, const uint64_t* val) const {
@@ -280,6 +303,150 @@ struct Strip {
         r[2] = (uint32_t)hi;
         r[3] = (uint32_t)(hi >> 32);
         return r;
+    }
+};
+
+// ------------------------------------------------------------------ T1 strips for the fp8 MFMA
+// The 16x16x128 fp8 MFMA contracts 128 k per step; lane group g (lanes 16g..16g+15) supplies
+// 32 bytes of k.  Any bijection between (lane group, operand byte) and k is allowed as long as
+// the activation operand uses the same one, so each lane group takes whole digit bytes of a
+// 256-value block: over the block's two steps, operand byte j (0..63) of lane group g holds
+//   value t1_kmap(g, j) = 60g + j          for j < 60   (digit bytes 12g .. 12g+11)
+//                         240 + 4g + j-60  for j >= 60  (four of the 16 values in bytes 48..51)
+// and step h takes operand bytes 32h .. 32h+31.
+__host__ __device__ constexpr int t1_kmap(int g, int j) { return j < 60 ? 60 * g + j : 240 + 4 * g + (j - 60); }
+
+// Selector table: entry (r, b) holds the five base-3 digits of byte b (least significant first,
+// each 0..2) as bytes r .. r+4 of a 64-bit word (r = 0..3).  Bytes above 242 are not produced by
+// the format; they decode as five 1-digits (weight 0).
+constexpr int TSEL_ENTRIES = 4 * 256;
+__host__ __device__ inline uint64_t tsel_entry(int idx) {
+    const int r = idx >> 8;
+    uint32_t b = (uint32_t)idx & 255u;
+    if (b > 242u) b = 121u;  // 11111 in base 3
+    uint64_t v = 0;
+    for (int i = 0; i < 5; ++i) {
+        v |= (uint64_t)(b % 3u) << (8 * (i + r));
+        b /= 3u;
+    }
+    return v;
+}
+
+// Raw bytes of one lane's share of a T1 block, loaded at their byte offsets (unaligned buffer
+// loads): bytes 0..7 (d, sub-scales), the 12 digit bytes 12g.. of the lane group, and the
+// block's last four bytes (digit bytes 48..51), so that no load reaches past the block.
+struct T1Raw8 {
+    uint32_t h[2], w[3], t;
+    // block at byte offset row_off + blk (blk uniform across the wave)
+    template <class Src>
+    __host__ __device__ inline void load(const Src& src, uint32_t row_off, uint32_t blk, int g) {
+        src.dw2(row_off, blk, h);
+        src.dw3(row_off + 5u + 12u * (uint32_t)g, blk, w);
+        t = src.dw(row_off + 53u, blk);
+    }
+};
+
+// Per-lane constants of lane group g.
+struct T1Lane8 {
+    uint32_t shA, shB, shC;      // bit position of the sub-scales used by the lane (3 per group)
+    uint32_t m1, m2, m8, m9, m10;  // +4 on the selectors of dwords that take the second table
+    uint32_t tbs;                // tail: first tail byte 48 + (4g)/5 as a bit shift of the last dword
+    uint32_t tsh;                // tail: digit offset inside its first byte, in bits
+    uint32_t trot, tmask;        // tail: rotation of the second byte's lookup, and its mask
+    __host__ __device__ inline void init(int g) {
+        // dword q (values 60g+4q .. +3) lies in sub-scale group (60g+4q)/32: groups
+        // A = max(2g-1, 0), B = 2g, C = 2g+1 cover every lane (for g = 0, A = B)
+        shA = 3u * (uint32_t)(g > 0 ? 2 * g - 1 : 0);
+        shB = 3u * (uint32_t)(2 * g);
+        shC = 3u * (uint32_t)(2 * g + 1);
+        const uint32_t M = 0x04040404u;
+        m1 = g == 1 ? M : 0u;
+        m2 = (g == 1 || g == 2) ? M : 0u;
+        m8 = g == 0 ? M : 0u;
+        m9 = g <= 1 ? M : 0u;
+        m10 = g <= 2 ? M : 0u;
+        const int r0 = (4 * g) % 5;
+        tbs = 8u * (uint32_t)((4 * g) / 5);
+        tsh = 8u * (uint32_t)r0;
+        trot = r0 == 0 ? 0u : (uint32_t)(5 - r0);
+        tmask = r0 == 0 ? 0u : 0xFFFFFFFFu;
+    }
+};
+
+// Decoder of one lane's share of a T1 block, in two parts so that a kernel holds the operands
+// of one MFMA step at a time: prep() takes the raw dwords (which can then be reused for the
+// next block's loads) and keeps the aligned digit bytes, the tail word and the four scale
+// tables; step(h, ...) returns the fp8 operand of step h (exact s*(digit-1)).
+// tbl8[s] = [e(-s), e(0), e(+s), 0] (e = the fp8 e4m3 encoding; all zero for s = 0).  A block
+// with d = 0 decodes to zero operands.
+struct T1Dec8 {
+    uint32_t a[3];              // digit bytes 12g .. 12g+11 of the lane group
+    uint32_t tw;                // tail bytes 48 + (4g)/5 and the next one (low 16 bits)
+    uint32_t TA, TB, TC, TD;    // scale tables of the lane's sub-scale groups (see T1Lane8), TD: group 7
+    float d;
+
+    __host__ __device__ inline void prep(const T1Raw8& raw, const T1Lane8& ln, const uint32_t* tbl8) {
+        d = half_bits_to_float(raw.h[0] & 0xFFFFu);
+        uint32_t sw = (raw.h[0] >> 16) | (raw.h[1] << 16);  // bits 3i..3i+2: sub-scale of values 32i..32i+31
+        if (d == 0.0f) sw = 0u;
+        TA = tbl8[(sw >> ln.shA) & 7u];
+        TB = tbl8[(sw >> ln.shB) & 7u];
+        TC = tbl8[(sw >> ln.shC) & 7u];
+        TD = tbl8[(sw >> 21) & 7u];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) a[i] = raw.w[i];
+        tw = raw.t >> ln.tbs;
+    }
+
+    // selector entry of digit byte j (0..11) with rotation j%4: covers stream dwords
+    // 5(j/4) + j%4 and the next one
+    __host__ __device__ inline uint64_t sel(int j, const uint64_t* tsel) const {
+        return tsel[(j & 3) * 256 + ((a[j >> 2] >> (8 * (j & 3))) & 255u)];
+    }
+
+    __host__ __device__ inline void step(int h, const T1Lane8& ln, const uint64_t* tsel, uint32_t b[8]) const {
+        // stream dwords of groups of four bytes: q[5m] = lo(4m), q[5m+1..3] = hi | lo, q[5m+4] = hi(4m+3)
+        if (h == 0) {  // stream dwords 0..7: bytes 0..6
+            uint32_t lo[7], hi[7];
+#pragma unroll
+            for (int j = 0; j < 7; ++j) {
+                const uint64_t e = sel(j, tsel);
+                lo[j] = (uint32_t)e;
+                hi[j] = (uint32_t)(e >> 32);
+            }
+            const uint32_t q0 = lo[0], q1 = hi[0] | lo[1] | ln.m1, q2 = hi[1] | lo[2] | ln.m2;
+            const uint32_t q3 = hi[2] | lo[3], q4 = hi[3], q5 = lo[4], q6 = hi[4] | lo[5], q7 = hi[5] | lo[6];
+            // selectors 0..3 pick from the first table, 4..7 from the second
+            b[0] = perm2(TA, TA, q0);
+            b[1] = perm2(TB, TA, q1);
+            b[2] = perm2(TB, TA, q2);
+            b[3] = perm2(TB, TB, q3);
+            b[4] = perm2(TB, TB, q4);
+            b[5] = perm2(TB, TB, q5);
+            b[6] = perm2(TB, TB, q6);
+            b[7] = perm2(TB, TB, q7);
+        } else {  // stream dwords 8..14: bytes 6..11, dword 15: tail
+            uint32_t lo[12], hi[12];
+#pragma unroll
+            for (int j = 6; j < 12; ++j) {
+                const uint64_t e = sel(j, tsel);
+                lo[j] = (uint32_t)e;
+                hi[j] = (uint32_t)(e >> 32);
+            }
+            const uint32_t q8 = hi[6] | lo[7] | ln.m8, q9 = hi[7] | ln.m9, q10 = lo[8] | ln.m10;
+            const uint32_t q11 = hi[8] | lo[9], q12 = hi[9] | lo[10], q13 = hi[10] | lo[11], q14 = hi[11];
+            const uint64_t x0 = tsel[tw & 255u];
+            const uint32_t x1 = (uint32_t)tsel[ln.trot * 256u + ((tw >> 8) & 255u)];
+            const uint32_t q15 = (uint32_t)(x0 >> ln.tsh) | (x1 & ln.tmask);
+            b[0] = perm2(TC, TB, q8);
+            b[1] = perm2(TC, TB, q9);
+            b[2] = perm2(TC, TB, q10);
+            b[3] = perm2(TC, TC, q11);
+            b[4] = perm2(TC, TC, q12);
+            b[5] = perm2(TC, TC, q13);
+            b[6] = perm2(TC, TC, q14);
+            b[7] = perm2(TD, TD, q15);
+        }
     }
 };
 

@@ -460,15 +460,15 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup(GateUpArgs 
 
 // ---------------------------------------------------------------------------------------
 // T1 gate/up on the fp8 MFMA (16x16x128).  T1 operands s*t (|s*t| <= 7) are exact in fp8
-// e4m3, and each is produced by one byte-select per four weights (Strip::frag8).  The bf16
-// activations become an exact pair hi + lo of fp8 values after a per-token power-of-two
-// scaling 2^sigma (max |x| * 2^sigma in [128, 256)): hi = fp8(v), lo = fp8(v - hi) keeps all 8
-// significant bits of v except for elements below ~2^-10 of the row's maximum.  Two fp8
-// MFMAs (hi, lo) take the same MFMA time as one bf16 MFMA over the same k, and the weights
-// need no 16-bit value table.
+// e4m3; the decoder (T1Frag8) produces them with one LDS lookup per digit byte and one
+// byte-select per four weights.  The bf16 activations become an exact pair hi + lo of fp8
+// values after a per-token power-of-two scaling 2^sigma (max |x| * 2^sigma in [128, 256)):
+// hi = fp8(v), lo = fp8(v - hi) keeps all 8 significant bits of v except for elements below
+// ~2^-10 of the row's maximum.  Two fp8 MFMAs (hi, lo) take the same MFMA time as one bf16
+// MFMA over the same k.
 
 // x [T][H] bf16 -> xq [T][2H] fp8 bytes, per token ordered [kb][h][g][hi 32 | lo 32] where
-// byte p of a 32-byte group holds k = 256*kb + 64*g + 32*h + pi(p) (pi as in Strip::frag8);
+// byte p of the 32-byte group (kb, h, g) holds k = 256*kb + t1_kmap(g, 32*h + p);
 // xinv[t] = 2^-sigma.
 __global__ __launch_bounds__(256) void k_xsplit(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
                                                 float* __restrict__ xinv, int H) {
@@ -497,18 +497,19 @@ __global__ __launch_bounds__(256) void k_xsplit(const uint16_t* __restrict__ x, 
     if (tid == 0) xinv[t] = __uint_as_float((uint32_t)(127 - sigma) << 23);
     for (int k = 8 * tid; k < H; k += 8 * 256) {
         const u32x4 v = *(const u32x4*)(xr + k);
-        const int kb = k >> 8, g = (k >> 6) & 3, h = (k >> 5) & 1, v0 = k & 31;
-        uint8_t* grp = row + kb * 512 + h * 256 + g * 64;
+        uint8_t* blk = row + (k >> 8) * 512;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float xv = __uint_as_float(i & 1 ? (v[i >> 1] & 0xFFFF0000u) : (v[i >> 1] << 16)) * sc;
             const uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv, 0.f, 0, false) & 255u;
             const float hv = __builtin_amdgcn_cvt_f32_fp8((int)hb, 0);
             const uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv - hv, 0.f, 0, false) & 255u;
-            const int vv = v0 + i, rem = vv & 15;
-            const int p = 16 * (vv >> 4) + 4 * (rem & 3) + (rem >> 2);
-            grp[p] = (uint8_t)hb;
-            grp[32 + p] = (uint8_t)lb;
+            const int vv = (k & 255) + i;  // position in the block -> (g, j) of t1_kmap
+            const int g = vv < 240 ? vv / 60 : (vv - 240) >> 2;
+            const int j = vv < 240 ? vv - 60 * g : 60 + ((vv - 240) & 3);
+            uint8_t* grp = blk + (j >> 5) * 256 + g * 64;
+            grp[j & 31] = (uint8_t)hb;
+            grp[32 + (j & 31)] = (uint8_t)lb;
         }
     }
     __syncthreads();
@@ -543,99 +544,194 @@ struct GateUpF8Args {
     int H, I, k, ns;
 };
 
-// staged activation chunk = one MFMA step (kb, h): [64 rows][4 groups][hi 32 | lo 32] bytes
-constexpr int F8_ROW = 256;
-constexpr int F8_LDA = F8_ROW + 16;
+// Work item of the T1 gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and
+// the same NTI tiles of up (NT = 2*NTI weight strips per lane); an item covers 16*NTI*GU_NW
+// columns of I for one 64-pair chunk at a time.  Activations reach LDS by direct buffer-to-LDS
+// loads (no registers) into a ring of 4 steps of 16 KB (four separate arrays, so that the
+// compiler can tell their loads apart), prefetched 3 steps ahead; the waits on them are
+// counted explicitly (vm_barrier), the weight loads run one block ahead in registers.  Per
+// wave and block, vector-memory instructions are issued in the fixed order
+//   raw(kb+1) [RAWL = 3*NT] | step 2kb: dma(2kb+3) [GU_DMA] | step 2kb+1: dma(2kb+4) [GU_DMA]
+// (prologue: dma(0), raw(0), dma(1), dma(2)), so when step c waits for dma(c) at most
+//   2*RAWL + 2*GU_DMA (c even) or RAWL + 2*GU_DMA (c odd)
+// later loads may still be in flight; the last two steps of a chunk wait for everything.
+constexpr int GU_STEP = 64 * 256;  // one staged step: 64 rows x [4 groups][hi 32 | lo 32] bytes
+constexpr int GU_NW = 4;
+constexpr int GU_DMA = GU_STEP / 1024 / GU_NW;  // 1 KB buffer-to-LDS loads per wave per step
 
-template <int NW, int NTI, int MT>
-__device__ __forceinline__ void gateup_f8_chunk(const GateUpF8Args& a, const uint32_t* tern, const uint32_t* tbl8,
-                                                uint8_t (*As)[64 * F8_LDA], const BufSrc& srcx, const BufSrc& srcg,
-                                                const BufSrc& srcu, const uint32_t* xoff, const uint32_t* roff,
-                                                int nkb, f32x4 (&acc)[4][2 * NTI], RunScale* rs) {
-    constexpr int NTHR = 64 * NW;
-    constexpr int NT = 2 * NTI;
-    constexpr int BB = Fmt<QT_T1>::BYTES;
-    constexpr int PIECES = 64 * F8_ROW / 16;
-    constexpr int XL = PIECES / NTHR;
-    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
-    StripRaw<QT_T1, 64> raw[NT];
-    Strip<QT_T1, 64> st[NT];
-    u32x4 xv[XL];
-    auto xload = [&](int c) {  // step c = 2*kb + h
-#pragma unroll
-        for (int i = 0; i < XL; ++i)
-            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(srcx.r, xoff[i] + (uint32_t)c * F8_ROW, 0, 0);
-    };
-    auto xstore = [&](uint8_t* buf) {
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int idx = tid + NTHR * i;
-            *(u32x4*)&buf[(idx >> 4) * F8_LDA + 16 * (idx & 15)] = xv[i];
-        }
-    };
-#pragma unroll
-    for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], 64 * g);
-    xload(0);
-    __syncthreads();  // the previous chunk's readers are done with As
-    xstore(As[0]);
-    xload(1);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            st[t].prepare(raw[t], tern);
-            const float r = rs[t].step(st[t].d);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kb + 1 < nkb) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t] + (uint32_t)(kb + 1) * BB, 64 * g);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint8_t* Ab = As[h];
-            uint32_t b[NT][8];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) st[t].frag8(h, tbl8[st[t].sb[h] >> 8], b[t]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* ar = Ab + (mt * 16 + n) * F8_LDA + 64 * g;
-                uint32_t ahi[8], alo[8];
-                *(u32x4*)&ahi[0] = *(const u32x4*)(ar);
-                *(u32x4*)&ahi[4] = *(const u32x4*)(ar + 16);
-                *(u32x4*)&alo[0] = *(const u32x4*)(ar + 32);
-                *(u32x4*)&alo[4] = *(const u32x4*)(ar + 48);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
-                    acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // one M tile's activation operands at a time
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const int c = 2 * kb + h;
-            if (c + 1 < 2 * nkb) xstore(As[h ^ 1]);
-            if (c + 2 < 2 * nkb) xload(c + 2);
-            __syncthreads();
-        }
-    }
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+
+// Wait until at most N vector-memory loads of this wave are outstanding and all its LDS reads
+// are done, then synchronise the work-group.  One asm statement, so nothing is moved between
+// the wait and the barrier, and no memory access moves across it.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int NW, int NTI>
-__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup_f8(GateUpF8Args a) {
-    constexpr int NTHR = 64 * NW;
+struct GuShared {
+    uint8_t* ring[4];
+    const uint64_t* tsel;
+    const uint32_t* tbl8;
+    float* rscale;
+};
+
+template <int NTI, int MT>
+struct GuChunk {
+    static constexpr int NT = 2 * NTI;
+    static constexpr int RAWL = 3 * NT;
+    static constexpr int BB = Fmt<QT_T1>::BYTES;
+
+    const GuShared& sh;
+    const BufSrc &srcx, &srcg, &srcu;
+    const uint32_t* xoff;
+    const uint32_t* roff;
+    const T1Lane8& ln;
+    int nkb, NS, wave, m, g;
+    T1Raw8 raw[NT];
+    T1Dec8 dec[NT];
+    RunScale rs[NT];
+    f32x4 acc[MT][NT];
+
+    __device__ __forceinline__ void dma(int c, int slot) {
+        if (c < NS) {
+            uint8_t* base = sh.ring[slot] + wave * (GU_DMA * 1024);
+#pragma unroll
+            for (int i = 0; i < GU_DMA; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(base + i * 1024), 16, xoff[i],
+                                                         (uint32_t)c * 256u, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void rawload(int kb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], (uint32_t)kb * BB, g);
+    }
+    // top of block kb: decoder state from the raw dwords, block scale into the accumulators,
+    // then the next block's loads
+    __device__ __forceinline__ void block_top(int kb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            dec[t].prep(raw[t], ln, sh.tbl8);
+            const float r = rs[t].step(dec[t].d);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
+        }
+        if (kb + 1 < nkb) rawload(kb + 1);
+    }
+    // step c = 2*kb + H staged in ring slot S = c % 4
+    template <int H, int S>
+    __device__ __forceinline__ void step(int c) {
+        if (c + 2 >= NS)
+            vm_barrier<0>();
+        else if (H == 0)
+            vm_barrier<2 * RAWL + 2 * GU_DMA>();
+        else
+            vm_barrier<RAWL + 2 * GU_DMA>();
+        dma(c + 3, (S + 3) & 3);
+        mem_fence_compiler();
+        uint32_t b[NT][8];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            dec[t].step(H, ln, sh.tsel, b[t]);
+            __builtin_amdgcn_sched_barrier(0);  // one strip's lookups in flight at a time
+        }
+        const uint8_t* ring = sh.ring[S];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint8_t* rp = ring + (mt * 16 + m) * 256;
+            uint32_t ahi[8], alo[8];
+            *(u32x4*)&ahi[0] = *(const u32x4*)(rp + (((4 * g + 0) ^ m) << 4));
+            *(u32x4*)&ahi[4] = *(const u32x4*)(rp + (((4 * g + 1) ^ m) << 4));
+            *(u32x4*)&alo[0] = *(const u32x4*)(rp + (((4 * g + 2) ^ m) << 4));
+            *(u32x4*)&alo[4] = *(const u32x4*)(rp + (((4 * g + 3) ^ m) << 4));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
+                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one M tile's activation operands at a time
+        }
+        // the step's MFMAs are issued before the next step's barrier (not sunk past it, which
+        // would keep two steps' operands live)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(acc[mt][t]));
+    }
+
+    __device__ __forceinline__ void run() {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // earlier stores and loads: out of the count
+        dma(0, 0);
+        mem_fence_compiler();
+        rawload(0);
+        mem_fence_compiler();
+        dma(1, 1);
+        dma(2, 2);
+        mem_fence_compiler();
+        for (int kb = 0; kb < nkb; kb += 2) {  // two blocks per pass: ring slots are constants
+            block_top(kb);
+            step<0, 0>(2 * kb);
+            step<1, 1>(2 * kb + 1);
+            if (kb + 1 < nkb) {
+                block_top(kb + 1);
+                step<0, 2>(2 * kb + 2);
+                step<1, 3>(2 * kb + 3);
+            }
+        }
+    }
+};
+
+template <int NTI, int MT>
+__device__ __forceinline__ void gu_t1_item(const GateUpF8Args& a, const GuShared& sh, const BufSrc& srcx,
+                                           const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
+                                           const uint32_t* roff, const T1Lane8& ln, int nkb, int p0, int mc,
+                                           int rows, int colw) {
+    const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
+    GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, ln, nkb, 2 * nkb, wave, n, g};
+    ch.run();
+    if (tid < 64) sh.rscale[tid] = tid < rows ? a.xinv[a.pair_src[p0 + mc + tid] / a.k] : 0.f;
+    __syncthreads();
+    // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ti = 0; ti < NTI; ++ti)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mt * 16 + 4 * g + i;
+                if (r < rows) {
+                    const float xs = sh.rscale[r];
+                    const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
+                    const float uv = ch.acc[mt][NTI + ti][i] * ch.rs[NTI + ti].dprev * xs;
+                    a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
+                }
+            }
+    __syncthreads();  // rscale is rewritten by the next chunk
+}
+
+template <int NTI>
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
+    constexpr int NTHR = 64 * GU_NW;
     constexpr int NT = 2 * NTI;
     constexpr int BB = Fmt<QT_T1>::BYTES;
-    constexpr int XL = 64 * F8_ROW / 16 / NTHR;
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][64 * F8_LDA];
-    __shared__ uint32_t tern[256];
+    // the selector table sits at the bottom of LDS (largest alignment first), so that its
+    // constant offsets fit the 16-bit offset of LDS instructions
+    __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
     __shared__ int item_sh;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-    for (int i = tid; i < 256; i += NTHR) tern[i] = tern_entry((uint32_t)i);
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[GU_STEP];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[GU_STEP];
+    const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
+    for (int i = tid; i < TSEL_ENTRIES; i += NTHR) tsel[i] = tsel_entry(i);
     if (tid < 8) {  // [e(-s), e(0), e(+s), 0] with the hardware's fp8 encoding; s = 0 -> all zero
         const float sv = (float)tid;
         const uint32_t pos = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv, 0.f, 0, false) & 255u;
@@ -643,6 +739,9 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup_f8(GateUpF8
         tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
     }
     __syncthreads();
+    const GuShared sh{{ring0, ring1, ring2, ring3}, tsel, tbl8, rscale};
+    T1Lane8 ln;
+    ln.init(g);
     const int n_ranks = uni(*a.wl_len);
     const int nkb = a.H >> 8;
     const uint32_t row_bytes = (uint32_t)nkb * BB;
@@ -654,54 +753,28 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup_f8(GateUpF8
         const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
         const BufSrc srcg(a.arena + uni64(a.desc[e].gate_off), mat_bytes);
         const BufSrc srcu(a.arena + uni64(a.desc[e].up_off), mat_bytes);
-        const int colw = slice * (16 * NTI * NW) + wave * (16 * NTI);
+        const int colw = slice * (16 * NTI * GU_NW) + wave * (16 * NTI);
         uint32_t roff[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
 
         for (int mc = 0; mc < ne; mc += 64) {
             const int rows = min(64, ne - mc);
-            const int mtiles = (rows + 15) >> 4;
-            uint32_t xoff[XL];
+            // buffer-to-LDS load i of this wave fills slots (wave*GU_DMA + i)*64 + lane of a step:
+            // row = slot / 16, piece = (slot % 16) ^ (row % 16) (XOR swizzle: conflict-free reads)
+            uint32_t xoff[GU_DMA];
 #pragma unroll
-            for (int i = 0; i < XL; ++i) {
-                const int idx = tid + NTHR * i;
-                const int row = idx >> 4;
+            for (int i = 0; i < GU_DMA; ++i) {
+                const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
+                const int piece = (lane & 15) ^ (row & 15);
                 const int tok = a.pair_src[p0 + mc + (row < rows ? row : 0)] / a.k;
-                xoff[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (idx & 15);
+                xoff[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (uint32_t)piece;
             }
-            f32x4 acc[4][NT];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            RunScale rs[NT];
-            switch (mtiles) {
-                case 1: gateup_f8_chunk<NW, NTI, 1>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
-                case 2: gateup_f8_chunk<NW, NTI, 2>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
-                case 3: gateup_f8_chunk<NW, NTI, 3>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
-                default: gateup_f8_chunk<NW, NTI, 4>(a, tern, tbl8, As, srcx, srcg, srcu, xoff, roff, nkb, acc, rs); break;
-            }
-            if (tid < 64) rscale[tid] = tid < rows ? a.xinv[a.pair_src[p0 + mc + tid] / a.k] : 0.f;
-            __syncthreads();
-            // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (mt < mtiles) {
-#pragma unroll
-                    for (int ti = 0; ti < NTI; ++ti)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = mt * 16 + 4 * g + i;
-                            if (r < rows) {
-                                const float xs = rscale[r];
-                                const float gv = acc[mt][ti][i] * rs[ti].dprev * xs;
-                                const float uv = acc[mt][NTI + ti][i] * rs[NTI + ti].dprev * xs;
-                                a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] =
-                                    f32_to_f16_bits(silu_fast(gv) * uv);
-                            }
-                        }
-                }
+            switch ((rows + 15) >> 4) {
+                case 1: gu_t1_item<NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
+                case 2: gu_t1_item<NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
+                case 3: gu_t1_item<NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
+                default: gu_t1_item<NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
             }
         }
     }

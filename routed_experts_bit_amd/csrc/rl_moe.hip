@@ -114,13 +114,13 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
 
 // Persistent grids: as many work-groups as fit on the device at once (occupancy query, cached
 // per kernel), a multiple of 8 so that every XCD gets the same number.
-template <typename K>
-int resident_grid(K kernel, int block) {
+template <auto K>
+int resident_grid(int block) {
     static int cached = 0;
     if (cached == 0) {
         int dev = 0, cus = 256, per_cu = 1;
         if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
         cached = ((cus * per_cu + 7) / 8) * 8;
     }
     return cached;
@@ -138,11 +138,11 @@ void launch_gateup_t(const GateUpArgs& a, int n_experts, hipStream_t s) {
     GateUpArgs b = a;
     if (a.I % 128 == 0) {
         b.ns = a.I / 128;
-        const int grid = grid_cap(resident_grid(k_gateup<QT, 8, 1>, 512), n_experts, b.ns);
+        const int grid = grid_cap(resident_grid<k_gateup<QT, 8, 1>>(512), n_experts, b.ns);
         hipLaunchKernelGGL((k_gateup<QT, 8, 1>), dim3(grid), dim3(512), 0, s, b);
     } else {
         b.ns = a.I / 64;
-        const int grid = grid_cap(resident_grid(k_gateup<QT, 4, 1>, 256), n_experts, b.ns);
+        const int grid = grid_cap(resident_grid<k_gateup<QT, 4, 1>>(256), n_experts, b.ns);
         hipLaunchKernelGGL((k_gateup<QT, 4, 1>), dim3(grid), dim3(256), 0, s, b);
     }
 }
@@ -151,12 +151,12 @@ void launch_gateup_f8(const GateUpF8Args& a, int n_experts, hipStream_t s) {
     GateUpF8Args b = a;
     if (a.I % 128 == 0) {
         b.ns = a.I / 128;
-        const int grid = grid_cap(resident_grid(k_gateup_f8<8, 1>, 512), n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup_f8<8, 1>), dim3(grid), dim3(512), 0, s, b);
+        const int grid = grid_cap(resident_grid<k_gateup_t1<2>>(64 * GU_NW), n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup_t1<2>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
     } else {
         b.ns = a.I / 64;
-        const int grid = grid_cap(resident_grid(k_gateup_f8<4, 1>, 256), n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup_f8<4, 1>), dim3(grid), dim3(256), 0, s, b);
+        const int grid = grid_cap(resident_grid<k_gateup_t1<1>>(64 * GU_NW), n_experts, b.ns);
+        hipLaunchKernelGGL((k_gateup_t1<1>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
     }
 }
 
@@ -165,13 +165,13 @@ void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
     DownArgs b = a;
     b.ns = a.H / 256;
     if (a.I % 256 == 0) {
-        const int grid = grid_cap(resident_grid(k_down<QT, 256, 8, 2>, 512), n_experts, b.ns);
+        const int grid = grid_cap(resident_grid<k_down<QT, 256, 8, 2>>(512), n_experts, b.ns);
         hipLaunchKernelGGL((k_down<QT, 256, 8, 2>), dim3(grid), dim3(512), 0, s, b);
     } else if (a.I == 128) {
-        const int grid = grid_cap(resident_grid(k_down<QT, 128, 8, 2>, 512), n_experts, b.ns);
+        const int grid = grid_cap(resident_grid<k_down<QT, 128, 8, 2>>(512), n_experts, b.ns);
         hipLaunchKernelGGL((k_down<QT, 128, 8, 2>), dim3(grid), dim3(512), 0, s, b);
     } else {
-        const int grid = grid_cap(resident_grid(k_down<QT, 64, 8, 2>, 512), n_experts, b.ns);
+        const int grid = grid_cap(resident_grid<k_down<QT, 64, 8, 2>>(512), n_experts, b.ns);
         hipLaunchKernelGGL((k_down<QT, 64, 8, 2>), dim3(grid), dim3(512), 0, s, b);
     }
 }

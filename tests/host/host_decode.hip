@@ -41,28 +41,42 @@ static void run(const uint8_t* blocks, int64_t nblocks, float* out) {
     }
 }
 
-// fp8 step operands of T1 strips with an identity byte table (bytes = digits), mapped back to
-// values through the documented byte order pi and the strip's sub-scales.
-extern "C" int hd_frag8_t1(const uint8_t* blocks, int64_t nblocks, float* out) {
-    uint32_t tern[256];
-    for (int i = 0; i < 256; ++i) tern[i] = tern_entry((uint32_t)i);
+// fp8 e4m3 (OCP, "fn") encoding of a small integer |v| <= 7, and its value.
+static uint32_t e4m3_of_int(int v) {
+    if (v == 0) return 0u;
+    const uint32_t sign = v < 0 ? 0x80u : 0u;
+    int a = v < 0 ? -v : v, e = 0;
+    while ((a >> (e + 1)) != 0) ++e;              // a = 2^e * (1 + m/8)
+    const uint32_t m = (uint32_t)(((a << 3) >> e) & 7);
+    return sign | ((uint32_t)(e + 7) << 3) | m;
+}
+static float e4m3_value(uint32_t b) {
+    const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+    const float mag = e == 0 ? (float)m / 8.0f / 64.0f : (1.0f + (float)m / 8.0f) * (float)(1 << e) / 128.0f;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// fp8 operands of the T1 byte strips of every lane group, mapped back to block positions
+// through t1_kmap and scaled by d.
+extern "C" int hd_t1f8(const uint8_t* blocks, int64_t nblocks, float* out) {
+    std::vector<uint64_t> tsel(TSEL_ENTRIES);
+    for (int i = 0; i < TSEL_ENTRIES; ++i) tsel[i] = tsel_entry(i);
+    uint32_t tbl8[8];
+    for (int s = 0; s < 8; ++s) tbl8[s] = s == 0 ? 0u : (e4m3_of_int(-s) | (e4m3_of_int(s) << 16));
     const PtrSrc src{blocks};
     for (int64_t b = 0; b < nblocks; ++b) {
         for (int g = 0; g < 4; ++g) {
-            StripRaw<QT_T1, 64> raw;
-            raw.load(src, (uint32_t)(b * Fmt<QT_T1>::BYTES), 64 * g);
-            Strip<QT_T1, 64> st;
-            st.prepare(raw, tern);
-            for (int h = 0; h < 2; ++h) {
-                uint32_t op[8];
-                st.frag8(h, 0x03020100u, op);
-                const int s = (int)(st.sb[h] >> 8);
-                for (int p = 0; p < 32; ++p) {
-                    const int digit = (int)((op[p >> 2] >> (8 * (p & 3))) & 255u);
-                    const int v = 16 * (p / 16) + 4 * (p % 4) + (p / 4) % 4;
-                    out[b * 256 + 64 * g + 32 * h + v] = st.d * (float)(s * (digit - 1));
-                }
-            }
+            T1Lane8 ln;
+            ln.init(g);
+            T1Raw8 raw;
+            raw.load(src, 0u, (uint32_t)(b * Fmt<QT_T1>::BYTES), g);
+            T1Dec8 dec;
+            dec.prep(raw, ln, tbl8);
+            uint32_t op[16];
+            dec.step(0, ln, tsel.data(), op);
+            dec.step(1, ln, tsel.data(), op + 8);
+            for (int j = 0; j < 64; ++j)
+                out[b * 256 + t1_kmap(g, j)] = dec.d * e4m3_value((op[j >> 2] >> (8 * (j & 3))) & 255u);
         }
     }
     return 0;

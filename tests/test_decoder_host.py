@@ -25,8 +25,8 @@ def harness(tmp_path_factory):
     L = C.CDLL(out)
     L.hd_decode.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int64, C.c_void_p]
     L.hd_decode.restype = C.c_int
-    L.hd_frag8_t1.argtypes = [C.c_void_p, C.c_int64, C.c_void_p]
-    L.hd_frag8_t1.restype = C.c_int
+    L.hd_t1f8.argtypes = [C.c_void_p, C.c_int64, C.c_void_p]
+    L.hd_t1f8.restype = C.c_int
     return L
 
 
@@ -68,12 +68,19 @@ def test_strip_decoder_matches_oracle(orc, harness, qtype, f16, strip, mis):
     assert np.array_equal(out.astype(np.float64), ref), np.nonzero(out != ref)[0][:10]
 
 
-def test_t1_fp8_step_operands(orc, harness):
-    """The fp8 operands of the T1 path: digit placement (byte order pi) and sub-scale per step."""
+@pytest.mark.parametrize("mis", [0, 1, 2, 3])
+def test_t1_fp8_byte_strips(orc, harness, mis):
+    """The fp8 operands of the T1 path: every block position is covered exactly once through
+    t1_kmap, with the right digit and sub-scale (per-dword table choice, tail bytes), at every
+    block misalignment; zero-scale blocks decode to zero."""
     blk, nb = _blocks(QTYPE_T1, 40, seed=77)
+    blk = blk.reshape(nb, BLOCK_BYTES[QTYPE_T1]).copy()
+    blk[5, 0:2] = 0  # d = 0 (fp16 +0) with non-zero digits and sub-scales
+    blk = blk.ravel()
     buf = np.zeros(blk.size + 32, np.uint8)
-    buf[: blk.size] = blk
+    buf[mis: mis + blk.size] = blk
     out = np.full(nb * 256, np.nan, np.float32)
-    assert harness.hd_frag8_t1(buf.ctypes.data, nb, out.ctypes.data) == 0
+    assert harness.hd_t1f8(buf.ctypes.data + mis, nb, out.ctypes.data) == 0
     ref = orc.dequant(QTYPE_T1, blk, nb * 256)
-    assert np.array_equal(out.astype(np.float64), ref)
+    assert not np.isnan(out).any()
+    assert np.array_equal(out.astype(np.float64), ref), np.nonzero(out != ref)[0][:10]
