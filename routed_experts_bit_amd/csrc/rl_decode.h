@@ -385,8 +385,10 @@ struct T1Dec8 {
     uint32_t TA, TB, TC, TD;    // scale tables of the lane's sub-scale groups (see T1Lane8), TD: group 7
     float d;
 
-    __host__ __device__ inline void prep(const T1Raw8& raw, const T1Lane8& ln, const uint32_t* tbl8) {
-        d = half_bits_to_float(raw.h[0] & 0xFFFFu);
+    // live = false: a padding block, decoded as zero (d = 0)
+    __host__ __device__ inline void prep(const T1Raw8& raw, const T1Lane8& ln, const uint32_t* tbl8,
+                                         bool live = true) {
+        d = live ? half_bits_to_float(raw.h[0] & 0xFFFFu) : 0.0f;
         uint32_t sw = (raw.h[0] >> 16) | (raw.h[1] << 16);  // bits 3i..3i+2: sub-scale of values 32i..32i+31
         if (d == 0.0f) sw = 0u;
         TA = tbl8[(sw >> ln.shA) & 7u];

@@ -56,6 +56,13 @@ constexpr int GT = 1024;           // pairs per tile
 constexpr int GROUP_NTHR = 256;    // threads per grouping work-group
 constexpr int NBIN = 256;
 
+// Work-list record of one expert: its pairs [p0, p0 + ne) in sorted order and the arena byte
+// offsets of its gate, up and down matrices (32 bytes: one scalar load).
+struct ItemRec {
+    int32_t p0, ne;
+    uint64_t off[3];
+};
+
 struct GroupArgs {
     const int32_t* ids;
     const rl_expert_desc* desc;  // may be NULL: no work lists
@@ -64,6 +71,7 @@ struct GroupArgs {
     int32_t* inv;
     int32_t* flags;
     int32_t* worklist;  // [2][E]
+    ItemRec* items;     // [2][E], same order as worklist
     int32_t* tile_hist; // [ntiles][E]
     int P, E, ntiles;
     int nflags;         // status words to clear
@@ -209,7 +217,15 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             const int key = before[e];
             if (key < 0) continue;
             const int q0 = key / NBIN, b = key % NBIN;
-            a.worklist[q0 * E + atomicAdd(&bins[q0][b], 1)] = e;
+            const int pos = q0 * E + atomicAdd(&bins[q0][b], 1);
+            a.worklist[pos] = e;
+            ItemRec r;
+            r.p0 = scan[e] - tot[e];
+            r.ne = tot[e];
+            r.off[0] = a.desc[e].gate_off;
+            r.off[1] = a.desc[e].up_off;
+            r.off[2] = a.desc[e].down_off;
+            a.items[pos] = r;
         }
         __syncthreads();
         if (tid == 0 && (bad_sh & 2)) atomicOr(&a.flags[0], FLAG_BAD_QTYPE);
@@ -468,10 +484,11 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup(GateUpArgs 
 // MFMA over the same k.
 
 // x [T][H] bf16 -> xq [T][2H] fp8 bytes, per token ordered [kb][h][g][hi 32 | lo 32] where
-// byte p of the 32-byte group (kb, h, g) holds k = 256*kb + t1_kmap(g, 32*h + p);
-// xinv[t] = 2^-sigma.
+// byte p of the 32-byte group (kb, h, g) holds k = 256*kb + t1_kmap(g, 32*h + p).  For each
+// pair (t, j) at sorted position p = inv[t*k + j]: ptok[p] = t, pscale[p] = 2^-sigma(t).
 __global__ __launch_bounds__(256) void k_xsplit(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
-                                                float* __restrict__ xinv, int H) {
+                                                const int32_t* __restrict__ inv, int32_t* __restrict__ ptok,
+                                                float* __restrict__ pscale, int k, int H) {
     __shared__ __attribute__((aligned(16))) uint8_t row[2 * 8192];
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
@@ -494,7 +511,13 @@ __global__ __launch_bounds__(256) void k_xsplit(const uint16_t* __restrict__ x, 
     int sigma = 7 - ex;
     sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
     const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
-    if (tid == 0) xinv[t] = __uint_as_float((uint32_t)(127 - sigma) << 23);
+    if (tid < k) {
+        const int p = inv[(size_t)t * k + tid];
+        if (p >= 0) {
+            ptok[p] = t;
+            pscale[p] = __uint_as_float((uint32_t)(127 - sigma) << 23);
+        }
+    }
     for (int k = 8 * tid; k < H; k += 8 * 256) {
         const u32x4 v = *(const u32x4*)(xr + k);
         uint8_t* blk = row + (k >> 8) * 512;
@@ -531,17 +554,14 @@ __device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f
 }
 
 struct GateUpF8Args {
-    const uint8_t* xq;   // [T][2H] split activations
-    const float* xinv;   // [T]
+    const uint8_t* xq;      // [T][2H] split activations
+    const int32_t* ptok;    // [P] token of each sorted pair
+    const float* pscale;    // [P] 2^-sigma of that token
     const uint8_t* arena;
-    const rl_expert_desc* desc;
-    const int32_t* offsets;
-    const int32_t* pair_src;
-    const int32_t* worklist;
-    const int32_t* wl_len;
-    int32_t* counters;
+    const ItemRec* items;   // this type's work list, longest first
+    const int32_t* wl_len;  // its length (device)
     uint16_t* hbuf;
-    int H, I, k, ns;
+    int H, I, ns;
 };
 
 // Work item of the T1 gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and
@@ -578,6 +598,40 @@ struct GuShared {
     float* rscale;
 };
 
+// Static schedule of one XCD's share of a type's work list: ranks r = xcd (mod 8), each cut
+// into ns column slices, item ix -> (rank 8*(ix / ns) + xcd, slice ix % ns).  The nw
+// work-groups of the XCD (blockIdx = 8*j + xcd: work-groups are dealt round-robin over the
+// XCDs) take the items in snake order, round q taking item q*nw + j (q even) or
+// q*nw + nw-1-j (q odd), which balances a longest-first list without atomics; every item of
+// an expert stays on one XCD (one L2 for its activation rows).
+struct StaticSched {
+    int xcd, j, nw, ns, nitems;
+    __device__ inline StaticSched(int n_ranks, int ns_) {
+        xcd = blockIdx.x & 7;
+        j = blockIdx.x >> 3;
+        nw = gridDim.x >> 3;
+        ns = ns_;
+        nitems = (n_ranks > xcd ? (n_ranks - xcd + 7) / 8 : 0) * ns;
+    }
+    __device__ inline int item(int q) const { return q * nw + ((q & 1) ? nw - 1 - j : j); }
+    __device__ inline int rank(int ix) const { return (ix / ns) * 8 + xcd; }
+    __device__ inline int slice(int ix) const { return ix % ns; }
+};
+
+// scalar (uniform) load of a work-list record
+__device__ __forceinline__ ItemRec load_item(const ItemRec* items, int rank) {
+    typedef const __attribute__((address_space(4))) uint64_t* cptr;
+    const cptr p = (cptr)(items + rank);
+    const uint64_t w0 = p[0];
+    ItemRec r;
+    r.p0 = (int32_t)(uint32_t)w0;
+    r.ne = (int32_t)(uint32_t)(w0 >> 32);
+    r.off[0] = p[1];
+    r.off[1] = p[2];
+    r.off[2] = p[3];
+    return r;
+}
+
 template <int NTI, int MT>
 struct GuChunk {
     static constexpr int NT = 2 * NTI;
@@ -609,20 +663,22 @@ struct GuChunk {
         for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], (uint32_t)kb * BB, g);
     }
     // top of block kb: decoder state from the raw dwords, block scale into the accumulators,
-    // then the next block's loads
+    // then the next block's loads (unconditional, so that no register copy of loads in flight
+    // forces a wait; past the last block they reload it).  kb == nkb is a padding block (odd
+    // nkb): zero operands.
     __device__ __forceinline__ void block_top(int kb) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            dec[t].prep(raw[t], ln, sh.tbl8);
+            dec[t].prep(raw[t], ln, sh.tbl8, kb < nkb);
             const float r = rs[t].step(dec[t].d);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
         }
-        if (kb + 1 < nkb) rawload(kb + 1);
+        rawload(min(kb + 1, nkb - 1));
     }
     // step c = 2*kb + H staged in ring slot S = c % 4
-    template <int H, int S>
-    __device__ __forceinline__ void step(int c) {
+    template <int H, int S, class Hook>
+    __device__ __forceinline__ void step(int c, Hook& hook) {
         if (c + 2 >= NS)
             vm_barrier<0>();
         else if (H == 0)
@@ -630,6 +686,8 @@ struct GuChunk {
         else
             vm_barrier<RAWL + 2 * GU_DMA>();
         dma(c + 3, (S + 3) & 3);
+        // loads issued here are waited for by the last step's full wait
+        if (c == NS - 2) hook();
         mem_fence_compiler();
         uint32_t b[NT][8];
 #pragma unroll
@@ -661,7 +719,8 @@ struct GuChunk {
             for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(acc[mt][t]));
     }
 
-    __device__ __forceinline__ void run() {
+    template <class Hook>
+    __device__ __forceinline__ void run(Hook& hook) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -676,26 +735,39 @@ struct GuChunk {
         mem_fence_compiler();
         for (int kb = 0; kb < nkb; kb += 2) {  // two blocks per pass: ring slots are constants
             block_top(kb);
-            step<0, 0>(2 * kb);
-            step<1, 1>(2 * kb + 1);
-            if (kb + 1 < nkb) {
-                block_top(kb + 1);
-                step<0, 2>(2 * kb + 2);
-                step<1, 3>(2 * kb + 3);
-            }
+            step<0, 0>(2 * kb, hook);
+            step<1, 1>(2 * kb + 1, hook);
+            block_top(kb + 1);
+            step<0, 2>(2 * kb + 2, hook);
+            step<1, 3>(2 * kb + 3, hook);
         }
     }
 };
 
+// One 64-pair chunk of a work item: K loop, then SwiGLU into h.  During the chunk's
+// next-to-last step the hook gathers the next chunk's activation row offsets (xon) and this
+// chunk's per-row activation scales (ps, one row per thread of the first wave).
 template <int NTI, int MT>
-__device__ __forceinline__ void gu_t1_item(const GateUpF8Args& a, const GuShared& sh, const BufSrc& srcx,
-                                           const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
-                                           const uint32_t* roff, const T1Lane8& ln, int nkb, int p0, int mc,
-                                           int rows, int colw) {
+__device__ __forceinline__ void gu_t1_chunk(const GateUpF8Args& a, const GuShared& sh, const BufSrc& srcx,
+                                            const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
+                                            const uint32_t* roff, const T1Lane8& ln, int nkb, int pc, int rows,
+                                            int colw, bool has_next, int pn, int rows_n, uint32_t* xon) {
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
+    float ps = 0.f;
+    auto hook = [&]() {
+        if (has_next) {
+#pragma unroll
+            for (int i = 0; i < GU_DMA; ++i) {
+                const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
+                const int tok = a.ptok[pn + (row < rows_n ? row : 0)];
+                xon[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+            }
+        }
+        if (tid < rows) ps = a.pscale[pc + tid];
+    };
     GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, ln, nkb, 2 * nkb, wave, n, g};
-    ch.run();
-    if (tid < 64) sh.rscale[tid] = tid < rows ? a.xinv[a.pair_src[p0 + mc + tid] / a.k] : 0.f;
+    ch.run(hook);
+    if (tid < 64) sh.rscale[tid] = ps;
     __syncthreads();
     // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
 #pragma unroll
@@ -709,7 +781,7 @@ __device__ __forceinline__ void gu_t1_item(const GateUpF8Args& a, const GuShared
                     const float xs = sh.rscale[r];
                     const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
                     const float uv = ch.acc[mt][NTI + ti][i] * ch.rs[NTI + ti].dprev * xs;
-                    a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
+                    a.hbuf[(size_t)(pc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
                 }
             }
     __syncthreads();  // rscale is rewritten by the next chunk
@@ -725,12 +797,13 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
     __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
-    __shared__ int item_sh;
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring2[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring3[GU_STEP];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const StaticSched sc(uni(*a.wl_len), a.ns);
+    if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
     for (int i = tid; i < TSEL_ENTRIES; i += NTHR) tsel[i] = tsel_entry(i);
     if (tid < 8) {  // [e(-s), e(0), e(+s), 0] with the hardware's fp8 encoding; s = 0 -> all zero
         const float sv = (float)tid;
@@ -738,45 +811,74 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
         const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
         tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
     }
-    __syncthreads();
+    // a padding step (odd number of blocks) reads a slot that no load of its chunk wrote: keep
+    // every slot finite
+    for (int i = tid; i < GU_STEP / 16; i += NTHR) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        ((u32x4*)ring0)[i] = z;
+        ((u32x4*)ring1)[i] = z;
+        ((u32x4*)ring2)[i] = z;
+        ((u32x4*)ring3)[i] = z;
+    }
     const GuShared sh{{ring0, ring1, ring2, ring3}, tsel, tbl8, rscale};
     T1Lane8 ln;
     ln.init(g);
-    const int n_ranks = uni(*a.wl_len);
     const int nkb = a.H >> 8;
     const uint32_t row_bytes = (uint32_t)nkb * BB;
     const uint32_t mat_bytes = (uint32_t)a.I * row_bytes;
     const BufSrc srcx(a.xq, 0x7FFFFFF0u);
-    int rank, slice;
-    while (next_item(a.counters, a.ns, n_ranks, &item_sh, rank, slice)) {
-        const int e = uni(a.worklist[rank]);
-        const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
-        const BufSrc srcg(a.arena + uni64(a.desc[e].gate_off), mat_bytes);
-        const BufSrc srcu(a.arena + uni64(a.desc[e].up_off), mat_bytes);
-        const int colw = slice * (16 * NTI * GU_NW) + wave * (16 * NTI);
+
+    // first chunk: record and activation rows; later chunks are prefetched by their predecessor
+    int q = 0, ix = sc.item(0), mc = 0;
+    ItemRec rec = load_item(a.items, sc.rank(ix));
+    uint32_t xoff[GU_DMA];
+    {
+        const int rows = min(64, rec.ne);
+#pragma unroll
+        for (int i = 0; i < GU_DMA; ++i) {
+            const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
+            const int tok = a.ptok[rec.p0 + (row < rows ? row : 0)];
+            xoff[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+        }
+    }
+    __syncthreads();  // tables
+    while (true) {
+        // the chunk after this one (uniform)
+        int qn = q, ixn = ix, mcn = mc + 64;
+        ItemRec recn = rec;
+        bool has_next = true;
+        if (mcn >= rec.ne) {
+            qn = q + 1;
+            ixn = sc.item(qn);
+            mcn = 0;
+            has_next = ixn < sc.nitems;
+            if (has_next) recn = load_item(a.items, sc.rank(ixn));
+        }
+        const int rows = min(64, rec.ne - mc);
+        const int rows_n = has_next ? min(64, recn.ne - mcn) : 1;
+        const BufSrc srcg(a.arena + rec.off[0], mat_bytes);
+        const BufSrc srcu(a.arena + rec.off[1], mat_bytes);
+        const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
         uint32_t roff[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
-
-        for (int mc = 0; mc < ne; mc += 64) {
-            const int rows = min(64, ne - mc);
-            // buffer-to-LDS load i of this wave fills slots (wave*GU_DMA + i)*64 + lane of a step:
-            // row = slot / 16, piece = (slot % 16) ^ (row % 16) (XOR swizzle: conflict-free reads)
-            uint32_t xoff[GU_DMA];
+        uint32_t xon[GU_DMA];
 #pragma unroll
-            for (int i = 0; i < GU_DMA; ++i) {
-                const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
-                const int piece = (lane & 15) ^ (row & 15);
-                const int tok = a.pair_src[p0 + mc + (row < rows ? row : 0)] / a.k;
-                xoff[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (uint32_t)piece;
-            }
-            switch ((rows + 15) >> 4) {
-                case 1: gu_t1_item<NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
-                case 2: gu_t1_item<NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
-                case 3: gu_t1_item<NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
-                default: gu_t1_item<NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, p0, mc, rows, colw); break;
-            }
+        for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
+        const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
+        switch ((rows + 15) >> 4) {
+            case 1: gu_t1_chunk<NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 2: gu_t1_chunk<NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 3: gu_t1_chunk<NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            default: gu_t1_chunk<NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
         }
+        if (!has_next) break;
+        q = qn;
+        ix = ixn;
+        mc = mcn;
+        rec = recn;
+#pragma unroll
+        for (int i = 0; i < GU_DMA; ++i) xoff[i] = xon[i];
     }
 }
 

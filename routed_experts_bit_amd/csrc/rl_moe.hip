@@ -20,7 +20,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, tile_hist, xq, xinv, hbuf, yslot, total;
+    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, ptok, pscale, hbuf, yslot, total;
 };
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
@@ -51,10 +51,14 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + 2 * (size_t)E * sizeof(int32_t));
     L.tile_hist = off;
     off = align_up(off + (size_t)(group_tiles((int64_t)P) > 0 ? group_tiles((int64_t)P) : 1) * E * sizeof(int32_t));
+    L.items = off;  // work-list records, [2][E]
+    off = align_up(off + 2 * (size_t)E * sizeof(ItemRec));
     L.xq = off;  // fp8 hi/lo activations of the T1 path
     off = align_up(off + (size_t)T * 2 * H);
-    L.xinv = off;
-    off = align_up(off + (size_t)T * sizeof(float));
+    L.ptok = off;  // token of each sorted pair (T1 path)
+    off = align_up(off + P * sizeof(int32_t));
+    L.pscale = off;  // activation scale of each sorted pair (T1 path)
+    off = align_up(off + P * sizeof(float));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
     L.yslot = off;
@@ -94,7 +98,7 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
 
 void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
                   int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, int32_t* tile_hist,
-                  hipStream_t s) {
+                  ItemRec* items, hipStream_t s) {
     GroupArgs g;
     g.ids = ids;
     g.desc = desc;
@@ -103,6 +107,7 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
     g.inv = inv;
     g.flags = flags;
     g.worklist = worklist;
+    g.items = items;
     g.tile_hist = tile_hist;
     g.P = T * k;
     g.E = E;
@@ -209,8 +214,9 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     int32_t* offsets = at<int32_t>(ws, L.offsets);
     int32_t* pair_src = at<int32_t>(ws, L.pair_src);
     int32_t* worklist = at<int32_t>(ws, L.worklist);
+    ItemRec* items = at<ItemRec>(ws, L.items);
     launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
-                 at<int32_t>(ws, L.tile_hist), s);
+                 at<int32_t>(ws, L.tile_hist), items, s);
     if (ev_after_group) (void)hipEventRecord(static_cast<hipEvent_t>(ev_after_group), s);
     GateUpArgs a;
     a.x = x;
@@ -231,22 +237,20 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     }
     if (present[QT_T1]) {
         uint8_t* xq = at<uint8_t>(ws, L.xq);
-        float* xinv = at<float>(ws, L.xinv);
-        hipLaunchKernelGGL(k_xsplit, dim3(T), dim3(256), 0, s, x, xq, xinv, ex->H);
+        int32_t* ptok = at<int32_t>(ws, L.ptok);
+        float* pscale = at<float>(ws, L.pscale);
+        hipLaunchKernelGGL(k_xsplit, dim3(T), dim3(256), 0, s, x, xq, at<int32_t>(ws, L.inv), ptok, pscale, k,
+                           ex->H);
         GateUpF8Args b;
         b.xq = xq;
-        b.xinv = xinv;
+        b.ptok = ptok;
+        b.pscale = pscale;
         b.arena = a.arena;
-        b.desc = a.desc;
-        b.offsets = offsets;
-        b.pair_src = pair_src;
-        b.worklist = worklist + (QT_T1 - 1) * ex->E;
+        b.items = items + (QT_T1 - 1) * ex->E;
         b.wl_len = flags + 8 + QT_T1;
-        b.counters = flags + counter_set(0, QT_T1);
         b.hbuf = hdst;
         b.H = ex->H;
         b.I = ex->I;
-        b.k = k;
         b.ns = 1;
         launch_gateup_f8(b, present[QT_T1], s);
     }
@@ -373,7 +377,7 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
     if (ws_bytes < L.tile_hist + (size_t)(group_tiles((int64_t)T * k) > 0 ? group_tiles((int64_t)T * k) : 1) * E * 4)
         return RL_EWORKSPACE;
     launch_group(topk_ids, T, k, E, nullptr, offsets, pair_src, inv, at<int32_t>(workspace, L.flags),
-                 at<int32_t>(workspace, L.worklist), at<int32_t>(workspace, L.tile_hist),
+                 at<int32_t>(workspace, L.worklist), at<int32_t>(workspace, L.tile_hist), nullptr,
                  static_cast<hipStream_t>(stream));
     return hip_status();
 }
