@@ -155,6 +155,7 @@ struct PtrSrc {
 // offset return the bytes at that offset (gfx950 runs in unaligned access mode).
 struct BufSrc {
     __amdgpu_buffer_rsrc_t r;
+    __device__ inline BufSrc() {}
     __device__ inline BufSrc(const void* base, uint32_t bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)((bytes + 3u) & ~3u), 0x00020000)) {}
     __device__ inline uint32_t dw(uint32_t off) const { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
@@ -332,17 +333,25 @@ __host__ __device__ inline uint64_t tsel_entry(int idx) {
     return v;
 }
 
-// Raw bytes of one lane's share of a T1 block, loaded at their byte offsets (unaligned buffer
-// loads): bytes 0..7 (d, sub-scales), the 12 digit bytes 12g.. of the lane group, and the
-// block's last four bytes (digit bytes 48..51), so that no load reaches past the block.
+// Raw bytes of one lane's share of a T1 block: bytes 0..7 (d, sub-scales; byte 4 in the low
+// byte of h[1]), the 12 digit bytes 12g.. of the lane group, and the block's last four bytes
+// (digit bytes 48..51).  They are cut out of a 64-byte window of dwords that starts at the
+// dword boundary at or below the block start (m = block start % 4), which holds the whole
+// 57-byte block; kernels fetch such windows with coalesced loads (four lanes per row).
 struct T1Raw8 {
     uint32_t h[2], w[3], t;
-    // block at byte offset row_off + blk (blk uniform across the wave)
-    template <class Src>
-    __host__ __device__ inline void load(const Src& src, uint32_t row_off, uint32_t blk, int g) {
-        src.dw2(row_off, blk, h);
-        src.dw3(row_off + 5u + 12u * (uint32_t)g, blk, w);
-        t = src.dw(row_off + 53u, blk);
+    template <class Win>
+    __host__ __device__ inline void load_window(const Win& win, uint32_t m, int g) {
+        const uint32_t h0 = win[0], h1 = win[1];
+        h[0] = funnel(h1, h0, m);
+        h[1] = h1 >> (8u * m);
+        const uint32_t o = m + 5u + 12u * (uint32_t)g, d = o >> 2, s = o & 3u;
+        const uint32_t w0 = win[d], w1 = win[d + 1], w2 = win[d + 2], w3 = win[d + 3];
+        w[0] = funnel(w1, w0, s);
+        w[1] = funnel(w2, w1, s);
+        w[2] = funnel(w3, w2, s);
+        const uint32_t o2 = m + 53u, d2 = o2 >> 2, s2 = o2 & 3u;
+        t = funnel(win[d2 + 1], win[d2], s2);
     }
 };
 
@@ -388,7 +397,7 @@ struct T1Dec8 {
     // live = false: a padding block, decoded as zero (d = 0)
     __host__ __device__ inline void prep(const T1Raw8& raw, const T1Lane8& ln, const uint32_t* tbl8,
                                          bool live = true) {
-        d = live ? half_bits_to_float(raw.h[0] & 0xFFFFu) : 0.0f;
+        d = live ? half_bits_to_float(raw.h[0] & 0xFFFFu) : 0.0f;  // (live = false: a block of zeros)
         uint32_t sw = (raw.h[0] >> 16) | (raw.h[1] << 16);  // bits 3i..3i+2: sub-scale of values 32i..32i+31
         if (d == 0.0f) sw = 0u;
         TA = tbl8[(sw >> ln.shA) & 7u];

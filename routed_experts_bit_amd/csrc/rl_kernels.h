@@ -566,15 +566,19 @@ struct GateUpF8Args {
 
 // Work item of the T1 gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and
 // the same NTI tiles of up (NT = 2*NTI weight strips per lane); an item covers 16*NTI*GU_NW
-// columns of I for one 64-pair chunk at a time.  Activations reach LDS by direct buffer-to-LDS
-// loads (no registers) into a ring of 4 steps of 16 KB (four separate arrays, so that the
-// compiler can tell their loads apart), prefetched 3 steps ahead; the waits on them are
-// counted explicitly (vm_barrier), the weight loads run one block ahead in registers.  Per
-// wave and block, vector-memory instructions are issued in the fixed order
-//   raw(kb+1) [RAWL = 3*NT] | step 2kb: dma(2kb+3) [GU_DMA] | step 2kb+1: dma(2kb+4) [GU_DMA]
-// (prologue: dma(0), raw(0), dma(1), dma(2)), so when step c waits for dma(c) at most
-//   2*RAWL + 2*GU_DMA (c even) or RAWL + 2*GU_DMA (c odd)
-// later loads may still be in flight; the last two steps of a chunk wait for everything.
+// columns of I for one 64-pair chunk at a time.  All operands reach LDS by direct buffer-to-LDS
+// loads (no registers in flight):
+//  - activations: a ring of 2 steps of 16 KB (two separate arrays, so that the compiler can
+//    tell their loads apart), each step loaded one step ahead and shared by the work-group;
+//  - weights: each wave loads the next block of its own rows into its own 1 KB-per-strip area
+//    (four consecutive lanes fetch one row's 64-byte window, a coalesced pattern; the lanes
+//    that decode a row are 16 apart, so loading into registers directly would not coalesce),
+//    right after it has read the current block out of that area.
+// The waits on the shared ring are counted explicitly (vm_barrier).  Per wave, vector-memory
+// instructions are issued in the fixed order
+//   block kb: wts(kb+1) [NT] | step 2kb: act(2kb+1) [GU_DMA] | step 2kb+1: act(2kb+2) [GU_DMA]
+// (prologue: act(0), wts(0)), so when step c waits for act(c) at most NT (c even) or 0 (c odd)
+// later loads may still be in flight.
 constexpr int GU_STEP = 64 * 256;  // one staged step: 64 rows x [4 groups][hi 32 | lo 32] bytes
 constexpr int GU_NW = 4;
 constexpr int GU_DMA = GU_STEP / 1024 / GU_NW;  // 1 KB buffer-to-LDS loads per wave per step
@@ -591,8 +595,12 @@ __device__ __forceinline__ void vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Work-group barrier for LDS data only (no wait on outstanding global stores or loads).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 struct GuShared {
-    uint8_t* ring[4];
+    uint8_t* ring[2];
+    uint8_t* wts;  // [GU_NW][NT][1024]: per wave and strip, 16 rows x 64-byte windows
     const uint64_t* tsel;
     const uint32_t* tbl8;
     float* rscale;
@@ -635,21 +643,22 @@ __device__ __forceinline__ ItemRec load_item(const ItemRec* items, int rank) {
 template <int NTI, int MT>
 struct GuChunk {
     static constexpr int NT = 2 * NTI;
-    static constexpr int RAWL = 3 * NT;
     static constexpr int BB = Fmt<QT_T1>::BYTES;
 
     const GuShared& sh;
     const BufSrc &srcx, &srcg, &srcu;
-    const uint32_t* xoff;
-    const uint32_t* roff;
+    const uint32_t* xoff;  // per lane: activation source offset of each of its GU_DMA loads
+    const uint32_t* roff;  // per lane: byte offset of the row it decodes, per strip
+    const uint32_t* woff;  // per lane: byte offset of its 16 bytes of a row window, per strip
     const T1Lane8& ln;
     int nkb, NS, wave, m, g;
-    T1Raw8 raw[NT];
     T1Dec8 dec[NT];
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    __device__ __forceinline__ void dma(int c, int slot) {
+    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * 1024; }
+
+    __device__ __forceinline__ void act(int c, int slot) {
         if (c < NS) {
             uint8_t* base = sh.ring[slot] + wave * (GU_DMA * 1024);
 #pragma unroll
@@ -658,35 +667,40 @@ struct GuChunk {
                                                          (uint32_t)c * 256u, 0, 0);
         }
     }
-    __device__ __forceinline__ void rawload(int kb) {
+    // the 64-byte windows of block kb (clamped to the last block, so that the number of loads
+    // is fixed) of this wave's rows: lane L fetches bytes 16*(L%4).. of the window of row L/4
+    __device__ __forceinline__ void wload(int kb) {
+        const uint32_t blk = (uint32_t)min(kb, nkb - 1) * BB;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], (uint32_t)kb * BB, g);
+        for (int t = 0; t < NT; ++t)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? srcg : srcu).r, (lds_void*)wts(t), 16,
+                                                     (woff[t] + blk) & ~3u, 0, 0, 0);
     }
-    // top of block kb: decoder state from the raw dwords, block scale into the accumulators,
-    // then the next block's loads (unconditional, so that no register copy of loads in flight
-    // forces a wait; past the last block they reload it).  kb == nkb is a padding block (odd
-    // nkb): zero operands.
+    // top of block kb: decoder state from this wave's windows, block scale into the
+    // accumulators; then (its windows read) the next block's windows
     __device__ __forceinline__ void block_top(int kb) {
+        const uint32_t blk = (uint32_t)kb * BB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            dec[t].prep(raw[t], ln, sh.tbl8, kb < nkb);
+            T1Raw8 raw;
+            raw.load_window((const uint32_t*)(wts(t) + 64 * m), (roff[t] + blk) & 3u, g);
+            dec[t].prep(raw, ln, sh.tbl8);
             const float r = rs[t].step(dec[t].d);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
         }
-        rawload(min(kb + 1, nkb - 1));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // windows read before they are replaced
+        wload(kb + 1);
     }
-    // step c = 2*kb + H staged in ring slot S = c % 4
-    template <int H, int S, class Hook>
+    // step c = 2*kb + H staged in ring slot H
+    template <int H, class Hook>
     __device__ __forceinline__ void step(int c, Hook& hook) {
-        if (c + 2 >= NS)
-            vm_barrier<0>();
-        else if (H == 0)
-            vm_barrier<2 * RAWL + 2 * GU_DMA>();
+        if (H == 0)
+            vm_barrier<NT>();
         else
-            vm_barrier<RAWL + 2 * GU_DMA>();
-        dma(c + 3, (S + 3) & 3);
-        // loads issued here are waited for by the last step's full wait
+            vm_barrier<0>();
+        act(c + 1, 1 - H);
+        // loads issued here are waited for by the next (odd) step's full wait
         if (c == NS - 2) hook();
         mem_fence_compiler();
         uint32_t b[NT][8];
@@ -695,7 +709,7 @@ struct GuChunk {
             dec[t].step(H, ln, sh.tsel, b[t]);
             __builtin_amdgcn_sched_barrier(0);  // one strip's lookups in flight at a time
         }
-        const uint8_t* ring = sh.ring[S];
+        const uint8_t* ring = sh.ring[H];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const uint8_t* rp = ring + (mt * 16 + m) * 256;
@@ -725,21 +739,16 @@ struct GuChunk {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // earlier stores and loads: out of the count
-        dma(0, 0);
+        // vector-memory operations complete in issue order, so the stores and loads before this
+        // chunk only make the counted waits below stricter
+        act(0, 0);
         mem_fence_compiler();
-        rawload(0);
+        wload(0);
         mem_fence_compiler();
-        dma(1, 1);
-        dma(2, 2);
-        mem_fence_compiler();
-        for (int kb = 0; kb < nkb; kb += 2) {  // two blocks per pass: ring slots are constants
+        for (int kb = 0; kb < nkb; ++kb) {
             block_top(kb);
-            step<0, 0>(2 * kb, hook);
-            step<1, 1>(2 * kb + 1, hook);
-            block_top(kb + 1);
-            step<0, 2>(2 * kb + 2, hook);
-            step<1, 3>(2 * kb + 3, hook);
+            step<0>(2 * kb, hook);
+            step<1>(2 * kb + 1, hook);
         }
     }
 };
@@ -750,8 +759,9 @@ struct GuChunk {
 template <int NTI, int MT>
 __device__ __forceinline__ void gu_t1_chunk(const GateUpF8Args& a, const GuShared& sh, const BufSrc& srcx,
                                             const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
-                                            const uint32_t* roff, const T1Lane8& ln, int nkb, int pc, int rows,
-                                            int colw, bool has_next, int pn, int rows_n, uint32_t* xon) {
+                                            const uint32_t* roff, const uint32_t* woff, const T1Lane8& ln,
+                                            int nkb, int pc, int rows, int colw, bool has_next, int pn,
+                                            int rows_n, uint32_t* xon) {
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     float ps = 0.f;
     auto hook = [&]() {
@@ -765,10 +775,10 @@ __device__ __forceinline__ void gu_t1_chunk(const GateUpF8Args& a, const GuShare
         }
         if (tid < rows) ps = a.pscale[pc + tid];
     };
-    GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, ln, nkb, 2 * nkb, wave, n, g};
+    GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g};
     ch.run(hook);
     if (tid < 64) sh.rscale[tid] = ps;
-    __syncthreads();
+    lds_barrier();
     // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -784,7 +794,7 @@ __device__ __forceinline__ void gu_t1_chunk(const GateUpF8Args& a, const GuShare
                     a.hbuf[(size_t)(pc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
                 }
             }
-    __syncthreads();  // rscale is rewritten by the next chunk
+    // rscale is rewritten only after the next chunk's step barriers
 }
 
 template <int NTI>
@@ -797,10 +807,9 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
     __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[GU_STEP];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[GU_STEP];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     const StaticSched sc(uni(*a.wl_len), a.ns);
     if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
@@ -811,16 +820,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
         const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
         tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
     }
-    // a padding step (odd number of blocks) reads a slot that no load of its chunk wrote: keep
-    // every slot finite
-    for (int i = tid; i < GU_STEP / 16; i += NTHR) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        ((u32x4*)ring0)[i] = z;
-        ((u32x4*)ring1)[i] = z;
-        ((u32x4*)ring2)[i] = z;
-        ((u32x4*)ring3)[i] = z;
-    }
-    const GuShared sh{{ring0, ring1, ring2, ring3}, tsel, tbl8, rscale};
+    const GuShared sh{{ring0, ring1}, wts, tsel, tbl8, rscale};
     T1Lane8 ln;
     ln.init(g);
     const int nkb = a.H >> 8;
@@ -859,18 +859,21 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
         const BufSrc srcg(a.arena + rec.off[0], mat_bytes);
         const BufSrc srcu(a.arena + rec.off[1], mat_bytes);
         const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
-        uint32_t roff[NT];
+        uint32_t roff[NT], woff[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
+        for (int t = 0; t < NT; ++t) {
+            roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
+            woff[t] = (uint32_t)(colw + 16 * (t % NTI) + (lane >> 2)) * row_bytes + 16u * (uint32_t)(lane & 3);
+        }
         uint32_t xon[GU_DMA];
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
         const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
         switch ((rows + 15) >> 4) {
-            case 1: gu_t1_chunk<NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            case 2: gu_t1_chunk<NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            case 3: gu_t1_chunk<NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            default: gu_t1_chunk<NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 1: gu_t1_chunk<NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 2: gu_t1_chunk<NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 3: gu_t1_chunk<NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            default: gu_t1_chunk<NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
         }
         if (!has_next) break;
         q = qn;

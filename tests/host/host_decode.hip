@@ -59,6 +59,10 @@ static float e4m3_value(uint32_t b) {
 // fp8 operands of the T1 byte strips of every lane group, mapped back to block positions
 // through t1_kmap and scaled by d.
 extern "C" int hd_t1f8(const uint8_t* blocks, int64_t nblocks, float* out) {
+    // dword reads relative to the dword boundary at or below the first block (the caller pads
+    // the buffer by at least 64 bytes)
+    const uint8_t* base4 = (const uint8_t*)((uintptr_t)blocks & ~(uintptr_t)3);
+    const PtrSrc src4{base4};
     std::vector<uint64_t> tsel(TSEL_ENTRIES);
     for (int i = 0; i < TSEL_ENTRIES; ++i) tsel[i] = tsel_entry(i);
     uint32_t tbl8[8];
@@ -68,8 +72,12 @@ extern "C" int hd_t1f8(const uint8_t* blocks, int64_t nblocks, float* out) {
         for (int g = 0; g < 4; ++g) {
             T1Lane8 ln;
             ln.init(g);
+            // 64-byte window of dwords from the dword boundary at or below the block start
+            const uint32_t blk = (uint32_t)(b * Fmt<QT_T1>::BYTES) + (uint32_t)(blocks - base4);
+            uint32_t win[16];
+            for (int i = 0; i < 16; ++i) win[i] = src4.dw((blk & ~3u) + 4u * (uint32_t)i);
             T1Raw8 raw;
-            raw.load(src, 0u, (uint32_t)(b * Fmt<QT_T1>::BYTES), g);
+            raw.load_window(win, blk & 3u, g);
             T1Dec8 dec;
             dec.prep(raw, ln, tbl8);
             uint32_t op[16];
