@@ -570,18 +570,25 @@ struct GateUpF8Args {
 // loads (no registers in flight):
 //  - activations: a ring of 2 steps of 16 KB (two separate arrays, so that the compiler can
 //    tell their loads apart), each step loaded one step ahead and shared by the work-group;
-//  - weights: each wave loads the next block of its own rows into its own 1 KB-per-strip area
-//    (four consecutive lanes fetch one row's 64-byte window, a coalesced pattern; the lanes
-//    that decode a row are 16 apart, so loading into registers directly would not coalesce),
-//    right after it has read the current block out of that area.
+//  - weights: each wave loads the next block of its own rows into its own area, right after it
+//    has read the current block out of it: four consecutive lanes fetch one row's 64-byte
+//    window (a coalesced pattern; the lanes that decode a row are 16 apart, so loading into
+//    registers directly would not coalesce).  A strip's 16 windows are written by four loads
+//    of 16 active lanes (4 rows each) at GU_WQ-byte spacing, which puts the rows that one LDS
+//    read serves in distinct banks (a 64-byte row spacing would put them in four).
 // The waits on the shared ring are counted explicitly (vm_barrier).  Per wave, vector-memory
 // instructions are issued in the fixed order
-//   block kb: wts(kb+1) [NT] | step 2kb: act(2kb+1) [GU_DMA] | step 2kb+1: act(2kb+2) [GU_DMA]
-// (prologue: act(0), wts(0)), so when step c waits for act(c) at most NT (c even) or 0 (c odd)
-// later loads may still be in flight.
+//   block kb: wts(kb+1) [4*NT] | step 2kb: act(2kb+1) [GU_DMA] | step 2kb+1: act(2kb+2) [GU_DMA]
+// (prologue: act(0), wts(0)), so when step c waits for act(c) at most 4*NT (c even) or 0 (c odd)
+// later loads may still be in flight.  A wave reads the windows of block kb at the top of the
+// block; those loads have completed by then (the odd step before waits for everything, and
+// the chunk prologue is followed by a full wait).  The compiler's own tracking of
+// buffer-to-LDS loads is not relied on: it can miss them.
 constexpr int GU_STEP = 64 * 256;  // one staged step: 64 rows x [4 groups][hi 32 | lo 32] bytes
 constexpr int GU_NW = 4;
 constexpr int GU_DMA = GU_STEP / 1024 / GU_NW;  // 1 KB buffer-to-LDS loads per wave per step
+constexpr int GU_WQ = 4 * 64 + 16;               // bytes per 4-row quarter of a strip's windows
+constexpr int GU_WS = 4 * GU_WQ;                 // bytes per strip
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -600,7 +607,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 struct GuShared {
     uint8_t* ring[2];
-    uint8_t* wts;  // [GU_NW][NT][1024]: per wave and strip, 16 rows x 64-byte windows
+    uint8_t* wts;  // [GU_NW][NT][GU_WS]: per wave and strip, 16 64-byte row windows
     const uint64_t* tsel;
     const uint32_t* tbl8;
     float* rscale;
@@ -652,11 +659,16 @@ struct GuChunk {
     const uint32_t* woff;  // per lane: byte offset of its 16 bytes of a row window, per strip
     const T1Lane8& ln;
     int nkb, NS, wave, m, g;
+    uint32_t rowb;         // bytes per weight row
     T1Dec8 dec[NT];
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * 1024; }
+    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * GU_WS; }
+    // window of row r (0..15) of strip t
+    __device__ __forceinline__ const uint32_t* win(int t, int r) const {
+        return (const uint32_t*)(wts(t) + GU_WQ * (r >> 2) + 64 * (r & 3));
+    }
 
     __device__ __forceinline__ void act(int c, int slot) {
         if (c < NS) {
@@ -668,13 +680,19 @@ struct GuChunk {
         }
     }
     // the 64-byte windows of block kb (clamped to the last block, so that the number of loads
-    // is fixed) of this wave's rows: lane L fetches bytes 16*(L%4).. of the window of row L/4
+    // is fixed) of this wave's rows: in quarter q, lane L < 16 fetches bytes 16*(L%4).. of the
+    // window of row 4q + L/4 (woff[t] holds lane L's offset for q = 0; rows are row_bytes apart)
     __device__ __forceinline__ void wload(int kb) {
         const uint32_t blk = (uint32_t)min(kb, nkb - 1) * BB;
+        if ((threadIdx.x & 63) < 16) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? srcg : srcu).r, (lds_void*)wts(t), 16,
-                                                     (woff[t] + blk) & ~3u, 0, 0, 0);
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? srcg : srcu).r,
+                                                             (lds_void*)(wts(t) + GU_WQ * q), 16,
+                                                             (woff[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
+        }
     }
     // top of block kb: decoder state from this wave's windows, block scale into the
     // accumulators; then (its windows read) the next block's windows
@@ -683,7 +701,7 @@ struct GuChunk {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             T1Raw8 raw;
-            raw.load_window((const uint32_t*)(wts(t) + 64 * m), (roff[t] + blk) & 3u, g);
+            raw.load_window(win(t, m), (roff[t] + blk) & 3u, g);
             dec[t].prep(raw, ln, sh.tbl8);
             const float r = rs[t].step(dec[t].d);
 #pragma unroll
@@ -696,7 +714,7 @@ struct GuChunk {
     template <int H, class Hook>
     __device__ __forceinline__ void step(int c, Hook& hook) {
         if (H == 0)
-            vm_barrier<NT>();
+            vm_barrier<4 * NT>();
         else
             vm_barrier<0>();
         act(c + 1, 1 - H);
@@ -744,7 +762,7 @@ struct GuChunk {
         act(0, 0);
         mem_fence_compiler();
         wload(0);
-        mem_fence_compiler();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block 0's windows before they are read
         for (int kb = 0; kb < nkb; ++kb) {
             block_top(kb);
             step<0>(2 * kb, hook);
@@ -775,7 +793,8 @@ __device__ __forceinline__ void gu_t1_chunk(const GateUpF8Args& a, const GuShare
         }
         if (tid < rows) ps = a.pscale[pc + tid];
     };
-    GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g};
+    GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g,
+                        (uint32_t)nkb * (uint32_t)Fmt<QT_T1>::BYTES};
     ch.run(hook);
     if (tid < 64) sh.rscale[tid] = ps;
     lds_barrier();
@@ -807,7 +826,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
     __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
-    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * GU_WS];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -863,7 +882,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
-            woff[t] = (uint32_t)(colw + 16 * (t % NTI) + (lane >> 2)) * row_bytes + 16u * (uint32_t)(lane & 3);
+            woff[t] = (uint32_t)(colw + 16 * (t % NTI) + ((lane >> 2) & 3)) * row_bytes + 16u * (uint32_t)(lane & 3);
         }
         uint32_t xon[GU_DMA];
 #pragma unroll

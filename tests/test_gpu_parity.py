@@ -206,6 +206,24 @@ def test_back_to_back_calls_no_sync(orc, rl, cases):
     assert torch.equal(o1, o3)
 
 
+@pytest.mark.parametrize("name", ["med_t1", "med_mixed"])
+def test_repeated_calls_identical(rl, cases, name):
+    """Ten calls in a row on one workspace (experts of more than 64 pairs, so work items span
+    several chunks): every output finite and bit-identical to the first.  Catches reads of
+    staged data before its loads complete, which show up as run-to-run differences."""
+    import torch
+
+    wl = _case(cases, name)
+    x, ids, w, ex = to_device(wl)
+    ws = rl.alloc_workspace(wl.T, wl.k, ex)
+    first = rl.prefill(x, ids, w, ex, ws=ws).clone()
+    h0 = rl.gate_up(x, ids, w, ex, ws=ws).clone()
+    assert torch.isfinite(first).all()
+    for _ in range(10):
+        assert torch.equal(rl.prefill(x, ids, w, ex, ws=ws), first)
+        assert torch.equal(rl.gate_up(x, ids, w, ex, ws=ws), h0)
+
+
 def test_empty_input(rl, cases):
     import torch
 
