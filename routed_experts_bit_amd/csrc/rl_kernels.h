@@ -553,16 +553,24 @@ __device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
 }
 
-struct GateUpF8Args {
-    const uint8_t* xq;      // [T][2H] split activations
-    const int32_t* ptok;    // [P] token of each sorted pair
-    const float* pscale;    // [P] 2^-sigma of that token
+// The two T1 expert GEMMs on the fp8 MFMA.  Gate/up: activations xq (split x, token rows,
+// gathered through ptok), weights gate and up [I][H], output h (fp16, SwiGLU, sorted-pair
+// rows).  Down: activations h8 (split h, sorted-pair rows), weights down [H][I], output y
+// (fp32, row = original pair index t*k + j).  K is the contracted length, N the output width.
+enum { T1_GATEUP = 0, T1_DOWN = 1 };
+struct T1F8Args {
+    const uint8_t* act;       // [rows][2K] split activations (hi/lo fp8, t1_kmap order)
+    const int32_t* ptok;      // gate/up: token (activation row) of each sorted pair
+    const float* pscale;      // [P] 2^-sigma of each sorted pair's activation row
+    const int32_t* pair_src;  // down: original pair index of each sorted pair
     const uint8_t* arena;
-    const ItemRec* items;   // this type's work list, longest first
-    const int32_t* wl_len;  // its length (device)
-    uint16_t* hbuf;
-    int H, I, ns;
+    const ItemRec* items;     // this type's work list, longest first
+    const int32_t* wl_len;    // its length (device)
+    uint16_t* hbuf;           // gate/up output [P][N] fp16
+    float* yslot;             // down output [P][N] fp32
+    int K, N, ns;
 };
+typedef T1F8Args GateUpF8Args;
 
 // Work item of the T1 gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and
 // the same NTI tiles of up (NT = 2*NTI weight strips per lane); an item covers 16*NTI*GU_NW
@@ -611,6 +619,7 @@ struct GuShared {
     const uint64_t* tsel;
     const uint32_t* tbl8;
     float* rscale;
+    int32_t* rdst;
 };
 
 // Static schedule of one XCD's share of a type's work list: ranks r = xcd (mod 8), each cut
@@ -647,9 +656,9 @@ __device__ __forceinline__ ItemRec load_item(const ItemRec* items, int rank) {
     return r;
 }
 
-template <int NTI, int MT>
+template <int NMAT, int NTI, int MT>
 struct GuChunk {
-    static constexpr int NT = 2 * NTI;
+    static constexpr int NT = NMAT * NTI;
     static constexpr int BB = Fmt<QT_T1>::BYTES;
 
     const GuShared& sh;
@@ -771,61 +780,79 @@ struct GuChunk {
     }
 };
 
-// One 64-pair chunk of a work item: K loop, then SwiGLU into h.  During the chunk's
-// next-to-last step the hook gathers the next chunk's activation row offsets (xon) and this
-// chunk's per-row activation scales (ps, one row per thread of the first wave).
-template <int NTI, int MT>
-__device__ __forceinline__ void gu_t1_chunk(const GateUpF8Args& a, const GuShared& sh, const BufSrc& srcx,
-                                            const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
-                                            const uint32_t* roff, const uint32_t* woff, const T1Lane8& ln,
-                                            int nkb, int pc, int rows, int colw, bool has_next, int pn,
-                                            int rows_n, uint32_t* xon) {
+// One 64-pair chunk of a work item: K loop, then the epilogue (gate/up: SwiGLU into h; down:
+// fp32 rows of y).  During the chunk's next-to-last step the hook gathers the next chunk's
+// activation row offsets (xon), this chunk's per-row activation scales (ps) and, for down, the
+// rows' original pair indices (one row per thread of the first wave).
+template <int MODE, int NTI, int MT>
+__device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, const BufSrc& srcx,
+                                         const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
+                                         const uint32_t* roff, const uint32_t* woff, const T1Lane8& ln, int nkb,
+                                         int pc, int rows, int colw, bool has_next, int pn, int rows_n,
+                                         uint32_t* xon) {
+    constexpr int NMAT = MODE == T1_GATEUP ? 2 : 1;
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     float ps = 0.f;
+    int pdst = 0;
     auto hook = [&]() {
         if (has_next) {
 #pragma unroll
             for (int i = 0; i < GU_DMA; ++i) {
                 const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
-                const int tok = a.ptok[pn + (row < rows_n ? row : 0)];
-                xon[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+                const int pr = pn + (row < rows_n ? row : 0);
+                const int arow = MODE == T1_GATEUP ? a.ptok[pr] : pr;
+                xon[i] = (uint32_t)arow * (uint32_t)(2 * a.K) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
             }
         }
-        if (tid < rows) ps = a.pscale[pc + tid];
+        if (tid < rows) {
+            ps = a.pscale[pc + tid];
+            if constexpr (MODE == T1_DOWN) pdst = a.pair_src[pc + tid];
+        }
     };
-    GuChunk<NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g,
-                        (uint32_t)nkb * (uint32_t)Fmt<QT_T1>::BYTES};
+    GuChunk<NMAT, NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g,
+                              (uint32_t)nkb * (uint32_t)Fmt<QT_T1>::BYTES};
     ch.run(hook);
-    if (tid < 64) sh.rscale[tid] = ps;
+    if (tid < 64) {
+        sh.rscale[tid] = ps;
+        if constexpr (MODE == T1_DOWN) sh.rdst[tid] = pdst;
+    }
     lds_barrier();
-    // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
+    // lane holds rows 4g..4g+3 of each 16-row tile, column n
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ti = 0; ti < NTI; ++ti)
+        for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            if (r < rows) {
+                const float xs = sh.rscale[r];
+                if constexpr (MODE == T1_GATEUP) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = mt * 16 + 4 * g + i;
-                if (r < rows) {
-                    const float xs = sh.rscale[r];
-                    const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
-                    const float uv = ch.acc[mt][NTI + ti][i] * ch.rs[NTI + ti].dprev * xs;
-                    a.hbuf[(size_t)(pc + r) * a.I + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
+                    for (int ti = 0; ti < NTI; ++ti) {
+                        const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
+                        const float uv = ch.acc[mt][NTI + ti][i] * ch.rs[NTI + ti].dprev * xs;
+                        a.hbuf[(size_t)(pc + r) * a.N + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
+                    }
+                } else {
+                    float* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + colw + n;
+#pragma unroll
+                    for (int t = 0; t < NTI; ++t) yrow[16 * t] = ch.acc[mt][t][i] * ch.rs[t].dprev * xs;
                 }
             }
-    // rscale is rewritten only after the next chunk's step barriers
+        }
+    // rscale and rdst are rewritten only after the next chunk's step barriers
 }
 
-template <int NTI>
-__global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
+template <int MODE, int NTI>
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
     constexpr int NTHR = 64 * GU_NW;
-    constexpr int NT = 2 * NTI;
+    constexpr int NT = (MODE == T1_GATEUP ? 2 : 1) * NTI;
     constexpr int BB = Fmt<QT_T1>::BYTES;
     // the selector table sits at the bottom of LDS (largest alignment first), so that its
     // constant offsets fit the 16-bit offset of LDS instructions
     __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
+    __shared__ int32_t rdst[64];
     __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * GU_WS];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
@@ -839,13 +866,14 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
         const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
         tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
     }
-    const GuShared sh{{ring0, ring1}, wts, tsel, tbl8, rscale};
+    const GuShared sh{{ring0, ring1}, wts, tsel, tbl8, rscale, rdst};
     T1Lane8 ln;
     ln.init(g);
-    const int nkb = a.H >> 8;
+    const int nkb = a.K >> 8;
     const uint32_t row_bytes = (uint32_t)nkb * BB;
-    const uint32_t mat_bytes = (uint32_t)a.I * row_bytes;
-    const BufSrc srcx(a.xq, 0x7FFFFFF0u);
+    const uint32_t mat_bytes = (uint32_t)a.N * row_bytes;
+    const BufSrc srcx(a.act, 0x7FFFFFF0u);
+    auto arow = [&](int p) { return MODE == T1_GATEUP ? a.ptok[p] : p; };
 
     // first chunk: record and activation rows; later chunks are prefetched by their predecessor
     int q = 0, ix = sc.item(0), mc = 0;
@@ -856,8 +884,8 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) {
             const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
-            const int tok = a.ptok[rec.p0 + (row < rows ? row : 0)];
-            xoff[i] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+            const int ar = arow(rec.p0 + (row < rows ? row : 0));
+            xoff[i] = (uint32_t)ar * (uint32_t)(2 * a.K) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
         }
     }
     __syncthreads();  // tables
@@ -875,7 +903,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
         }
         const int rows = min(64, rec.ne - mc);
         const int rows_n = has_next ? min(64, recn.ne - mcn) : 1;
-        const BufSrc srcg(a.arena + rec.off[0], mat_bytes);
+        const BufSrc srcg(a.arena + rec.off[MODE == T1_GATEUP ? 0 : 2], mat_bytes);
         const BufSrc srcu(a.arena + rec.off[1], mat_bytes);
         const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
         uint32_t roff[NT], woff[NT];
@@ -889,10 +917,10 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
         for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
         const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
         switch ((rows + 15) >> 4) {
-            case 1: gu_t1_chunk<NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            case 2: gu_t1_chunk<NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            case 3: gu_t1_chunk<NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            default: gu_t1_chunk<NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 1: t1_chunk<MODE, NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 2: t1_chunk<MODE, NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 3: t1_chunk<MODE, NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            default: t1_chunk<MODE, NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
         }
         if (!has_next) break;
         q = qn;
@@ -902,6 +930,56 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_gateup_t1(GateUpF8Args a) {
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xoff[i] = xon[i];
     }
+}
+
+// h [P][I] fp16 (sorted-pair rows) -> h8 [P][2I] split like xq (hi/lo fp8, t1_kmap order per
+// 256-value block), hscale[p] = 2^-sigma(p) with max |h[p]| * 2^sigma in [128, 256).  One wave
+// per row.
+__global__ __launch_bounds__(256) void k_hsplit(const uint16_t* __restrict__ h, uint8_t* __restrict__ h8,
+                                                float* __restrict__ hscale, int P, int I) {
+    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[4][2 * 4096];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int p = blockIdx.x * 4 + wave;
+    if (p >= P) return;  // only wave-level synchronisation below
+    const uint16_t* hr = h + (size_t)p * I;
+    float amax = 0.f;
+    for (int k = 8 * lane; k < I; k += 8 * 64) {
+        const u32x4 v = *(const u32x4*)(hr + k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(half_bits_to_float(v[i] & 0xFFFFu)));
+            amax = fmaxf(amax, fabsf(half_bits_to_float(v[i] >> 16)));
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 255u) - 127 : 7;  // floor(log2(amax))
+    int sigma = 7 - ex;
+    sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
+    const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
+    uint8_t* row = rowbuf[wave];
+    for (int k = 8 * lane; k < I; k += 8 * 64) {
+        const u32x4 v = *(const u32x4*)(hr + k);
+        uint8_t* blk = row + (k >> 8) * 512;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float xv = half_bits_to_float(i & 1 ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu)) * sc;
+            const uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv, 0.f, 0, false) & 255u;
+            const float hv = __builtin_amdgcn_cvt_f32_fp8((int)hb, 0);
+            const uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv - hv, 0.f, 0, false) & 255u;
+            const int vv = (k & 255) + i;  // position in the block -> (g, j) of t1_kmap
+            const int gg = vv < 240 ? vv / 60 : (vv - 240) >> 2;
+            const int j = vv < 240 ? vv - 60 * gg : 60 + ((vv - 240) & 3);
+            uint8_t* grp = blk + (j >> 5) * 256 + gg * 64;
+            grp[j & 31] = (uint8_t)hb;
+            grp[32 + (j & 31)] = (uint8_t)lb;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's row bytes, before other lanes read them
+    __builtin_amdgcn_wave_barrier();
+    uint8_t* dst = h8 + (size_t)p * 2 * I;
+    for (int i = 16 * lane; i < 2 * I; i += 16 * 64) *(u32x4*)(dst + i) = *(const u32x4*)(row + i);
+    if (lane == 0) hscale[p] = __uint_as_float((uint32_t)(127 - sigma) << 23);
 }
 
 struct DownArgs {

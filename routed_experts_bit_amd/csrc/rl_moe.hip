@@ -20,7 +20,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, ptok, pscale, hbuf, yslot, total;
+    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, ptok, pscale, h8, hscale, hbuf, yslot, total;
 };
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
@@ -58,6 +58,10 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     L.ptok = off;  // token of each sorted pair (T1 path)
     off = align_up(off + P * sizeof(int32_t));
     L.pscale = off;  // activation scale of each sorted pair (T1 path)
+    off = align_up(off + P * sizeof(float));
+    L.h8 = off;  // fp8 hi/lo h of the T1 down path
+    off = align_up(off + P * (size_t)2 * I);
+    L.hscale = off;  // scale of each row of h8
     off = align_up(off + P * sizeof(float));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
@@ -152,17 +156,28 @@ void launch_gateup_t(const GateUpArgs& a, int n_experts, hipStream_t s) {
     }
 }
 
-void launch_gateup_f8(const GateUpF8Args& a, int n_experts, hipStream_t s) {
-    GateUpF8Args b = a;
-    if (a.I % 128 == 0) {
-        b.ns = a.I / 128;
-        const int grid = grid_cap(resident_grid<k_gateup_t1<2>>(64 * GU_NW), n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup_t1<2>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
+void launch_gateup_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
+    T1F8Args b = a;
+    if (a.N % 128 == 0) {
+        b.ns = a.N / 128;
+        const int grid = grid_cap(resident_grid<k_t1_f8<T1_GATEUP, 2>>(64 * GU_NW), n_experts, b.ns);
+        hipLaunchKernelGGL((k_t1_f8<T1_GATEUP, 2>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
     } else {
-        b.ns = a.I / 64;
-        const int grid = grid_cap(resident_grid<k_gateup_t1<1>>(64 * GU_NW), n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup_t1<1>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
+        b.ns = a.N / 64;
+        const int grid = grid_cap(resident_grid<k_t1_f8<T1_GATEUP, 1>>(64 * GU_NW), n_experts, b.ns);
+        hipLaunchKernelGGL((k_t1_f8<T1_GATEUP, 1>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
     }
+}
+
+// T1 down on the fp8 MFMA (I a multiple of 256): split h, then 4 waves x 4 tiles = 256 output
+// columns per work item.
+void launch_down_f8(const T1F8Args& a, int n_experts, int P, hipStream_t s) {
+    hipLaunchKernelGGL(k_hsplit, dim3((P + 3) / 4), dim3(256), 0, s, a.hbuf, const_cast<uint8_t*>(a.act),
+                       const_cast<float*>(a.pscale), P, a.K);
+    T1F8Args b = a;
+    b.ns = a.N / 256;
+    const int grid = grid_cap(resident_grid<k_t1_f8<T1_DOWN, 4>>(64 * GU_NW), n_experts, b.ns);
+    hipLaunchKernelGGL((k_t1_f8<T1_DOWN, 4>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
 }
 
 template <int QT>
@@ -241,16 +256,16 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         float* pscale = at<float>(ws, L.pscale);
         hipLaunchKernelGGL(k_xsplit, dim3(T), dim3(256), 0, s, x, xq, at<int32_t>(ws, L.inv), ptok, pscale, k,
                            ex->H);
-        GateUpF8Args b;
-        b.xq = xq;
+        T1F8Args b = {};
+        b.act = xq;
         b.ptok = ptok;
         b.pscale = pscale;
         b.arena = a.arena;
         b.items = items + (QT_T1 - 1) * ex->E;
         b.wl_len = flags + 8 + QT_T1;
         b.hbuf = hdst;
-        b.H = ex->H;
-        b.I = ex->I;
+        b.K = ex->H;
+        b.N = ex->I;
         b.ns = 1;
         launch_gateup_f8(b, present[QT_T1], s);
     }
@@ -301,10 +316,24 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
         d.worklist = worklist + (q - 1) * experts->E;
         d.wl_len = flags + 8 + q;
         d.counters = flags + counter_set(1, q);
-        if (q == QT_Q2B)
+        if (q == QT_Q2B) {
             launch_down_t<QT_Q2B>(d, present[q], s);
-        else
+        } else if (experts->I % 256 == 0) {
+            T1F8Args b = {};
+            b.act = at<uint8_t>(workspace, L.h8);
+            b.pscale = at<float>(workspace, L.hscale);
+            b.pair_src = pair_src;
+            b.arena = d.arena;
+            b.items = at<ItemRec>(workspace, L.items) + (QT_T1 - 1) * experts->E;
+            b.wl_len = flags + 8 + QT_T1;
+            b.hbuf = hbuf;
+            b.yslot = yslot;
+            b.K = experts->I;
+            b.N = experts->H;
+            launch_down_f8(b, present[q], T * k, s);
+        } else {
             launch_down_t<QT_T1>(d, present[q], s);
+        }
     }
     mark(3);
     hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
