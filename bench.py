@@ -23,8 +23,39 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA (256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz)
+# Useful-FLOP ceiling of the gate/up kernel: it multiplies on the fp8 MFMA (5.03 PFLOP/s dense)
+# but every useful multiply-add takes two fp8 products (activation = hi + lo), so the ceiling is
+# half the fp8 peak, which equals the dense bf16/fp16 MFMA peak (256 CU x 4 SIMD x 1024 FLOP/clk
+# x 2.4 GHz).
+PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+STAGES = ("group", "xsplit", "gate_up", "hsplit", "down", "combine")
+KERNEL_SOURCES = ("routed_experts_bit_amd/csrc/rl_kernels.h", "routed_experts_bit_amd/csrc/rl_decode.h")
+
+
+def kernel_digest():
+    """sha256 over the kernel sources (a traffic measurement is valid only for these)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each calibrated against a device copy of known size), or None
+    when there is none for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("gate_up_bytes_per_launch")
 
 
 def log(msg):
@@ -104,8 +135,9 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # same number of steps with events between the stages (on the stream the kernels run on)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # same number of steps with events between the kernels (on the stream the kernels run on)
+    ne = rl.TIMED_EVENTS
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in range(args.steps)]
     for row in evs:  # torch creates the HIP event on its first record
         for e in row:
             e.record(stream)
@@ -113,8 +145,8 @@ def main():
     for i in range(args.steps):
         rl.prefill_timed(x, ids, w, sets[i % len(sets)], out, ws, evs[i])
     torch.cuda.synchronize()
-    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
-    st_ms = stage.mean(axis=0)
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(ne - 1)] for i in range(args.steps)])
+    st_ms = dict(zip(STAGES, stage.mean(axis=0)))
 
     # warm (same weights every step) for context
     torch.cuda.synchronize()
@@ -127,10 +159,10 @@ def main():
 
     gpu_out = out.cpu().numpy().astype(np.float64)
     tflops = flops / (ms_step * 1e-3) / 1e12
-    gu_tflops = flops_gateup / (st_ms[1] * 1e-3) / 1e12
+    gu_tflops = flops_gateup / (st_ms["gate_up"] * 1e-3) / 1e12
     log(f"[bench] {ms_step * 1e3:.1f} us/layer = {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 "
-        f"peak); stages us: group {st_ms[0] * 1e3:.1f} gate/up {st_ms[1] * 1e3:.1f} down {st_ms[2] * 1e3:.1f} "
-        f"combine {st_ms[3] * 1e3:.1f}; warm {ms_warm * 1e3:.1f} us")
+        f"peak); kernels us: " + " ".join(f"{k} {v * 1e3:.1f}" for k, v in st_ms.items()) +
+        f"; warm {ms_warm * 1e3:.1f} us")
 
     result = {
         "metric": "routed-expert layer ms & TFLOPS (% bf16 MFMA peak), 2048 tok, 512 exp, top-10",
@@ -153,16 +185,15 @@ def main():
         },
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 3),
         "ms_per_layer_warm": round(ms_warm, 5),
-        "stage_ms": {"group": round(st_ms[0], 5), "gate_up": round(st_ms[1], 5), "down": round(st_ms[2], 5),
-                     "combine": round(st_ms[3], 5)},
+        "stage_ms": {k: round(v, 5) for k, v in st_ms.items()},
         "roofline": {
-            "kernel": "k_gateup (fused T1 decode + gate/up grouped GEMM + SwiGLU)",
+            "kernel": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU)",
             "bound": "mfma",
             "achieved": round(gu_tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 5),
-            "traffic": None,
+            "traffic": measured_traffic(args.config),
         },
     }
 

@@ -90,11 +90,14 @@ int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk
                    const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                    void* workspace, size_t ws_bytes, void* stream);
 
-/* Measurement hook: rl_moe_prefill with five events (events [host] array of hipEvent_t,
- * created by the caller) recorded on `stream`: before the grouping kernel, after it, after the
- * gate/up kernel(s), after the down kernel(s) and after the combine, so that the caller can
- * time each stage on the stream the kernels run on.  Otherwise identical to rl_moe_prefill;
- * RL_EINVAL if an event is NULL. */
+/* Measurement hook: rl_moe_prefill with RL_TIMED_EVENTS events (events [host] array of
+ * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels,
+ * 1 after them, 2 after the activation split of the T1 path, 3 after the gate/up kernel(s),
+ * 4 after the split of h for the T1 down path, 5 after the down kernel(s), 6 after the combine
+ * (an event whose kernel a layer does not use is recorded at the same place as the one before
+ * it), so that the caller can time each kernel on the stream the kernels run on.  Otherwise
+ * identical to rl_moe_prefill; RL_EINVAL if an event is NULL. */
+#define RL_TIMED_EVENTS 7
 int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                          const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                          void* workspace, size_t ws_bytes, void* stream, void* const* events);

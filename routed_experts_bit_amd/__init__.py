@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     alloc_workspace,
     prefill,
     prefill_timed,
+    TIMED_EVENTS,
     decode,
     gate_up,
     group_pairs,

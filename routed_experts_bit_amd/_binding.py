@@ -175,10 +175,16 @@ def prefill(x, ids, w, ex: DeviceExperts, out=None, ws=None):
     return out
 
 
+TIMED_EVENTS = 7  # RL_TIMED_EVENTS
+
+
 def prefill_timed(x, ids, w, ex: DeviceExperts, out, ws, events):
-    """rl_moe_prefill with 5 torch.cuda.Event (enable_timing) recorded between its stages."""
+    """rl_moe_prefill with TIMED_EVENTS torch.cuda.Event (enable_timing) recorded between its
+    kernels: grouping | activation split | gate/up | h split | down | combine."""
     T, k = ids.shape
-    arr = (C.c_void_p * 5)(*[C.c_void_p(e.cuda_event) for e in events])
+    if len(events) != TIMED_EVENTS:
+        raise RlError(f"prefill_timed needs {TIMED_EVENTS} events")
+    arr = (C.c_void_p * TIMED_EVENTS)(*[C.c_void_p(e.cuda_event) for e in events])
     rc = lib().rl_moe_prefill_timed(_ptr(x), _ptr(ids), _ptr(w), ex.blobs, _ptr(out), T, k, _ptr(ws), ws.numel(),
                                     _stream(), arr)
     _check(rc, "rl_moe_prefill_timed")

@@ -171,9 +171,11 @@ void launch_gateup_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
 
 // T1 down on the fp8 MFMA (I a multiple of 256): split h, then 4 waves x 4 tiles = 256 output
 // columns per work item.
-void launch_down_f8(const T1F8Args& a, int n_experts, int P, hipStream_t s) {
+void launch_hsplit(const T1F8Args& a, int P, hipStream_t s) {
     hipLaunchKernelGGL(k_hsplit, dim3((P + 3) / 4), dim3(256), 0, s, a.hbuf, const_cast<uint8_t*>(a.act),
                        const_cast<float*>(a.pscale), P, a.K);
+}
+void launch_down_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
     T1F8Args b = a;
     b.ns = a.N / 256;
     const int grid = grid_cap(resident_grid<k_t1_f8<T1_DOWN, 4>>(64 * GU_NW), n_experts, b.ns);
@@ -223,7 +225,10 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
 // grouping + gate/up for every present type; returns the layout used
 void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blobs* ex, int32_t T, int32_t k,
                       void* ws, const int present[3], uint16_t* hdst, hipStream_t s, Layout& L,
-                      void* ev_after_group = nullptr) {
+                      void* const* events = nullptr) {
+    auto mark = [&](int i) {
+        if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    };
     L = layout(T, k, ex->E, ex->H, ex->I);
     int32_t* flags = at<int32_t>(ws, L.flags);
     int32_t* offsets = at<int32_t>(ws, L.offsets);
@@ -232,7 +237,7 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     ItemRec* items = at<ItemRec>(ws, L.items);
     launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
                  at<int32_t>(ws, L.tile_hist), items, s);
-    if (ev_after_group) (void)hipEventRecord(static_cast<hipEvent_t>(ev_after_group), s);
+    mark(1);
     GateUpArgs a;
     a.x = x;
     a.arena = static_cast<const uint8_t*>(ex->arena);
@@ -244,6 +249,7 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     a.I = ex->I;
     a.k = k;
     a.ns = 1;
+    if (!present[QT_T1]) mark(2);
     if (present[QT_Q2B]) {
         a.worklist = worklist + (QT_Q2B - 1) * ex->E;
         a.wl_len = flags + 8 + QT_Q2B;
@@ -256,6 +262,7 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         float* pscale = at<float>(ws, L.pscale);
         hipLaunchKernelGGL(k_xsplit, dim3(T), dim3(256), 0, s, x, xq, at<int32_t>(ws, L.inv), ptok, pscale, k,
                            ex->H);
+        mark(2);
         T1F8Args b = {};
         b.act = xq;
         b.ptok = ptok;
@@ -269,6 +276,7 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         b.ns = 1;
         launch_gateup_f8(b, present[QT_T1], s);
     }
+    mark(3);
 }
 
 }  // namespace
@@ -299,8 +307,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     float* yslot = at<float>(workspace, L.yslot);
     mark(0);
     Layout L2;  // same layout as L
-    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events ? events[1] : nullptr);
-    mark(2);
+    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events);
     DownArgs d;
     d.hbuf = hbuf;
     d.arena = static_cast<const uint8_t*>(experts->arena);
@@ -311,33 +318,37 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     d.H = experts->H;
     d.I = experts->I;
     d.ns = 1;
+    const bool t1_f8 = present[QT_T1] && experts->I % 256 == 0;
+    T1F8Args b = {};
+    if (t1_f8) {
+        b.act = at<uint8_t>(workspace, L.h8);
+        b.pscale = at<float>(workspace, L.hscale);
+        b.pair_src = pair_src;
+        b.arena = d.arena;
+        b.items = at<ItemRec>(workspace, L.items) + (QT_T1 - 1) * experts->E;
+        b.wl_len = flags + 8 + QT_T1;
+        b.hbuf = hbuf;
+        b.yslot = yslot;
+        b.K = experts->I;
+        b.N = experts->H;
+        launch_hsplit(b, T * k, s);
+    }
+    mark(4);
     for (int q = QT_Q2B; q <= QT_T1; ++q) {
         if (!present[q]) continue;
         d.worklist = worklist + (q - 1) * experts->E;
         d.wl_len = flags + 8 + q;
         d.counters = flags + counter_set(1, q);
-        if (q == QT_Q2B) {
+        if (q == QT_Q2B)
             launch_down_t<QT_Q2B>(d, present[q], s);
-        } else if (experts->I % 256 == 0) {
-            T1F8Args b = {};
-            b.act = at<uint8_t>(workspace, L.h8);
-            b.pscale = at<float>(workspace, L.hscale);
-            b.pair_src = pair_src;
-            b.arena = d.arena;
-            b.items = at<ItemRec>(workspace, L.items) + (QT_T1 - 1) * experts->E;
-            b.wl_len = flags + 8 + QT_T1;
-            b.hbuf = hbuf;
-            b.yslot = yslot;
-            b.K = experts->I;
-            b.N = experts->H;
-            launch_down_f8(b, present[q], T * k, s);
-        } else {
+        else if (t1_f8)
+            launch_down_f8(b, present[q], s);
+        else
             launch_down_t<QT_T1>(d, present[q], s);
-        }
     }
-    mark(3);
+    mark(5);
     hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
-    mark(4);
+    mark(6);
     return hip_status();
 }
 
@@ -350,7 +361,7 @@ int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float
                          const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* workspace,
                          size_t ws_bytes, void* stream, void* const* events) {
     if (!events) return RL_EINVAL;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < RL_TIMED_EVENTS; ++i)
         if (!events[i]) return RL_EINVAL;
     return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, stream, events);
 }
