@@ -91,8 +91,9 @@ int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk
                    void* workspace, size_t ws_bytes, void* stream);
 
 /* Measurement hook: rl_moe_prefill with RL_TIMED_EVENTS events (events [host] array of
- * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels,
- * 1 after them, 2 after the activation split of the T1 path, 3 after the gate/up kernel(s),
+ * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels
+ * (whose first launch also splits x for the T1 path), 1 after them, 2 at the same place (the
+ * x split no longer has a launch of its own), 3 after the gate/up kernel(s),
  * 4 after the split of h for the T1 down path, 5 after the down kernel(s), 6 after the combine
  * (an event whose kernel a layer does not use is recorded at the same place as the one before
  * it), so that the caller can time each kernel on the stream the kernels run on.  Otherwise

@@ -415,16 +415,32 @@ struct T1Dec8 {
         return tsel[(j & 3) * 256 + ((a[j >> 2] >> (8 * (j & 3))) & 255u)];
     }
 
-    __host__ __device__ inline void step(int h, const T1Lane8& ln, const uint64_t* tsel, uint32_t b[8]) const {
-        // stream dwords of groups of four bytes: q[5m] = lo(4m), q[5m+1..3] = hi | lo, q[5m+4] = hi(4m+3)
-        if (h == 0) {  // stream dwords 0..7: bytes 0..6
-            uint32_t lo[7], hi[7];
+    // the selector entries that step h needs (h = 0: bytes 0..6; h = 1: bytes 6..11 and the
+    // two tail entries), issued apart from their use so that a kernel can overlap the lookups
+    // with other work
+    __host__ __device__ inline void look(int h, const T1Lane8& ln, const uint64_t* tsel, uint64_t e[8]) const {
+        if (h == 0) {
 #pragma unroll
-            for (int j = 0; j < 7; ++j) {
-                const uint64_t e = sel(j, tsel);
-                lo[j] = (uint32_t)e;
-                hi[j] = (uint32_t)(e >> 32);
-            }
+            for (int j = 0; j < 7; ++j) e[j] = sel(j, tsel);
+            e[7] = 0;
+        } else {
+#pragma unroll
+            for (int j = 6; j < 12; ++j) e[j - 6] = sel(j, tsel);
+            e[6] = tsel[tw & 255u];
+            e[7] = tsel[ln.trot * 256u + ((tw >> 8) & 255u)];
+        }
+    }
+
+    // the fp8 operand of step h from its selector entries
+    __host__ __device__ inline void build(int h, const T1Lane8& ln, const uint64_t e[8], uint32_t b[8]) const {
+        // stream dwords of groups of four bytes: q[5m] = lo(4m), q[5m+1..3] = hi | lo, q[5m+4] = hi(4m+3)
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo[j] = (uint32_t)e[j];
+            hi[j] = (uint32_t)(e[j] >> 32);
+        }
+        if (h == 0) {  // stream dwords 0..7: bytes 0..6
             const uint32_t q0 = lo[0], q1 = hi[0] | lo[1] | ln.m1, q2 = hi[1] | lo[2] | ln.m2;
             const uint32_t q3 = hi[2] | lo[3], q4 = hi[3], q5 = lo[4], q6 = hi[4] | lo[5], q7 = hi[5] | lo[6];
             // selectors 0..3 pick from the first table, 4..7 from the second
@@ -436,19 +452,10 @@ struct T1Dec8 {
             b[5] = perm2(TB, TB, q5);
             b[6] = perm2(TB, TB, q6);
             b[7] = perm2(TB, TB, q7);
-        } else {  // stream dwords 8..14: bytes 6..11, dword 15: tail
-            uint32_t lo[12], hi[12];
-#pragma unroll
-            for (int j = 6; j < 12; ++j) {
-                const uint64_t e = sel(j, tsel);
-                lo[j] = (uint32_t)e;
-                hi[j] = (uint32_t)(e >> 32);
-            }
-            const uint32_t q8 = hi[6] | lo[7] | ln.m8, q9 = hi[7] | ln.m9, q10 = lo[8] | ln.m10;
-            const uint32_t q11 = hi[8] | lo[9], q12 = hi[9] | lo[10], q13 = hi[10] | lo[11], q14 = hi[11];
-            const uint64_t x0 = tsel[tw & 255u];
-            const uint32_t x1 = (uint32_t)tsel[ln.trot * 256u + ((tw >> 8) & 255u)];
-            const uint32_t q15 = (uint32_t)(x0 >> ln.tsh) | (x1 & ln.tmask);
+        } else {  // stream dwords 8..14: bytes 6..11 (entries 0..5), dword 15: tail (entries 6, 7)
+            const uint32_t q8 = hi[0] | lo[1] | ln.m8, q9 = hi[1] | ln.m9, q10 = lo[2] | ln.m10;
+            const uint32_t q11 = hi[2] | lo[3], q12 = hi[3] | lo[4], q13 = hi[4] | lo[5], q14 = hi[5];
+            const uint32_t q15 = (uint32_t)(e[6] >> ln.tsh) | (lo[7] & ln.tmask);
             b[0] = perm2(TC, TB, q8);
             b[1] = perm2(TC, TB, q9);
             b[2] = perm2(TC, TB, q10);
@@ -458,6 +465,12 @@ struct T1Dec8 {
             b[6] = perm2(TC, TC, q14);
             b[7] = perm2(TD, TD, q15);
         }
+    }
+
+    __host__ __device__ inline void step(int h, const T1Lane8& ln, const uint64_t* tsel, uint32_t b[8]) const {
+        uint64_t e[8];
+        look(h, ln, tsel, e);
+        build(h, ln, e, b);
     }
 };
 

@@ -77,9 +77,9 @@ struct GroupArgs {
     int nflags;         // status words to clear
 };
 
-__global__ __launch_bounds__(GROUP_NTHR) void k_group_count(GroupArgs a) {
+__device__ __forceinline__ void group_count_tile(const GroupArgs& a, int tile) {
     __shared__ int32_t h[MAX_E];
-    const int tid = threadIdx.x, tile = blockIdx.x;
+    const int tid = threadIdx.x;
     if (tile == 0 && tid < a.nflags) a.flags[tid] = 0;
     for (int e = tid; e < a.E; e += GROUP_NTHR) h[e] = 0;
     __syncthreads();
@@ -91,6 +91,8 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_count(GroupArgs a) {
     __syncthreads();
     for (int e = tid; e < a.E; e += GROUP_NTHR) a.tile_hist[(size_t)tile * a.E + e] = h[e];
 }
+
+__global__ __launch_bounds__(GROUP_NTHR) void k_group_count(GroupArgs a) { group_count_tile(a, blockIdx.x); }
 
 __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     constexpr int NW = GROUP_NTHR / 64;
@@ -107,18 +109,37 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     const int p0 = tile * GT, n = min(a.P - p0, GT);
     if (tid == 0) bad_sh = 0;
     for (int i = tid; i < GT; i += GROUP_NTHR) ids_sh[i] = i < n ? a.ids[p0 + i] : -1;
-    for (int e = tid; e < MAX_E; e += GROUP_NTHR) {
-        int b = 0, t = 0;
-        if (e < E) {
-            for (int tl = 0; tl < a.ntiles; ++tl) {
-                const int c = a.tile_hist[(size_t)tl * E + e];
-                b += tl < tile ? c : 0;
-                t += c;
+    {
+        // pairs of each expert in earlier tiles and in all tiles; the histogram loads are issued
+        // eight tiles at a time so that their latencies overlap
+        constexpr int EPT = MAX_E / GROUP_NTHR;
+        int b[EPT], t[EPT];
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) b[i] = t[i] = 0;
+        for (int tl0 = 0; tl0 < a.ntiles; tl0 += 8) {
+            int c[EPT][8];
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const int e = tid + GROUP_NTHR * i;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    c[i][u] = (e < E && tl0 + u < a.ntiles) ? a.tile_hist[(size_t)(tl0 + u) * E + e] : 0;
             }
+#pragma unroll
+            for (int i = 0; i < EPT; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    b[i] += tl0 + u < tile ? c[i][u] : 0;
+                    t[i] += c[i][u];
+                }
         }
-        before[e] = b;
-        tot[e] = t;
-        scan[e] = t;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tid + GROUP_NTHR * i;
+            before[e] = b[i];
+            tot[e] = t[i];
+            scan[e] = t[i];
+        }
     }
     for (int i = tid; i < NW * MAX_E; i += GROUP_NTHR) (&whist[0][0])[i] = 0;
     __syncthreads();
@@ -203,14 +224,28 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             atomicAdd(&bins[q - 1][b], 1);
         }
         __syncthreads();
-        if (tid < 2) {  // start of each bin in the type's list, high counts first
-            int run = 0;
-            for (int b = NBIN - 1; b >= 0; --b) {
-                const int c = bins[tid][b];
-                bins[tid][b] = run;
-                run += c;
+        if (tid < 128) {  // start of each bin in the type's list, high counts first: wave q scans type q
+            static_assert(NBIN == 4 * 64, "four bins per lane");
+            const int q = tid >> 6, l = tid & 63;
+            int c[4], run = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // lane l owns bins 255-4l .. 252-4l (descending)
+                c[j] = bins[q][NBIN - 1 - 4 * l - j];
+                run += c[j];
             }
-            a.flags[8 + QT_Q2B + tid] = run;
+            int incl = run;  // inclusive scan over the lanes
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(incl, d, 64);
+                if (l >= d) incl += v;
+            }
+            int pos = incl - run;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bins[q][NBIN - 1 - 4 * l - j] = pos;
+                pos += c[j];
+            }
+            if (l == 63) a.flags[8 + QT_Q2B + q] = incl;
         }
         __syncthreads();
         for (int e = tid; e < E; e += GROUP_NTHR) {
@@ -483,61 +518,122 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup(GateUpArgs 
 // ~2^-10 of the row's maximum.  Two fp8 MFMAs (hi, lo) take the same MFMA time as one bf16
 // MFMA over the same k.
 
-// x [T][H] bf16 -> xq [T][2H] fp8 bytes, per token ordered [kb][h][g][hi 32 | lo 32] where
-// byte p of the 32-byte group (kb, h, g) holds k = 256*kb + t1_kmap(g, 32*h + p).  For each
-// pair (t, j) at sorted position p = inv[t*k + j]: ptok[p] = t, pscale[p] = 2^-sigma(t).
-__global__ __launch_bounds__(256) void k_xsplit(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
-                                                const int32_t* __restrict__ inv, int32_t* __restrict__ ptok,
-                                                float* __restrict__ pscale, int k, int H) {
-    __shared__ __attribute__((aligned(16))) uint8_t row[2 * 8192];
-    __shared__ float red[4];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const uint16_t* xr = x + (size_t)t * H;
-    float amax = 0.f;
-    for (int k = 8 * tid; k < H; k += 8 * 256) {
-        const u32x4 v = *(const u32x4*)(xr + k);
+// Activation rows split into hi/lo fp8 in the decoder's k order: row r of K values (bf16 x or
+// fp16 h) -> 2K bytes ordered [kb][h][g][hi 32 | lo 32], where byte p of the 32-byte group
+// (kb, h, g) holds k = 256*kb + t1_kmap(g, 32*h + p).  Each row is scaled by 2^sigma (max |v| *
+// 2^sigma in [128, 256)); hi = fp8(v), lo = fp8(v - hi).  The 32 values of a group are two
+// contiguous runs of the row (60g + 32h .. and, for h = 1, the four tail values 240 + 4g ..), so
+// one lane converts a whole group and writes its 64 bytes.  LPR lanes per row, NG groups per lane.
+// scale[r] = 2^-sigma(r).  SPLIT_X: bf16 token rows (x); SPLIT_H: fp16 sorted-pair rows (h).
+enum { SPLIT_X = 0, SPLIT_H = 1 };
+struct SplitArgs {
+    const uint16_t* src;
+    uint8_t* dst;
+    float* scale;  // [rows]
+    int rows, K;
+};
+
+template <int MODE, int LPR, int NG>
+__device__ __forceinline__ void split_rows(const SplitArgs& a, int blk) {
+    constexpr int RPB = 256 / LPR;
+    // the block's rows pass through LDS: coalesced 16-byte global loads, then 8-byte reads of
+    // each group's two runs
+    __shared__ __attribute__((aligned(16))) uint8_t stage[256 * 64 * NG];
+    const int sub = threadIdx.x % LPR, rl = (int)threadIdx.x / LPR, r = blk * RPB + rl;
+    const bool live = r < a.rows;
+    const int G = a.K >> 5;
+    const uint8_t* row = (const uint8_t*)(a.src + (size_t)(live ? r : 0) * a.K);
+    uint8_t* srow = stage + rl * (64 * LPR * NG);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+    for (int n = 0; n < NG; ++n) {
+        const int gi = sub + LPR * n;
+        if (gi < G) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(u32x4*)(srow + 64 * gi + 16 * i) = *(const u32x4*)(row + 64 * gi + 16 * i);
+        }
+    }
+    __syncthreads();
+    const uint16_t* lrow = (const uint16_t*)srow;
+    uint2 raw[NG][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+        const int gi = sub + LPR * n;
+        const int gl = gi < G ? gi : 0;
+        const int kb = gl >> 3, hh = (gl >> 2) & 1, g = gl & 3;
+        const int base = 256 * kb + 60 * g + 32 * hh;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int off = (hh == 0 || i < 7) ? base + 4 * i : 256 * kb + 240 + 4 * g;
+            raw[n][i] = *(const uint2*)(lrow + off);
+        }
+        if (gi < G) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t w = q ? raw[n][i].y : raw[n][i].x;
+                    const float f0 = MODE == SPLIT_X ? __uint_as_float(w << 16) : half_bits_to_float(w & 0xFFFFu);
+                    const float f1 = MODE == SPLIT_X ? __uint_as_float(w & 0xFFFF0000u) : half_bits_to_float(w >> 16);
+                    amax = fmaxf(amax, fmaxf(fabsf(f0), fabsf(f1)));
+                }
+            }
         }
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 255u) - 127 : 7;  // floor(log2(amax))
+    for (int d = LPR / 2; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 255u) - 127 : 7;  // floor(log2(amax))
     int sigma = 7 - ex;
     sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
     const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
-    if (tid < k) {
-        const int p = inv[(size_t)t * k + tid];
-        if (p >= 0) {
-            ptok[p] = t;
-            pscale[p] = __uint_as_float((uint32_t)(127 - sigma) << 23);
-        }
-    }
-    for (int k = 8 * tid; k < H; k += 8 * 256) {
-        const u32x4 v = *(const u32x4*)(xr + k);
-        uint8_t* blk = row + (k >> 8) * 512;
+    const float inv_sc = __uint_as_float((uint32_t)(127 - sigma) << 23);
+    if (!live) return;
+    uint8_t* drow = a.dst + (size_t)r * 2 * a.K;
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+        const int gi = sub + LPR * n;
+        if (gi >= G) continue;
+        uint32_t hi[8], lo[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float xv = __uint_as_float(i & 1 ? (v[i >> 1] & 0xFFFF0000u) : (v[i >> 1] << 16)) * sc;
-            const uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv, 0.f, 0, false) & 255u;
-            const float hv = __builtin_amdgcn_cvt_f32_fp8((int)hb, 0);
-            const uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv - hv, 0.f, 0, false) & 255u;
-            const int vv = (k & 255) + i;  // position in the block -> (g, j) of t1_kmap
-            const int g = vv < 240 ? vv / 60 : (vv - 240) >> 2;
-            const int j = vv < 240 ? vv - 60 * g : 60 + ((vv - 240) & 3);
-            uint8_t* grp = blk + (j >> 5) * 256 + g * 64;
-            grp[j & 31] = (uint8_t)hb;
-            grp[32 + (j & 31)] = (uint8_t)lb;
+            float x[4];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t w = q ? raw[n][i].y : raw[n][i].x;
+                x[2 * q] = (MODE == SPLIT_X ? __uint_as_float(w << 16) : half_bits_to_float(w & 0xFFFFu)) * sc;
+                x[2 * q + 1] = (MODE == SPLIT_X ? __uint_as_float(w & 0xFFFF0000u) : half_bits_to_float(w >> 16)) * sc;
+            }
+            uint32_t h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+            h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], (int)h, true);
+            uint32_t l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0] - __builtin_amdgcn_cvt_f32_fp8((int)h, 0),
+                                                                   x[1] - __builtin_amdgcn_cvt_f32_fp8((int)h, 1), 0, false);
+            l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2] - __builtin_amdgcn_cvt_f32_fp8((int)h, 2),
+                                                          x[3] - __builtin_amdgcn_cvt_f32_fp8((int)h, 3), (int)l, true);
+            hi[i] = h;
+            lo[i] = l;
         }
+        u32x4* out = (u32x4*)(drow + 64 * gi);
+        out[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        out[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+        out[2] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        out[3] = u32x4{lo[4], lo[5], lo[6], lo[7]};
     }
-    __syncthreads();
-    uint8_t* dst = xq + (size_t)t * 2 * H;
-    for (int i = 16 * tid; i < 2 * H; i += 16 * 256) *(u32x4*)(dst + i) = *(const u32x4*)(row + i);
+    if (sub == 0) a.scale[r] = inv_sc;
+}
+
+template <int MODE, int LPR, int NG>
+__global__ __launch_bounds__(256) void k_split(SplitArgs a) {
+    split_rows<MODE, LPR, NG>(a, blockIdx.x);
+}
+
+// The pair histograms of the grouping and the split of x in one launch (they are independent):
+// work-groups [0, ntiles) count, the others split 256/LPR token rows each.
+template <int LPR, int NG>
+__global__ __launch_bounds__(256) void k_count_split(GroupArgs g, SplitArgs a) {
+    if ((int)blockIdx.x < g.ntiles)
+        group_count_tile(g, blockIdx.x);
+    else
+        split_rows<SPLIT_X, LPR, NG>(a, blockIdx.x - g.ntiles);
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -554,21 +650,21 @@ __device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f
 }
 
 // The two T1 expert GEMMs on the fp8 MFMA.  Gate/up: activations xq (split x, token rows,
-// gathered through ptok), weights gate and up [I][H], output h (fp16, SwiGLU, sorted-pair
+// gathered through the token pair_src[p] / k of each sorted pair p), weights gate and up [I][H], output h (fp16, SwiGLU, sorted-pair
 // rows).  Down: activations h8 (split h, sorted-pair rows), weights down [H][I], output y
 // (fp32, row = original pair index t*k + j).  K is the contracted length, N the output width.
 enum { T1_GATEUP = 0, T1_DOWN = 1 };
 struct T1F8Args {
     const uint8_t* act;       // [rows][2K] split activations (hi/lo fp8, t1_kmap order)
-    const int32_t* ptok;      // gate/up: token (activation row) of each sorted pair
-    const float* pscale;      // [P] 2^-sigma of each sorted pair's activation row
-    const int32_t* pair_src;  // down: original pair index of each sorted pair
+    const float* ascale;      // 2^-sigma of each activation row (gate/up: [T] per token; down: [P])
+    const int32_t* pair_src;  // original pair index t*k + j of each sorted pair
     const uint8_t* arena;
     const ItemRec* items;     // this type's work list, longest first
     const int32_t* wl_len;    // its length (device)
     uint16_t* hbuf;           // gate/up output [P][N] fp16
     float* yslot;             // down output [P][N] fp32
     int K, N, ns;
+    int k;                    // pairs per token (gate/up: token of pair index q is q / k)
 };
 typedef T1F8Args GateUpF8Args;
 
@@ -800,13 +896,17 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
             for (int i = 0; i < GU_DMA; ++i) {
                 const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
                 const int pr = pn + (row < rows_n ? row : 0);
-                const int arow = MODE == T1_GATEUP ? a.ptok[pr] : pr;
+                const int arow = MODE == T1_GATEUP ? a.pair_src[pr] / a.k : pr;
                 xon[i] = (uint32_t)arow * (uint32_t)(2 * a.K) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
             }
         }
         if (tid < rows) {
-            ps = a.pscale[pc + tid];
-            if constexpr (MODE == T1_DOWN) pdst = a.pair_src[pc + tid];
+            if constexpr (MODE == T1_GATEUP) {
+                ps = a.ascale[a.pair_src[pc + tid] / a.k];
+            } else {
+                ps = a.ascale[pc + tid];
+                pdst = a.pair_src[pc + tid];
+            }
         }
     };
     GuChunk<NMAT, NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g,
@@ -873,7 +973,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
     const uint32_t row_bytes = (uint32_t)nkb * BB;
     const uint32_t mat_bytes = (uint32_t)a.N * row_bytes;
     const BufSrc srcx(a.act, 0x7FFFFFF0u);
-    auto arow = [&](int p) { return MODE == T1_GATEUP ? a.ptok[p] : p; };
+    auto arow = [&](int p) { return MODE == T1_GATEUP ? a.pair_src[p] / a.k : p; };
 
     // first chunk: record and activation rows; later chunks are prefetched by their predecessor
     int q = 0, ix = sc.item(0), mc = 0;
@@ -930,56 +1030,6 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xoff[i] = xon[i];
     }
-}
-
-// h [P][I] fp16 (sorted-pair rows) -> h8 [P][2I] split like xq (hi/lo fp8, t1_kmap order per
-// 256-value block), hscale[p] = 2^-sigma(p) with max |h[p]| * 2^sigma in [128, 256).  One wave
-// per row.
-__global__ __launch_bounds__(256) void k_hsplit(const uint16_t* __restrict__ h, uint8_t* __restrict__ h8,
-                                                float* __restrict__ hscale, int P, int I) {
-    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[4][2 * 4096];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int p = blockIdx.x * 4 + wave;
-    if (p >= P) return;  // only wave-level synchronisation below
-    const uint16_t* hr = h + (size_t)p * I;
-    float amax = 0.f;
-    for (int k = 8 * lane; k < I; k += 8 * 64) {
-        const u32x4 v = *(const u32x4*)(hr + k);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(half_bits_to_float(v[i] & 0xFFFFu)));
-            amax = fmaxf(amax, fabsf(half_bits_to_float(v[i] >> 16)));
-        }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 255u) - 127 : 7;  // floor(log2(amax))
-    int sigma = 7 - ex;
-    sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
-    const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
-    uint8_t* row = rowbuf[wave];
-    for (int k = 8 * lane; k < I; k += 8 * 64) {
-        const u32x4 v = *(const u32x4*)(hr + k);
-        uint8_t* blk = row + (k >> 8) * 512;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float xv = half_bits_to_float(i & 1 ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu)) * sc;
-            const uint32_t hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv, 0.f, 0, false) & 255u;
-            const float hv = __builtin_amdgcn_cvt_f32_fp8((int)hb, 0);
-            const uint32_t lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xv - hv, 0.f, 0, false) & 255u;
-            const int vv = (k & 255) + i;  // position in the block -> (g, j) of t1_kmap
-            const int gg = vv < 240 ? vv / 60 : (vv - 240) >> 2;
-            const int j = vv < 240 ? vv - 60 * gg : 60 + ((vv - 240) & 3);
-            uint8_t* grp = blk + (j >> 5) * 256 + gg * 64;
-            grp[j & 31] = (uint8_t)hb;
-            grp[32 + (j & 31)] = (uint8_t)lb;
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's row bytes, before other lanes read them
-    __builtin_amdgcn_wave_barrier();
-    uint8_t* dst = h8 + (size_t)p * 2 * I;
-    for (int i = 16 * lane; i < 2 * I; i += 16 * 64) *(u32x4*)(dst + i) = *(const u32x4*)(row + i);
-    if (lane == 0) hscale[p] = __uint_as_float((uint32_t)(127 - sigma) << 23);
 }
 
 struct DownArgs {

@@ -20,7 +20,7 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, ptok, pscale, h8, hscale, hbuf, yslot, total;
+    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, total;
 };
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
@@ -55,10 +55,8 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + 2 * (size_t)E * sizeof(ItemRec));
     L.xq = off;  // fp8 hi/lo activations of the T1 path
     off = align_up(off + (size_t)T * 2 * H);
-    L.ptok = off;  // token of each sorted pair (T1 path)
-    off = align_up(off + P * sizeof(int32_t));
-    L.pscale = off;  // activation scale of each sorted pair (T1 path)
-    off = align_up(off + P * sizeof(float));
+    L.xscale = off;  // scale of each row of xq
+    off = align_up(off + (size_t)T * sizeof(float));
     L.h8 = off;  // fp8 hi/lo h of the T1 down path
     off = align_up(off + P * (size_t)2 * I);
     L.hscale = off;  // scale of each row of h8
@@ -100,9 +98,10 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
     return RL_OK;
 }
 
+// Pair grouping; with split != NULL the split of x runs in the histogram launch.
 void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
                   int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, int32_t* tile_hist,
-                  ItemRec* items, hipStream_t s) {
+                  ItemRec* items, hipStream_t s, const SplitArgs* split = nullptr) {
     GroupArgs g;
     g.ids = ids;
     g.desc = desc;
@@ -117,7 +116,30 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
     g.E = E;
     g.ntiles = group_tiles(g.P) > 0 ? group_tiles(g.P) : 1;
     g.nflags = FLAGS_WORDS;
-    hipLaunchKernelGGL(k_group_count, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
+    if (split != nullptr && split->rows > 0) {
+        const SplitArgs& a = *split;
+        const int G = a.K / 32;  // K <= 8192: G <= 256
+#define RL_CSPLIT(LPR, NG)                                                                                      \
+    hipLaunchKernelGGL((k_count_split<LPR, NG>), dim3(g.ntiles + (a.rows + 256 / LPR - 1) / (256 / LPR)), \
+                       dim3(256), 0, s, g, a)
+        if (G <= 8)
+            RL_CSPLIT(8, 1);
+        else if (G <= 16)
+            RL_CSPLIT(16, 1);
+        else if (G <= 32)
+            RL_CSPLIT(32, 1);
+        else if (G <= 64)
+            RL_CSPLIT(64, 1);
+        else if (G <= 128)
+            RL_CSPLIT(64, 2);
+        else if (G <= 192)
+            RL_CSPLIT(64, 3);
+        else
+            RL_CSPLIT(64, 4);
+#undef RL_CSPLIT
+    } else {
+        hipLaunchKernelGGL(k_group_count, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
+    }
     hipLaunchKernelGGL(k_group_scatter, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
 }
 
@@ -169,11 +191,41 @@ void launch_gateup_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
     }
 }
 
+// Split of activation rows into hi/lo fp8 (k_split): LPR lanes per row, NG groups of 32 values
+// per lane; K <= 8192.
+template <int MODE>
+void launch_split(const SplitArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return;
+    const int G = a.K / 32;
+#define RL_SPLIT(LPR, NG) \
+    hipLaunchKernelGGL((k_split<MODE, LPR, NG>), dim3((a.rows + 256 / LPR - 1) / (256 / LPR)), dim3(256), 0, s, a)
+    if (G <= 8)
+        RL_SPLIT(8, 1);
+    else if (G <= 16)
+        RL_SPLIT(16, 1);
+    else if (G <= 32)
+        RL_SPLIT(32, 1);
+    else if (G <= 64)
+        RL_SPLIT(64, 1);
+    else if (G <= 128)
+        RL_SPLIT(64, 2);
+    else if (G <= 192)
+        RL_SPLIT(64, 3);
+    else
+        RL_SPLIT(64, 4);
+#undef RL_SPLIT
+}
+
 // T1 down on the fp8 MFMA (I a multiple of 256): split h, then 4 waves x 4 tiles = 256 output
 // columns per work item.
 void launch_hsplit(const T1F8Args& a, int P, hipStream_t s) {
-    hipLaunchKernelGGL(k_hsplit, dim3((P + 3) / 4), dim3(256), 0, s, a.hbuf, const_cast<uint8_t*>(a.act),
-                       const_cast<float*>(a.pscale), P, a.K);
+    SplitArgs sa = {};
+    sa.src = a.hbuf;
+    sa.dst = const_cast<uint8_t*>(a.act);
+    sa.rows = P;
+    sa.K = a.K;
+    sa.scale = const_cast<float*>(a.ascale);
+    launch_split<SPLIT_H>(sa, s);
 }
 void launch_down_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
     T1F8Args b = a;
@@ -235,8 +287,16 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     int32_t* pair_src = at<int32_t>(ws, L.pair_src);
     int32_t* worklist = at<int32_t>(ws, L.worklist);
     ItemRec* items = at<ItemRec>(ws, L.items);
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    float* xscale = at<float>(ws, L.xscale);
+    SplitArgs sa = {};  // the T1 path's split of x, in the grouping's first launch
+    sa.src = x;
+    sa.dst = xq;
+    sa.scale = xscale;
+    sa.rows = T;
+    sa.K = ex->H;
     launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
-                 at<int32_t>(ws, L.tile_hist), items, s);
+                 at<int32_t>(ws, L.tile_hist), items, s, present[QT_T1] ? &sa : nullptr);
     mark(1);
     GateUpArgs a;
     a.x = x;
@@ -257,16 +317,12 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
     }
     if (present[QT_T1]) {
-        uint8_t* xq = at<uint8_t>(ws, L.xq);
-        int32_t* ptok = at<int32_t>(ws, L.ptok);
-        float* pscale = at<float>(ws, L.pscale);
-        hipLaunchKernelGGL(k_xsplit, dim3(T), dim3(256), 0, s, x, xq, at<int32_t>(ws, L.inv), ptok, pscale, k,
-                           ex->H);
         mark(2);
         T1F8Args b = {};
         b.act = xq;
-        b.ptok = ptok;
-        b.pscale = pscale;
+        b.ascale = xscale;
+        b.pair_src = pair_src;
+        b.k = k;
         b.arena = a.arena;
         b.items = items + (QT_T1 - 1) * ex->E;
         b.wl_len = flags + 8 + QT_T1;
@@ -322,7 +378,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     T1F8Args b = {};
     if (t1_f8) {
         b.act = at<uint8_t>(workspace, L.h8);
-        b.pscale = at<float>(workspace, L.hscale);
+        b.ascale = at<float>(workspace, L.hscale);
         b.pair_src = pair_src;
         b.arena = d.arena;
         b.items = at<ItemRec>(workspace, L.items) + (QT_T1 - 1) * experts->E;
