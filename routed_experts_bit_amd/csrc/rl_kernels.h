@@ -683,7 +683,9 @@ typedef T1F8Args GateUpF8Args;
 // The waits on the shared ring are counted explicitly (vm_barrier).  Per wave, vector-memory
 // instructions are issued in the fixed order
 //   block kb: wts(kb+1) [4*NT] | step 2kb: act(2kb+1) [GU_DMA] | step 2kb+1: act(2kb+2) [GU_DMA]
-// (prologue: act(0), wts(0)), so when step c waits for act(c) at most 4*NT (c even) or 0 (c odd)
+// (prologue: act(0), wts(0); in place of the last block's wts(nkb) and act(NS) a chunk loads the
+// next chunk's wts(0) and act(0), and the next chunk then starts with a full wait only), so when
+// step c waits for act(c) at most 4*NT (c even) or 0 (c odd)
 // later loads may still be in flight.  A wave reads the windows of block kb at the top of the
 // block; those loads have completed by then (the odd step before waits for everything, and
 // the chunk prologue is followed by a full wait).  The compiler's own tracking of
@@ -759,12 +761,17 @@ struct GuChunk {
 
     const GuShared& sh;
     const BufSrc &srcx, &srcg, &srcu;
-    const uint32_t* xoff;  // per lane: activation source offset of each of its GU_DMA loads
-    const uint32_t* roff;  // per lane: byte offset of the row it decodes, per strip
-    const uint32_t* woff;  // per lane: byte offset of its 16 bytes of a row window, per strip
+    const BufSrc &srcg_n, &srcu_n;  // weights of the next chunk
+    const uint32_t* xoff;    // per lane: activation source offset of each of its GU_DMA loads
+    const uint32_t* roff;    // per lane: byte offset of the row it decodes, per strip
+    const uint32_t* woff;    // per lane: byte offset of its 16 bytes of a row window, per strip
+    const uint32_t* woff_n;  // the same for the next chunk
+    const uint32_t* xon;     // xoff of the next chunk (written by the hook)
     const T1Lane8& ln;
     int nkb, NS, wave, m, g;
-    uint32_t rowb;         // bytes per weight row
+    uint32_t rowb;           // bytes per weight row
+    bool pf_next;            // load the next chunk's first windows and activation step
+    bool pf_have;            // this chunk's were loaded by the chunk before
     T1Dec8 dec[NT];
     RunScale rs[NT];
     f32x4 acc[MT][NT];
@@ -775,29 +782,32 @@ struct GuChunk {
         return (const uint32_t*)(wts(t) + GU_WQ * (r >> 2) + 64 * (r & 3));
     }
 
+    // step c of the activations into ring slot `slot`; c = NS: step 0 of the next chunk
     __device__ __forceinline__ void act(int c, int slot) {
-        if (c < NS) {
+        if (c < NS || pf_next) {
             uint8_t* base = sh.ring[slot] + wave * (GU_DMA * 1024);
+            const uint32_t* xo = c < NS ? xoff : xon;
+            const uint32_t so = c < NS ? (uint32_t)c * 256u : 0u;
 #pragma unroll
             for (int i = 0; i < GU_DMA; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(base + i * 1024), 16, xoff[i],
-                                                         (uint32_t)c * 256u, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(base + i * 1024), 16, xo[i], so, 0, 0);
         }
     }
     // the 64-byte windows of block kb (clamped to the last block, so that the number of loads
     // is fixed) of this wave's rows: in quarter q, lane L < 16 fetches bytes 16*(L%4).. of the
     // window of row 4q + L/4 (woff[t] holds lane L's offset for q = 0; rows are row_bytes apart)
-    __device__ __forceinline__ void wload(int kb) {
-        const uint32_t blk = (uint32_t)min(kb, nkb - 1) * BB;
+    __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo, uint32_t blk) {
         if ((threadIdx.x & 63) < 16) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? srcg : srcu).r,
-                                                             (lds_void*)(wts(t) + GU_WQ * q), 16,
-                                                             (woff[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? sg : su).r, (lds_void*)(wts(t) + GU_WQ * q),
+                                                             16, (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
         }
+    }
+    __device__ __forceinline__ void wload(int kb) {
+        wload_from(srcg, srcu, woff, (uint32_t)min(kb, nkb - 1) * BB);
     }
     // top of block kb: decoder state from this wave's windows, block scale into the
     // accumulators; then (its windows read) the next block's windows
@@ -813,7 +823,10 @@ struct GuChunk {
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // windows read before they are replaced
-        wload(kb + 1);
+        if (kb + 1 < nkb || !pf_next)
+            wload(kb + 1);
+        else
+            wload_from(srcg_n, srcu_n, woff_n, 0u);  // block 0 of the next chunk
     }
     // step c = 2*kb + H staged in ring slot H
     template <int H, class Hook>
@@ -864,9 +877,11 @@ struct GuChunk {
             for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         // vector-memory operations complete in issue order, so the stores and loads before this
         // chunk only make the counted waits below stricter
-        act(0, 0);
-        mem_fence_compiler();
-        wload(0);
+        if (!pf_have) {
+            act(0, 0);
+            mem_fence_compiler();
+            wload(0);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block 0's windows before they are read
         for (int kb = 0; kb < nkb; ++kb) {
             block_top(kb);
@@ -882,10 +897,11 @@ struct GuChunk {
 // rows' original pair indices (one row per thread of the first wave).
 template <int MODE, int NTI, int MT>
 __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, const BufSrc& srcx,
-                                         const BufSrc& srcg, const BufSrc& srcu, const uint32_t* xoff,
-                                         const uint32_t* roff, const uint32_t* woff, const T1Lane8& ln, int nkb,
-                                         int pc, int rows, int colw, bool has_next, int pn, int rows_n,
-                                         uint32_t* xon) {
+                                         const BufSrc& srcg, const BufSrc& srcu, const BufSrc& srcg_n,
+                                         const BufSrc& srcu_n, const uint32_t* xoff, const uint32_t* roff,
+                                         const uint32_t* woff, const uint32_t* woff_n, const T1Lane8& ln, int nkb,
+                                         int pc, int rows, int colw, bool has_next, bool pf_have, int pn,
+                                         int rows_n, uint32_t* xon) {
     constexpr int NMAT = MODE == T1_GATEUP ? 2 : 1;
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     float ps = 0.f;
@@ -909,8 +925,9 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
             }
         }
     };
-    GuChunk<NMAT, NTI, MT> ch{sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, 2 * nkb, wave, n, g,
-                              (uint32_t)nkb * (uint32_t)Fmt<QT_T1>::BYTES};
+    GuChunk<NMAT, NTI, MT> ch{sh,     srcx,    srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, xon, ln, nkb,
+                              2 * nkb, wave,   n,    g,    (uint32_t)nkb * (uint32_t)Fmt<QT_T1>::BYTES,
+                              has_next, pf_have};
     ch.run(hook);
     if (tid < 64) {
         sh.rscale[tid] = ps;
@@ -977,6 +994,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
 
     // first chunk: record and activation rows; later chunks are prefetched by their predecessor
     int q = 0, ix = sc.item(0), mc = 0;
+    bool pf_have = false;  // the current chunk's first windows and activations were prefetched
     ItemRec rec = load_item(a.items, sc.rank(ix));
     uint32_t xoff[GU_DMA];
     {
@@ -1005,24 +1023,29 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
         const int rows_n = has_next ? min(64, recn.ne - mcn) : 1;
         const BufSrc srcg(a.arena + rec.off[MODE == T1_GATEUP ? 0 : 2], mat_bytes);
         const BufSrc srcu(a.arena + rec.off[1], mat_bytes);
+        const BufSrc srcg_n(a.arena + recn.off[MODE == T1_GATEUP ? 0 : 2], mat_bytes);
+        const BufSrc srcu_n(a.arena + recn.off[1], mat_bytes);
         const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
-        uint32_t roff[NT], woff[NT];
+        const int colw_n = sc.slice(ixn) * (16 * NTI * GU_NW) + wave * (16 * NTI);
+        uint32_t roff[NT], woff[NT], woff_n[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
             woff[t] = (uint32_t)(colw + 16 * (t % NTI) + ((lane >> 2) & 3)) * row_bytes + 16u * (uint32_t)(lane & 3);
+            woff_n[t] = (uint32_t)(colw_n + 16 * (t % NTI) + ((lane >> 2) & 3)) * row_bytes + 16u * (uint32_t)(lane & 3);
         }
         uint32_t xon[GU_DMA];
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
         const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
         switch ((rows + 15) >> 4) {
-            case 1: t1_chunk<MODE, NTI, 1>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            case 2: t1_chunk<MODE, NTI, 2>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            case 3: t1_chunk<MODE, NTI, 3>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
-            default: t1_chunk<MODE, NTI, 4>(a, sh, srcx, srcg, srcu, xoff, roff, woff, ln, nkb, pc, rows, colw, has_next, pn, rows_n, xon); break;
+            case 1: t1_chunk<MODE, NTI, 1>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
+            case 2: t1_chunk<MODE, NTI, 2>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
+            case 3: t1_chunk<MODE, NTI, 3>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
+            default: t1_chunk<MODE, NTI, 4>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
         }
         if (!has_next) break;
+        pf_have = true;
         q = qn;
         ix = ixn;
         mc = mcn;
