@@ -665,6 +665,7 @@ struct T1F8Args {
     float* yslot;             // down output [P][N] fp32
     int K, N, ns;
     int k;                    // pairs per token (gate/up: token of pair index q is q / k)
+    int P;                    // pairs (k_t1_dn: y has a spare row P for padding rows)
 };
 typedef T1F8Args GateUpF8Args;
 
@@ -1052,6 +1053,246 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
         rec = recn;
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xoff[i] = xon[i];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// T1 down on the fp8 MFMA with the activations held in LDS (K = I <= 512).  A work item is
+// (expert, group of columns of H).  For each chunk of up to DN_ROWS of the expert's sorted pairs
+// the work-group stages the chunk's split h rows once for all of K; then every wave sweeps its
+// own columns, 16*DN_NT at a time, without work-group synchronisation: only its own weight
+// windows move (the same windows, decoder and MFMA steps as k_t1_f8).  y rows are fp32 at the
+// pairs' original index; padding rows of a tile go to the spare row P of y.
+constexpr int DN_ROWS = 48;
+constexpr int DN_NT = 4;                     // strips of 16 columns per wave per sweep
+constexpr int DN_SW = 16 * DN_NT * GU_NW;    // columns per sweep of the work-group
+constexpr int DN_KMAX = 512;
+constexpr int DN_ACT = DN_ROWS * 256;        // staged bytes per 128-value step (hi/lo fp8)
+
+template <int MT>
+struct DnSweep {
+    static constexpr int NT = DN_NT;
+    static constexpr int BB = Fmt<QT_T1>::BYTES;
+
+    const GuShared& sh;         // ring[0]: the chunk's activations [K/128 steps][DN_ROWS][256 B]
+    const BufSrc &srcw, &srcw_n;  // down matrix of this sweep and of the next one
+    const uint32_t* roff;       // per lane: byte offset of the row it decodes, per strip
+    const uint32_t* woff;       // per lane: byte offset of its 16 bytes of a row window, per strip
+    const uint32_t* woff_n;     // the same for the next sweep
+    const T1Lane8& ln;
+    int nkb, wave, m, g;
+    uint32_t rowb;
+    bool pf_next;               // load the next sweep's first windows during the last block
+    bool pf_have;               // this sweep's first windows were loaded by the sweep before
+    T1Dec8 dec[NT];
+    RunScale rs[NT];
+    f32x4 acc[MT][NT];
+
+    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * GU_WS; }
+    __device__ __forceinline__ const uint32_t* win(int t, int r) const {
+        return (const uint32_t*)(wts(t) + GU_WQ * (r >> 2) + 64 * (r & 3));
+    }
+    __device__ __forceinline__ void wload_from(const BufSrc& sw, const uint32_t* wo, uint32_t blk) {
+        if ((threadIdx.x & 63) < 16) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wts(t) + GU_WQ * q), 16,
+                                                             (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
+        }
+    }
+    // windows of block kb: the wave's own loads, so a wait on its own counter suffices
+    __device__ __forceinline__ void block_top(int kb) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t blk = (uint32_t)kb * BB;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            T1Raw8 raw;
+            raw.load_window(win(t, m), (roff[t] + blk) & 3u, g);
+            dec[t].prep(raw, ln, sh.tbl8);
+            const float r = rs[t].step(dec[t].d);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // windows read before they are replaced
+        if (kb + 1 < nkb)
+            wload_from(srcw, woff, (uint32_t)(kb + 1) * BB);
+        else if (pf_next)
+            wload_from(srcw_n, woff_n, 0u);
+    }
+    template <int H>
+    __device__ __forceinline__ void step(int c) {
+        uint32_t b[NT][8];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            dec[t].step(H, ln, sh.tsel, b[t]);
+            __builtin_amdgcn_sched_barrier(0);  // one strip's lookups in flight at a time
+        }
+        const uint8_t* act = sh.ring[0] + c * DN_ACT;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint8_t* rp = act + (mt * 16 + m) * 256;
+            uint32_t ahi[8], alo[8];
+            *(u32x4*)&ahi[0] = *(const u32x4*)(rp + (((4 * g + 0) ^ m) << 4));
+            *(u32x4*)&ahi[4] = *(const u32x4*)(rp + (((4 * g + 1) ^ m) << 4));
+            *(u32x4*)&alo[0] = *(const u32x4*)(rp + (((4 * g + 2) ^ m) << 4));
+            *(u32x4*)&alo[4] = *(const u32x4*)(rp + (((4 * g + 3) ^ m) << 4));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
+                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(acc[mt][t]));
+    }
+    __device__ __forceinline__ void run() {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!pf_have) wload_from(srcw, woff, 0u);
+        for (int kb = 0; kb < nkb; ++kb) {
+            block_top(kb);
+            step<0>(2 * kb);
+            step<1>(2 * kb + 1);
+        }
+    }
+};
+
+// All sweeps of one chunk (MT row tiles) of a work item: columns cbase + s*DN_SW, s < nsw.
+template <int MT>
+__device__ __forceinline__ void dn_chunk(const T1F8Args& a, const GuShared& sh, const BufSrc& srcw,
+                                         const BufSrc& srcw_next_item, const T1Lane8& ln, int nkb, uint32_t rowb,
+                                         int cbase, int nsw, int cbase_next, bool next_item) {
+    const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
+    bool pf_have = true;  // the first sweep's windows were loaded before the chunk's staging
+    for (int s = 0; s < nsw; ++s) {
+        const int col0 = cbase + s * DN_SW + wave * (16 * DN_NT);
+        const bool last = s + 1 == nsw;
+        const int col0n = last ? cbase_next + wave * (16 * DN_NT) : col0 + DN_SW;
+        uint32_t roff[DN_NT], woff[DN_NT], woff_n[DN_NT];
+#pragma unroll
+        for (int t = 0; t < DN_NT; ++t) {
+            roff[t] = (uint32_t)(col0 + 16 * t + n) * rowb;
+            woff[t] = (uint32_t)(col0 + 16 * t + ((lane >> 2) & 3)) * rowb + 16u * (uint32_t)(lane & 3);
+            woff_n[t] = (uint32_t)(col0n + 16 * t + ((lane >> 2) & 3)) * rowb + 16u * (uint32_t)(lane & 3);
+        }
+        DnSweep<MT> sw{sh, srcw, last ? srcw_next_item : srcw, roff, woff, woff_n, ln, nkb, wave, n, g, rowb,
+                       !last || next_item, pf_have};
+        sw.run();
+        // y rows of the tile (padding rows to the spare row)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mt * 16 + 4 * g + i;
+                const float xs = sh.rscale[r];
+                float* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + col0 + n;
+#pragma unroll
+                for (int t = 0; t < DN_NT; ++t) yrow[16 * t] = sw.acc[mt][t][i] * sw.rs[t].dprev * xs;
+            }
+        pf_have = true;
+    }
+}
+
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
+    constexpr int NTHR = 64 * GU_NW;
+    constexpr int BB = Fmt<QT_T1>::BYTES;
+    __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
+    __shared__ uint32_t tbl8[8];
+    __shared__ float rscale[DN_ROWS];
+    __shared__ int32_t rdst[DN_ROWS];
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * DN_NT * GU_WS];
+    __shared__ __attribute__((aligned(16))) uint8_t actb[(DN_KMAX / 128) * DN_ACT];
+    const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, g = lane >> 4;
+    const StaticSched sc(uni(*a.wl_len), a.ns);
+    if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
+    for (int i = tid; i < TSEL_ENTRIES; i += NTHR) tsel[i] = tsel_entry(i);
+    if (tid < 8) {
+        const float sv = (float)tid;
+        const uint32_t pos = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv, 0.f, 0, false) & 255u;
+        const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
+        tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
+    }
+    const GuShared sh{{actb, actb}, wts, tsel, tbl8, rscale, rdst};
+    T1Lane8 ln;
+    ln.init(g);
+    const int nkb = a.K >> 8, NS = 2 * nkb;
+    const uint32_t rowb = (uint32_t)nkb * BB;
+    const uint32_t mat_bytes = (uint32_t)a.N * rowb;
+    const int P = a.P;  // y row P is the spare row
+    const BufSrc srcx(a.act, 0x7FFFFFF0u);
+    const int cw = a.N / a.ns;        // columns per item
+    const int nsw = cw / DN_SW;
+    // staging of a chunk: 3*NS loads of 1 KB per wave, each 4 rows x 256 bytes of one step
+    auto stage = [&](int pc, int rows) {
+#pragma unroll 4
+        for (int j = 0; j < 3 * NS; ++j) {
+            const int J = wave * 3 * NS + j;         // 0 .. 12*NS-1
+            const int c = J / 12, rg = J % 12;
+            const int row = 4 * rg + (lane >> 4);
+            const int pr = pc + (row < rows ? row : 0);
+            const uint32_t off = (uint32_t)pr * (uint32_t)(2 * a.K) + (uint32_t)c * 256u +
+                                 16u * (uint32_t)((lane & 15) ^ (row & 15));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(actb + c * DN_ACT + rg * 1024), 16, off, 0, 0, 0);
+        }
+        if (tid < DN_ROWS) {
+            rscale[tid] = tid < rows ? a.ascale[pc + tid] : 0.f;
+            rdst[tid] = tid < rows ? a.pair_src[pc + tid] : P;
+        }
+    };
+    int q = 0, ix = sc.item(0), mc = 0;
+    ItemRec rec = load_item(a.items, sc.rank(ix));
+    __syncthreads();  // tables
+    bool first = true;
+    while (true) {
+        int qn = q, ixn = ix, mcn = mc + DN_ROWS;
+        ItemRec recn = rec;
+        bool has_next = true;
+        if (mcn >= rec.ne) {
+            qn = q + 1;
+            ixn = sc.item(qn);
+            mcn = 0;
+            has_next = ixn < sc.nitems;
+            if (has_next) recn = load_item(a.items, sc.rank(ixn));
+        }
+        const int rows = min(DN_ROWS, rec.ne - mc);
+        const BufSrc srcw(a.arena + rec.off[2], mat_bytes);
+        const BufSrc srcw_n(a.arena + recn.off[2], mat_bytes);
+        const int cbase = sc.slice(ix) * cw, cbase_n = sc.slice(ixn) * cw;
+        if (!first) __syncthreads();  // every wave is done with the previous chunk's activations
+        stage(rec.p0 + mc, rows);
+        if (first) {  // the first sweep's windows (later ones are loaded by the sweep before)
+            const int col0 = cbase + wave * (16 * DN_NT);
+            if ((lane & 63) < 16) {
+#pragma unroll
+                for (int t = 0; t < DN_NT; ++t)
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const uint32_t wo = (uint32_t)(col0 + 16 * t + ((lane >> 2) & 3)) * rowb + 16u * (uint32_t)(lane & 3);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wts + (wave * DN_NT + t) * GU_WS + GU_WQ * qq),
+                                                                 16, (wo + 4u * (uint32_t)qq * rowb) & ~3u, 0, 0, 0);
+                    }
+            }
+            first = false;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // the chunk's activations and row tables
+        switch ((rows + 15) >> 4) {
+            case 1: dn_chunk<1>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+            case 2: dn_chunk<2>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+            default: dn_chunk<3>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+        }
+        if (!has_next) break;
+        q = qn;
+        ix = ixn;
+        mc = mcn;
+        rec = recn;
     }
 }
 

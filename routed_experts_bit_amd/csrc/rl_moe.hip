@@ -63,8 +63,8 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + P * sizeof(float));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
-    L.yslot = off;
-    off = align_up(off + P * (size_t)H * sizeof(float));
+    L.yslot = off;  // row t*k + j of each pair, plus a spare row for the padding rows of tiles
+    off = align_up(off + (P + 1) * (size_t)H * sizeof(float));
     L.total = off;
     return L;
 }
@@ -229,6 +229,13 @@ void launch_hsplit(const T1F8Args& a, int P, hipStream_t s) {
 }
 void launch_down_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
     T1F8Args b = a;
+    if (a.K <= DN_KMAX) {  // activations held in LDS; items of up to 1024 columns
+        const int cw = a.N % 1024 == 0 ? 1024 : (a.N % 512 == 0 ? 512 : 256);
+        b.ns = a.N / cw;
+        const int grid = grid_cap(resident_grid<k_t1_dn>(64 * GU_NW), n_experts, b.ns);
+        hipLaunchKernelGGL(k_t1_dn, dim3(grid), dim3(64 * GU_NW), 0, s, b);
+        return;
+    }
     b.ns = a.N / 256;
     const int grid = grid_cap(resident_grid<k_t1_f8<T1_DOWN, 4>>(64 * GU_NW), n_experts, b.ns);
     hipLaunchKernelGGL((k_t1_f8<T1_DOWN, 4>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
@@ -387,6 +394,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
         b.yslot = yslot;
         b.K = experts->I;
         b.N = experts->H;
+        b.P = T * k;
         launch_hsplit(b, T * k, s);
     }
     mark(4);
