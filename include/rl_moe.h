@@ -91,14 +91,13 @@ int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk
                    void* workspace, size_t ws_bytes, void* stream);
 
 /* Measurement hook: rl_moe_prefill with RL_TIMED_EVENTS events (events [host] array of
- * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels
- * (whose first launch also splits x for the T1 path), 1 after them, 2 at the same place (the
- * x split no longer has a launch of its own), 3 after the gate/up kernel(s),
- * 4 after the split of h for the T1 down path, 5 after the down kernel(s), 6 after the combine
- * (an event whose kernel a layer does not use is recorded at the same place as the one before
- * it), so that the caller can time each kernel on the stream the kernels run on.  Otherwise
+ * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels (whose
+ * first launch also splits x for the T1 path), 1 after them, 2 after the gate/up kernel(s), 3
+ * after the split of h for the T1 down path, 4 after the down kernel(s), 5 after the combine (an
+ * event whose kernel a layer does not use is recorded at the same place as the one before it),
+ * so that the caller can time each kernel on the stream the kernels run on.  Otherwise
  * identical to rl_moe_prefill; RL_EINVAL if an event is NULL. */
-#define RL_TIMED_EVENTS 7
+#define RL_TIMED_EVENTS 6
 int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                          const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                          void* workspace, size_t ws_bytes, void* stream, void* const* events);

@@ -175,12 +175,12 @@ def prefill(x, ids, w, ex: DeviceExperts, out=None, ws=None):
     return out
 
 
-TIMED_EVENTS = 7  # RL_TIMED_EVENTS
+TIMED_EVENTS = 6  # RL_TIMED_EVENTS
 
 
 def prefill_timed(x, ids, w, ex: DeviceExperts, out, ws, events):
     """rl_moe_prefill with TIMED_EVENTS torch.cuda.Event (enable_timing) recorded between its
-    kernels: grouping | activation split | gate/up | h split | down | combine."""
+    kernels: grouping (which also splits x) | gate/up | h split | down | combine."""
     T, k = ids.shape
     if len(events) != TIMED_EVENTS:
         raise RlError(f"prefill_timed needs {TIMED_EVENTS} events")

@@ -1229,11 +1229,14 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
     const BufSrc srcx(a.act, 0x7FFFFFF0u);
     const int cw = a.N / a.ns;        // columns per item
     const int nsw = cw / DN_SW;
-    // staging of a chunk: 3*NS loads of 1 KB per wave, each 4 rows x 256 bytes of one step
+    // staging of a chunk: 12*NS loads of 1 KB (each 4 rows x 256 bytes of one step), shared by
+    // the waves (12*NS is a multiple of 24, so of GU_NW)
+    static_assert(24 % GU_NW == 0, "staging loads split evenly over the waves");
+    const int npw = 12 * NS / GU_NW;
     auto stage = [&](int pc, int rows) {
 #pragma unroll 4
-        for (int j = 0; j < 3 * NS; ++j) {
-            const int J = wave * 3 * NS + j;         // 0 .. 12*NS-1
+        for (int j = 0; j < npw; ++j) {
+            const int J = wave * npw + j;            // 0 .. 12*NS-1
             const int c = J / 12, rg = J % 12;
             const int row = 4 * rg + (lane >> 4);
             const int pr = pc + (row < rows ? row : 0);

@@ -316,7 +316,6 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     a.I = ex->I;
     a.k = k;
     a.ns = 1;
-    if (!present[QT_T1]) mark(2);
     if (present[QT_Q2B]) {
         a.worklist = worklist + (QT_Q2B - 1) * ex->E;
         a.wl_len = flags + 8 + QT_Q2B;
@@ -324,7 +323,6 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
     }
     if (present[QT_T1]) {
-        mark(2);
         T1F8Args b = {};
         b.act = xq;
         b.ascale = xscale;
@@ -339,7 +337,7 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         b.ns = 1;
         launch_gateup_f8(b, present[QT_T1], s);
     }
-    mark(3);
+    mark(2);
 }
 
 }  // namespace
@@ -397,7 +395,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
         b.P = T * k;
         launch_hsplit(b, T * k, s);
     }
-    mark(4);
+    mark(3);
     for (int q = QT_Q2B; q <= QT_T1; ++q) {
         if (!present[q]) continue;
         d.worklist = worklist + (q - 1) * experts->E;
@@ -410,9 +408,9 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
         else
             launch_down_t<QT_T1>(d, present[q], s);
     }
-    mark(5);
+    mark(4);
     hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
-    mark(6);
+    mark(5);
     return hip_status();
 }
 

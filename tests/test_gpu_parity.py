@@ -224,6 +224,29 @@ def test_repeated_calls_identical(rl, cases, name):
         assert torch.equal(rl.gate_up(x, ids, w, ex, ws=ws), h0)
 
 
+@pytest.mark.parametrize("name", ["med_t1", "tiny_q2b"])
+def test_timed_hook_matches_prefill(rl, cases, name):
+    """rl_moe_prefill_timed: the same output bits as rl_moe_prefill, and its events recorded in
+    order on the call's stream (every interval non-negative)."""
+    import torch
+
+    wl = _case(cases, name)
+    x, ids, w, ex = to_device(wl)
+    ws = rl.alloc_workspace(wl.T, wl.k, ex)
+    ref = rl.prefill(x, ids, w, ex, ws=ws).clone()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(rl.TIMED_EVENTS)]
+    stream = torch.cuda.current_stream()
+    for e in evs:
+        e.record(stream)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    rl.prefill_timed(x, ids, w, ex, out, ws, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    gaps = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
+    assert all(g >= 0.0 for g in gaps), gaps
+
+
 def test_empty_input(rl, cases):
     import torch
 
