@@ -20,7 +20,9 @@
  * Errors: a negative status is returned synchronously, before anything is launched, and
  * `out` is then untouched.  An expert id outside [0, E) is only seen on the device: it sets
  * bit 0 of the workspace status flags (read with rl_moe_status after the stream is synced);
- * such a token's output is then unspecified, every other token's is still correct.
+ * such a token's output is then unspecified, every other token's is still correct.  The
+ * per-pair down outputs are kept in fp16 (as h is): one beyond the fp16 range (|y| >= 65520)
+ * sets bit 2 of the status flags, and its token's output is then infinite.
  */
 #ifndef RL_MOE_H
 #define RL_MOE_H

@@ -3,7 +3,7 @@
 //   k_group_*    token-expert pairs grouped per expert (stable, deterministic), plus the
 //                per-type expert work lists, longest expert first
 //   k_gateup     fused block decode + gate/up grouped GEMM (bf16 MFMA) + SwiGLU -> h (fp16)
-//   k_down       fused block decode + down grouped GEMM (fp16 MFMA) -> y per pair (fp32)
+//   k_down       fused block decode + down grouped GEMM (fp16 MFMA) -> y per pair (fp16)
 //   k_combine    out_t = sum_j w[t][j] * y_{t,j}, j ascending (selection order)
 //   k_gv_gateup  1-2 row matrix-vector gate/up + SwiGLU (fp32 VALU, 16 lanes per row)
 //   k_gv_down    1-2 row matrix-vector down + ordered combine in one dispatch
@@ -23,6 +23,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int FLAG_BAD_ID = 1;
 constexpr int FLAG_BAD_QTYPE = 2;
+constexpr int FLAG_Y_RANGE = 4;   // a per-pair down output beyond the fp16 range
 constexpr int FLAGS_WORDS = 64;   // flags[0] error bits; flags[8 + q] work-list length of type q
 constexpr int MAX_E = 1024;
 
@@ -40,6 +41,16 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// y (the per-pair down outputs, summed later by k_combine) is kept in fp16; a value that rounds
+// beyond the fp16 range marks the call's status flags.
+__device__ __forceinline__ uint16_t y_bits(float v, bool& ovf) {
+    ovf |= fabsf(v) >= 65520.0f;
+    return f32_to_f16_bits(v);
+}
+__device__ __forceinline__ void y_range_flag(bool ovf, int32_t* flags) {
+    if (__ballot(ovf) != 0ull && __lane_id() == 0) atomicOr(flags, FLAG_Y_RANGE);
+}
 
 // ---------------------------------------------------------------------------------------
 // Pair grouping: two kernels over tiles of GT consecutive flattened pairs p = t*k + j.
@@ -652,7 +663,7 @@ __device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f
 // The two T1 expert GEMMs on the fp8 MFMA.  Gate/up: activations xq (split x, token rows,
 // gathered through the token pair_src[p] / k of each sorted pair p), weights gate and up [I][H], output h (fp16, SwiGLU, sorted-pair
 // rows).  Down: activations h8 (split h, sorted-pair rows), weights down [H][I], output y
-// (fp32, row = original pair index t*k + j).  K is the contracted length, N the output width.
+// (fp16, row = original pair index t*k + j).  K is the contracted length, N the output width.
 enum { T1_GATEUP = 0, T1_DOWN = 1 };
 struct T1F8Args {
     const uint8_t* act;       // [rows][2K] split activations (hi/lo fp8, t1_kmap order)
@@ -662,7 +673,8 @@ struct T1F8Args {
     const ItemRec* items;     // this type's work list, longest first
     const int32_t* wl_len;    // its length (device)
     uint16_t* hbuf;           // gate/up output [P][N] fp16
-    float* yslot;             // down output [P][N] fp32
+    uint16_t* yslot;          // down output [P+1][N] fp16
+    int32_t* flags;           // status words (flags[0])
     int K, N, ns;
     int k;                    // pairs per token (gate/up: token of pair index q is q / k)
     int P;                    // pairs (k_t1_dn: y has a spare row P for padding rows)
@@ -935,6 +947,7 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
         if constexpr (MODE == T1_DOWN) sh.rdst[tid] = pdst;
     }
     lds_barrier();
+    bool ovf = false;
     // lane holds rows 4g..4g+3 of each 16-row tile, column n
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -951,12 +964,13 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
                         a.hbuf[(size_t)(pc + r) * a.N + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
                     }
                 } else {
-                    float* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + colw + n;
+                    uint16_t* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + colw + n;
 #pragma unroll
-                    for (int t = 0; t < NTI; ++t) yrow[16 * t] = ch.acc[mt][t][i] * ch.rs[t].dprev * xs;
+                    for (int t = 0; t < NTI; ++t) yrow[16 * t] = y_bits(ch.acc[mt][t][i] * ch.rs[t].dprev * xs, ovf);
                 }
             }
         }
+    if constexpr (MODE == T1_DOWN) y_range_flag(ovf, a.flags);
     // rscale and rdst are rewritten only after the next chunk's step barriers
 }
 
@@ -1186,16 +1200,18 @@ __device__ __forceinline__ void dn_chunk(const T1F8Args& a, const GuShared& sh, 
                        !last || next_item, pf_have};
         sw.run();
         // y rows of the tile (padding rows to the spare row)
+        bool ovf = false;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = mt * 16 + 4 * g + i;
                 const float xs = sh.rscale[r];
-                float* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + col0 + n;
+                uint16_t* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + col0 + n;
 #pragma unroll
-                for (int t = 0; t < DN_NT; ++t) yrow[16 * t] = sw.acc[mt][t][i] * sw.rs[t].dprev * xs;
+                for (int t = 0; t < DN_NT; ++t) yrow[16 * t] = y_bits(sw.acc[mt][t][i] * sw.rs[t].dprev * xs, ovf);
             }
+        y_range_flag(ovf, a.flags);
         pf_have = true;
     }
 }
@@ -1308,7 +1324,8 @@ struct DownArgs {
     const int32_t* worklist;
     const int32_t* wl_len;
     int32_t* counters;
-    float* yslot;  // [T*k][H] fp32, row t*k + j
+    uint16_t* yslot;  // [T*k + 1][H] fp16, row t*k + j
+    int32_t* flags;
     int H, I, ns;
 };
 
@@ -1427,6 +1444,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
                 case 3: down_chunk<QT, LCH, NW, NTW, 3>(a, tab, As, srch, src, sx, col0, acc, rs); break;
                 default: down_chunk<QT, LCH, NW, NTW, 4>(a, tab, As, srch, src, sx, col0, acc, rs); break;
             }
+            bool ovf = false;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (mt < mtiles) {
@@ -1434,32 +1452,38 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
                     for (int i = 0; i < 4; ++i) {
                         const int r = mt * 16 + 4 * g + i;
                         if (r < rows) {
-                            float* yrow = a.yslot + (size_t)a.pair_src[p0 + mc + r] * a.H + col0 + n;
+                            uint16_t* yrow = a.yslot + (size_t)a.pair_src[p0 + mc + r] * a.H + col0 + n;
 #pragma unroll
-                            for (int t = 0; t < NTW; ++t) yrow[16 * t] = acc[mt][t][i] * rs[t].dprev;
+                            for (int t = 0; t < NTW; ++t) yrow[16 * t] = y_bits(acc[mt][t][i] * rs[t].dprev, ovf);
                         }
                     }
                 }
             }
+            y_range_flag(ovf, a.flags);
         }
     }
 }
 
 // out[t][c] = sum over j = 0..k-1 (ascending) of w[t][j] * y[t*k + j][c]; one work-group per
 // token, four columns per thread (16-byte loads).
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ yslot, const float* __restrict__ w,
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yslot, const float* __restrict__ w,
                                                  float* __restrict__ out, int k, int H) {
     const int t = blockIdx.x;
     const float* wt = w + (size_t)t * k;
-    for (int c = 4 * threadIdx.x; c < H; c += 4 * 256) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 8 * threadIdx.x; c < H; c += 8 * 256) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
             const float wj = wt[j];
-            const f32x4 y = *(const f32x4*)(yslot + ((size_t)t * k + j) * H + c);
+            const u32x4 y = *(const u32x4*)(yslot + ((size_t)t * k + j) * H + c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __fmaf_rn(wj, y[i], acc[i]);
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = __fmaf_rn(wj, half_bits_to_float(y[i] & 0xFFFFu), acc[2 * i]);
+                acc[2 * i + 1] = __fmaf_rn(wj, half_bits_to_float(y[i] >> 16), acc[2 * i + 1]);
+            }
         }
-        *(f32x4*)(out + (size_t)t * H + c) = acc;
+        f32x4* o = (f32x4*)(out + (size_t)t * H + c);
+        o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
     }
 }
 

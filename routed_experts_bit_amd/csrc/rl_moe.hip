@@ -64,7 +64,7 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
     L.yslot = off;  // row t*k + j of each pair, plus a spare row for the padding rows of tiles
-    off = align_up(off + (P + 1) * (size_t)H * sizeof(float));
+    off = align_up(off + (P + 1) * (size_t)H * sizeof(uint16_t));
     L.total = off;
     return L;
 }
@@ -365,7 +365,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     int32_t* offsets = at<int32_t>(workspace, L.offsets);
     int32_t* pair_src = at<int32_t>(workspace, L.pair_src);
     int32_t* worklist = at<int32_t>(workspace, L.worklist);
-    float* yslot = at<float>(workspace, L.yslot);
+    uint16_t* yslot = at<uint16_t>(workspace, L.yslot);
     mark(0);
     Layout L2;  // same layout as L
     run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events);
@@ -376,6 +376,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     d.offsets = offsets;
     d.pair_src = pair_src;
     d.yslot = yslot;
+    d.flags = flags;
     d.H = experts->H;
     d.I = experts->I;
     d.ns = 1;
@@ -390,6 +391,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
         b.wl_len = flags + 8 + QT_T1;
         b.hbuf = hbuf;
         b.yslot = yslot;
+        b.flags = flags;
         b.K = experts->I;
         b.N = experts->H;
         b.P = T * k;
