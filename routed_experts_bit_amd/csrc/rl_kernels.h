@@ -59,10 +59,10 @@ __device__ __forceinline__ void y_range_flag(bool ovf, int32_t* flags) {
 //                    histograms) plus the exclusive scan of all counts place the tile's pairs;
 //                    inside the tile wave w owns a contiguous run and lanes holding the same
 //                    expert are found with ballots over the bits of the id and ranked by lane.
-// The sorted order is (expert, token, slot), identical to a sequential stable sort.  Tile 0
-// also writes the offsets and the per-type work lists (experts with pairs, more pairs first;
-// ties and experts above 255 pairs come in no particular order: the lists only steer
-// scheduling).
+// The sorted order is (expert, token, slot), identical to a sequential stable sort.  One extra
+// work-group (index ntiles, no pairs of its own) writes the offsets and the per-type work lists
+// (experts with pairs, more pairs first; ties and experts above 255 pairs come in no particular
+// order: the lists only steer scheduling) while the tiles scatter.
 constexpr int GT = 1024;           // pairs per tile
 constexpr int GROUP_NTHR = 256;    // threads per grouping work-group
 constexpr int NBIN = 256;
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     __shared__ int32_t bins[2][NBIN];
     __shared__ int32_t bad_sh;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tile = blockIdx.x;
+    const bool lister = tile == a.ntiles;  // the offsets and work lists; no pairs (n <= 0)
     const int E = a.E;
     const int p0 = tile * GT, n = min(a.P - p0, GT);
     if (tid == 0) bad_sh = 0;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             run += c;
         }
     }
-    if (tile == 0)
+    if (lister)
         for (int e = tid; e <= E; e += GROUP_NTHR) a.offsets[e] = e == 0 ? 0 : scan[e - 1];
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -218,8 +219,8 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     __syncthreads();
     if (tid == 0 && bad_sh) atomicOr(&a.flags[0], FLAG_BAD_ID);
 
-    // tile 0: per-type work lists, binned by pair count
-    if (tile == 0 && a.desc != nullptr) {
+    // per-type work lists, binned by pair count
+    if (lister && a.desc != nullptr) {
         for (int i = tid; i < 2 * NBIN; i += GROUP_NTHR) (&bins[0][0])[i] = 0;
         __syncthreads();
         for (int e = tid; e < E; e += GROUP_NTHR) {

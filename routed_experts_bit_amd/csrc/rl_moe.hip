@@ -140,7 +140,7 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
     } else {
         hipLaunchKernelGGL(k_group_count, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
     }
-    hipLaunchKernelGGL(k_group_scatter, dim3(g.ntiles), dim3(GROUP_NTHR), 0, s, g);
+    hipLaunchKernelGGL(k_group_scatter, dim3(g.ntiles + 1), dim3(GROUP_NTHR), 0, s, g);  // + the lister
 }
 
 // Persistent grids: as many work-groups as fit on the device at once (occupancy query, cached
