@@ -1504,10 +1504,8 @@ struct GvTables {
 // sum over the S values of one strip (inside one block) of w_i * xs[i], times the block scale;
 // xs is bf16 bits (XS_BF16) or fp32.  Fixed order: i ascending, then the scale.
 template <int QT, int S, bool XS_BF16>
-__device__ __forceinline__ float strip_dot(const BufSrc& src, uint32_t blk_off, int vs, const void* xs,
-                                           const DecodeTables<QT, false>& tb) {
-    StripRaw<QT, S> raw;
-    raw.load(src, blk_off, vs);
+__device__ __forceinline__ float strip_dot_raw(const StripRaw<QT, S>& raw, const void* xs,
+                                               const DecodeTables<QT, false>& tb) {
     Strip<QT, S> st;
     st.prepare(raw, tb.tern);
     float part = 0.f;
@@ -1524,26 +1522,38 @@ __device__ __forceinline__ float strip_dot(const BufSrc& src, uint32_t blk_off, 
     return part * st.d;
 }
 
-// span values of row `row` of a [rows x C] matrix (mat_bytes long) starting at column c0,
-// strips of S
-template <int QMASK, int S, bool XS_BF16>
+// nst (<= MAXS) strips of S values of row `row` of a [rows x C] matrix, starting at column c0:
+// the sum over the strips in ascending order.  All the strips' loads are issued before the first
+// is decoded, so a lane waits for memory once.
+template <int QT, int S, int MAXS, bool XS_BF16>
+__device__ __forceinline__ float row_dot_t(const BufSrc& src, int C, int row, int c0, int nst, const void* xs,
+                                           const DecodeTables<QT, false>& tb) {
+    StripRaw<QT, S> raw[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s)
+        if (s < nst) {
+            const uint32_t flat = (uint32_t)row * (uint32_t)C + (uint32_t)(c0 + s * S);
+            raw[s].load(src, (flat >> 8) * Fmt<QT>::BYTES, (int)(flat & 255));
+        }
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s)
+        if (s < nst)
+            acc += strip_dot_raw<QT, S, XS_BF16>(
+                raw[s], XS_BF16 ? (const void*)((const uint16_t*)xs + s * S) : (const void*)((const float*)xs + s * S), tb);
+    return acc;
+}
+
+template <int QMASK, int S, int MAXS, bool XS_BF16>
 __device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, uint32_t mat_bytes, int C, int row, int c0,
                                          int span, const void* xs, const GvTables<QMASK>& tb) {
     const BufSrc src(W, mat_bytes);
-    float acc = 0.f;
-    for (int s = 0; s < span; s += S) {
-        const uint32_t flat = (uint32_t)row * (uint32_t)C + (uint32_t)(c0 + s);
-        const void* xp = XS_BF16 ? (const void*)((const uint16_t*)xs + s) : (const void*)((const float*)xs + s);
-        if constexpr (QMASK & 2) {
-            if (QMASK == 2 || qtype == QT_T1) {
-                acc += strip_dot<QT_T1, S, XS_BF16>(src, (flat >> 8) * Fmt<QT_T1>::BYTES, (int)(flat & 255), xp, tb.t1);
-                continue;
-            }
-        }
-        if constexpr (QMASK & 1)
-            acc += strip_dot<QT_Q2B, S, XS_BF16>(src, (flat >> 8) * Fmt<QT_Q2B>::BYTES, (int)(flat & 255), xp, tb.q2b);
+    const int nst = span / S;
+    if constexpr (QMASK & 2) {
+        if (QMASK == 2 || qtype == QT_T1) return row_dot_t<QT_T1, S, MAXS, XS_BF16>(src, C, row, c0, nst, xs, tb.t1);
     }
-    return acc;
+    if constexpr (QMASK & 1) return row_dot_t<QT_Q2B, S, MAXS, XS_BF16>(src, C, row, c0, nst, xs, tb.q2b);
+    return 0.f;
 }
 
 struct GvArgs {
@@ -1558,10 +1568,32 @@ struct GvArgs {
     int R, k, E, H, I;
 };
 
+// The call's pairs (R*k <= 32) read once per work-group: expert (-1 for an id outside [0, E)),
+// type and matrix offsets, so that a wave's weight loads wait on LDS rather than on two
+// dependent global loads.
+struct GvPair {
+    int32_t e, qt;
+    uint64_t gate_off, up_off, down_off;
+};
+constexpr int GV_MAX_PAIRS = 32;
+
+__device__ __forceinline__ void gv_load_pairs(const GvArgs& a, GvPair* sp) {
+    const int tid = threadIdx.x;
+    if (tid < a.R * a.k) {
+        const int e = a.ids[tid];
+        GvPair p{-1, 0, 0, 0, 0};
+        if (e >= 0 && e < a.E) {
+            const rl_expert_desc d = a.desc[e];
+            p = GvPair{e, d.qtype, d.gate_off, d.up_off, d.down_off};
+        }
+        sp[tid] = p;
+    }
+}
+
 // A wave computes features i0, i0+1 of one (row, slot) pair: lanes 0-15 gate row i0, 16-31
 // gate i0+1, 32-47 up i0, 48-63 up i0+1; each lane covers H/16 consecutive values (two lanes
 // per 256-value block when H = 2048), then a fixed xor tree reduces the 16 partial sums.
-template <int QMASK, int S1>
+template <int QMASK, int S1, int MAXS>
 __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
     __shared__ GvTables<QMASK> tb;
     tb.build(threadIdx.x, 256);
@@ -1582,7 +1614,7 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
             const rl_expert_desc dsc = a.desc[e];
             const uint8_t* W = a.arena + (rs < 2 ? dsc.gate_off : dsc.up_off);
             const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 * (dsc.qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
-            part = row_dot<QMASK, S1, true>(dsc.qtype, W, mb, a.H, row, q * span, span, a.x + (size_t)r * a.H + q * span, tb);
+            part = row_dot<QMASK, S1, MAXS, true>(dsc.qtype, W, mb, a.H, row, q * span, span, a.x + (size_t)r * a.H + q * span, tb);
         }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
@@ -1593,30 +1625,72 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
 
 // One wave per (row r, output column c): lane group gq = lane/16 takes slot j = 4*round + gq,
 // each lane I/16 values of row c of that expert's W_down; after the 16-lane reduction the slot
-// outputs are added to the accumulator in selection order j = 0..k-1.
-template <int QMASK, int S2>
+// outputs are added to the accumulator in selection order j = 0..k-1.  The weights of all
+// rounds are loaded before the first is decoded.
+template <int QMASK, int S2, int MAXS>
 __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
     __shared__ GvTables<QMASK> tb;
+    __shared__ GvPair sp[GV_MAX_PAIRS];
+    __shared__ float wsh[GV_MAX_PAIRS];
     tb.build(threadIdx.x, 256);
+    gv_load_pairs(a, sp);
+    if (threadIdx.x < a.R * a.k) {
+        wsh[threadIdx.x] = a.w[threadIdx.x];
+        const int e = a.ids[threadIdx.x];
+        if (blockIdx.x == 0 && (e < 0 || e >= a.E)) atomicOr(&a.flags[0], FLAG_BAD_ID);
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63, gq = lane >> 4, q = lane & 15;
     const int span = a.I >> 4;
+    const int nst = span / S2;
+    constexpr int MAXR = GV_MAX_PAIRS / 2 / 4;  // rounds of 4 slots (k <= 16)
     for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < a.R * a.H; wv += gridDim.x * 4) {
         const int r = wv / a.H, c = wv % a.H;
+        // loads of every round
+        StripRaw<QT_T1, S2> rt[MAXR][MAXS];
+        StripRaw<QT_Q2B, S2> rq[MAXR][MAXS];
+#pragma unroll
+        for (int rd = 0; rd < MAXR; ++rd) {
+            const int j = 4 * rd + gq;
+            if (4 * rd < a.k && j < a.k) {
+                const GvPair p = sp[r * a.k + j];
+                if (p.e >= 0) {
+                    const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 * (p.qt == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
+                    const BufSrc src(a.arena + p.down_off, mb);
+#pragma unroll
+                    for (int st = 0; st < MAXS; ++st)
+                        if (st < nst) {
+                            const uint32_t flat = (uint32_t)c * (uint32_t)a.I + (uint32_t)(q * span + st * S2);
+                            if ((QMASK & 2) && (QMASK == 2 || p.qt == QT_T1))
+                                rt[rd][st].load(src, (flat >> 8) * Fmt<QT_T1>::BYTES, (int)(flat & 255));
+                            else if (QMASK & 1)
+                                rq[rd][st].load(src, (flat >> 8) * Fmt<QT_Q2B>::BYTES, (int)(flat & 255));
+                        }
+                }
+            }
+        }
         float acc = 0.f;
-        for (int j0 = 0; j0 < a.k; j0 += 4) {
+#pragma unroll
+        for (int rd = 0; rd < MAXR; ++rd) {
+            const int j0 = 4 * rd;
+            if (j0 >= a.k) break;
             const int j = j0 + gq;
             float part = 0.f;
             if (j < a.k) {
-                const int e = a.ids[r * a.k + j];
-                if ((e < 0 || e >= a.E) && q == 0)
-                    __hip_atomic_fetch_or(&a.flags[0], FLAG_BAD_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (e >= 0 && e < a.E) {
-                    const rl_expert_desc dsc = a.desc[e];
-                    const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 *
-                                                   (dsc.qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
-                    part = row_dot<QMASK, S2, false>(dsc.qtype, a.arena + dsc.down_off, mb, a.I, c, q * span, span,
-                                                     a.hgv + (size_t)(r * a.k + j) * a.I + q * span, tb);
+                const GvPair p = sp[r * a.k + j];
+                if (p.e >= 0) {
+                    const float* hx = a.hgv + (size_t)(r * a.k + j) * a.I + q * span;
+#pragma unroll
+                    for (int st = 0; st < MAXS; ++st)
+                        if (st < nst) {
+                            if constexpr (QMASK & 2) {
+                                if (QMASK == 2 || p.qt == QT_T1) {
+                                    part += strip_dot_raw<QT_T1, S2, false>(rt[rd][st], hx + st * S2, tb.t1);
+                                    continue;
+                                }
+                            }
+                            if constexpr (QMASK & 1) part += strip_dot_raw<QT_Q2B, S2, false>(rq[rd][st], hx + st * S2, tb.q2b);
+                        }
                 }
             }
 #pragma unroll
@@ -1624,7 +1698,7 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 const float y = __shfl(part, 16 * s2, 64);
-                if (j0 + s2 < a.k) acc = __fmaf_rn(a.w[r * a.k + j0 + s2], y, acc);
+                if (j0 + s2 < a.k) acc = __fmaf_rn(wsh[r * a.k + j0 + s2], y, acc);
             }
         }
         if (lane == 0) a.out[(size_t)r * a.H + c] = acc;

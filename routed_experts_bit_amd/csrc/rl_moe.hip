@@ -265,20 +265,37 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
     const int waves2 = a.R * a.H;
     dim3 g1((waves1 + 3) / 4 < 1024 ? (waves1 + 3) / 4 : 1024);
     dim3 g2((waves2 + 3) / 4 < 1024 ? (waves2 + 3) / 4 : 1024);
-    const int s1 = a.H >= 1024 ? 64 : a.H / 16;
-    const int s2 = a.I >= 1024 ? 64 : a.I / 16;
-    if (s1 == 64)
-        hipLaunchKernelGGL((k_gv_gateup<QMASK, 64>), g1, dim3(256), 0, s, a);
-    else if (s1 == 32)
-        hipLaunchKernelGGL((k_gv_gateup<QMASK, 32>), g1, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_gv_gateup<QMASK, 16>), g1, dim3(256), 0, s, a);
-    if (s2 == 64)
-        hipLaunchKernelGGL((k_gv_down<QMASK, 64>), g2, dim3(256), 0, s, a);
-    else if (s2 == 32)
-        hipLaunchKernelGGL((k_gv_down<QMASK, 32>), g2, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_gv_down<QMASK, 16>), g2, dim3(256), 0, s, a);
+    // strips of S values per lane: S = 64 for dimensions >= 1024 (then H/1024 or I/1024 strips)
+#define RL_GV1(S, M) hipLaunchKernelGGL((k_gv_gateup<QMASK, S, M>), g1, dim3(256), 0, s, a)
+    if (a.H >= 1024) {
+        if (a.H <= 1024)
+            RL_GV1(64, 1);
+        else if (a.H <= 2048)
+            RL_GV1(64, 2);
+        else if (a.H <= 4096)
+            RL_GV1(64, 4);
+        else
+            RL_GV1(64, 8);
+    } else if (a.H == 512) {
+        RL_GV1(32, 1);
+    } else {
+        RL_GV1(16, 1);
+    }
+#undef RL_GV1
+#define RL_GV2(S, M) hipLaunchKernelGGL((k_gv_down<QMASK, S, M>), g2, dim3(256), 0, s, a)
+    if (a.I >= 1024) {
+        if (a.I <= 1024)
+            RL_GV2(64, 1);
+        else if (a.I <= 2048)
+            RL_GV2(64, 2);
+        else
+            RL_GV2(64, 4);
+    } else if (a.I == 512) {
+        RL_GV2(32, 1);
+    } else {
+        RL_GV2(16, 1);
+    }
+#undef RL_GV2
 }
 
 // grouping + gate/up for every present type; returns the layout used
