@@ -158,6 +158,36 @@ def main():
     ms_warm = e0.elapsed_time(e1) / args.steps
 
     gpu_out = out.cpu().numpy().astype(np.float64)
+
+    # the 1-2 row path (decode and 2-row verify) on the same experts: each step its own seeded
+    # routing and x, weight sets rotating as above; weight bytes = distinct experts x 3 matrices
+    from workload.gen import _routing, gen_x
+
+    dec = {}
+    nd = 100
+    for R in (1, 2):
+        xs_d, ids_d, w_d, uniq = [], [], [], []
+        for s in range(nd):
+            i_np, w_np = _routing(R, E, k, args.seed + 100 + s)
+            uniq.append(len(set(i_np.ravel().tolist())))
+            ids_d.append(torch.from_numpy(i_np).cuda())
+            w_d.append(torch.from_numpy(w_np).cuda())
+            xs_d.append(torch.from_numpy(gen_x(R, H, args.seed + 300 + s).view(np.int16).copy()).cuda())
+        out_d = torch.empty((R, H), dtype=torch.float32, device="cuda")
+        ws_d = rl.alloc_workspace(R, k, dev)
+        for s in range(5):
+            rl.decode(xs_d[s], ids_d[s], w_d[s], sets[s % len(sets)], out=out_d, ws=ws_d)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(nd):
+            rl.decode(xs_d[s], ids_d[s], w_d[s], sets[s % len(sets)], out=out_d, ws=ws_d)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / nd * 1e3
+        wbytes = float(np.mean(uniq)) * 3 * H * I / 256 * 57
+        dec[f"rows_{R}"] = {"us_per_step": round(us, 2), "weight_bytes": round(wbytes), "GB_s": round(wbytes / us / 1e3, 1),
+                            "pct_hbm_peak": round(100 * wbytes / us / 1e3 / PEAK_HBM_GBS, 2)}
+    log("[bench] 1-2 row path: " + "; ".join(f"{k_}: {v['us_per_step']} us/step, {v['GB_s']} GB/s" for k_, v in dec.items()))
     tflops = flops / (ms_step * 1e-3) / 1e12
     gu_tflops = flops_gateup / (st_ms["gate_up"] * 1e-3) / 1e12
     log(f"[bench] {ms_step * 1e3:.1f} us/layer = {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 "
@@ -185,7 +215,8 @@ def main():
         },
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 3),
         "ms_per_layer_warm": round(ms_warm, 5),
-        "stage_ms": {k: round(v, 5) for k, v in st_ms.items()},
+        "stage_ms": {k_: round(v, 5) for k_, v in st_ms.items()},
+        "decode_path": dec,
         "roofline": {
             "kernel": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU)",
             "bound": "mfma",
