@@ -1491,10 +1491,15 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ ys
 // ---------------------------------------------------------------------------------------
 // 1-2 row path (decode and 2-row verify).  Memory-bound: every weight is read once per row.
 // Types present are a template mask (1: Q2B, 2: T1, 3: both; both tables are then in LDS).
-template <int QMASK>
+// Weights are decoded to exact 16-bit operands (bf16 against x, fp16 against h) and multiplied
+// two at a time by the packed dot products v_dot2_f32_bf16 / v_dot2_f32_f16 (fp32 sums).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int QMASK, bool F16>
 struct GvTables {
-    DecodeTables<QT_Q2B, false> q2b;
-    DecodeTables<QT_T1, false> t1;
+    DecodeTables<QT_Q2B, F16> q2b;
+    DecodeTables<QT_T1, F16> t1;
     __device__ inline void build(int tid, int nthr) {
         if constexpr (QMASK & 1) q2b.build(tid, nthr);
         if constexpr (QMASK & 2) t1.build(tid, nthr);
@@ -1502,21 +1507,28 @@ struct GvTables {
 };
 
 // sum over the S values of one strip (inside one block) of w_i * xs[i], times the block scale;
-// xs is bf16 bits (XS_BF16) or fp32.  Fixed order: i ascending, then the scale.
+// xs is bf16 bits (XS_BF16, weights decoded to bf16) or fp16 bits (weights decoded to fp16).
+// Fixed order: pairs (2i, 2i+1) ascending, then the scale.
 template <int QT, int S, bool XS_BF16>
-__device__ __forceinline__ float strip_dot_raw(const StripRaw<QT, S>& raw, const void* xs,
-                                               const DecodeTables<QT, false>& tb) {
+__device__ __forceinline__ float strip_dot_raw(const StripRaw<QT, S>& raw, const uint16_t* xs,
+                                               const DecodeTables<QT, !XS_BF16>& tb) {
     Strip<QT, S> st;
     st.prepare(raw, tb.tern);
     float part = 0.f;
 #pragma unroll
     for (int f = 0; f < S / 8; ++f) {
         const u32x4 fr = st.frag(f, tb.val);
+        const u32x4 xv = *(const u32x4*)(xs + 8 * f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float wv = __uint_as_float(i & 1 ? (fr[i >> 1] & 0xFFFF0000u) : (fr[i >> 1] << 16));
-            const float xv = XS_BF16 ? bf16_bits_to_f32(((const uint16_t*)xs)[8 * f + i]) : ((const float*)xs)[8 * f + i];
-            part = __fmaf_rn(wv, xv, part);
+        for (int i = 0; i < 4; ++i) {
+            // through scalars: a bit_cast straight from a vector element reads element 0 only
+            // with this compiler
+            const uint32_t fw = fr[i], xw = xv[i];
+            if constexpr (XS_BF16)
+                part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, fw), __builtin_bit_cast(bf16x2, xw), part,
+                                                       false);
+            else
+                part = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, fw), __builtin_bit_cast(f16x2, xw), part, false);
         }
     }
     return part * st.d;
@@ -1526,8 +1538,8 @@ __device__ __forceinline__ float strip_dot_raw(const StripRaw<QT, S>& raw, const
 // the sum over the strips in ascending order.  All the strips' loads are issued before the first
 // is decoded, so a lane waits for memory once.
 template <int QT, int S, int MAXS, bool XS_BF16>
-__device__ __forceinline__ float row_dot_t(const BufSrc& src, int C, int row, int c0, int nst, const void* xs,
-                                           const DecodeTables<QT, false>& tb) {
+__device__ __forceinline__ float row_dot_t(const BufSrc& src, int C, int row, int c0, int nst, const uint16_t* xs,
+                                           const DecodeTables<QT, !XS_BF16>& tb) {
     StripRaw<QT, S> raw[MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
@@ -1539,14 +1551,13 @@ __device__ __forceinline__ float row_dot_t(const BufSrc& src, int C, int row, in
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nst)
-            acc += strip_dot_raw<QT, S, XS_BF16>(
-                raw[s], XS_BF16 ? (const void*)((const uint16_t*)xs + s * S) : (const void*)((const float*)xs + s * S), tb);
+            acc += strip_dot_raw<QT, S, XS_BF16>(raw[s], xs + s * S, tb);
     return acc;
 }
 
 template <int QMASK, int S, int MAXS, bool XS_BF16>
 __device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, uint32_t mat_bytes, int C, int row, int c0,
-                                         int span, const void* xs, const GvTables<QMASK>& tb) {
+                                         int span, const uint16_t* xs, const GvTables<QMASK, !XS_BF16>& tb) {
     const BufSrc src(W, mat_bytes);
     const int nst = span / S;
     if constexpr (QMASK & 2) {
@@ -1562,7 +1573,7 @@ struct GvArgs {
     const float* w;
     const uint8_t* arena;
     const rl_expert_desc* desc;
-    float* hgv;  // [R*k][I] fp32
+    uint16_t* hgv;  // [R*k][I] fp16
     float* out;  // [R][H]
     int32_t* flags;
     int R, k, E, H, I;
@@ -1595,7 +1606,7 @@ __device__ __forceinline__ void gv_load_pairs(const GvArgs& a, GvPair* sp) {
 // per 256-value block when H = 2048), then a fixed xor tree reduces the 16 partial sums.
 template <int QMASK, int S1, int MAXS>
 __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
-    __shared__ GvTables<QMASK> tb;
+    __shared__ GvTables<QMASK, false> tb;
     tb.build(threadIdx.x, 256);
     if (blockIdx.x == 0 && threadIdx.x < FLAGS_WORDS) a.flags[threadIdx.x] = 0;  // k_gv_down sets them
     __syncthreads();
@@ -1619,7 +1630,8 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
         const float other = __shfl_xor(part, 32, 64);  // gate lanes receive the up sum of their feature
-        if (rs < 2 && q == 0) a.hgv[(size_t)pr * a.I + row] = (e >= 0 && e < a.E) ? silu(part) * other : 0.f;
+        if (rs < 2 && q == 0)
+            a.hgv[(size_t)pr * a.I + row] = f32_to_f16_bits((e >= 0 && e < a.E) ? silu(part) * other : 0.f);
     }
 }
 
@@ -1629,7 +1641,7 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
 // rounds are loaded before the first is decoded.
 template <int QMASK, int S2, int MAXS>
 __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
-    __shared__ GvTables<QMASK> tb;
+    __shared__ GvTables<QMASK, true> tb;
     __shared__ GvPair sp[GV_MAX_PAIRS];
     __shared__ float wsh[GV_MAX_PAIRS];
     tb.build(threadIdx.x, 256);
@@ -1679,7 +1691,7 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
             if (j < a.k) {
                 const GvPair p = sp[r * a.k + j];
                 if (p.e >= 0) {
-                    const float* hx = a.hgv + (size_t)(r * a.k + j) * a.I + q * span;
+                    const uint16_t* hx = a.hgv + (size_t)(r * a.k + j) * a.I + q * span;
 #pragma unroll
                     for (int st = 0; st < MAXS; ++st)
                         if (st < nst) {

@@ -471,7 +471,7 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
     a.w = topk_w;
     a.arena = static_cast<const uint8_t*>(experts->arena);
     a.desc = experts->desc;
-    a.hgv = at<float>(workspace, L.hbuf);
+    a.hgv = at<uint16_t>(workspace, L.hbuf);  // [R*k][I] fp16
     a.out = out;
     a.flags = at<int32_t>(workspace, L.flags);
     a.R = T;
