@@ -117,6 +117,8 @@ CASES = {
     "i128_t1": lambda: _medium("t1_2048", 26, T=96, E=16, H=1024, I=128, k=4),
     "i64_q2b": lambda: _medium("q2b_1090", 27, T=80, E=12, H=512, I=64, k=3),
     "i256_mixed_k1": lambda: _medium("mixed_2048", 28, T=130, E=8, H=768, I=256, k=1),
+    # I > 512: h split by its own kernel and down on the streamed-activation kernel
+    "i1024_t1": lambda: _medium("t1_2048", 29, T=64, E=8, H=1024, I=1024, k=3),
 }
 
 
@@ -245,6 +247,35 @@ def test_timed_hook_matches_prefill(rl, cases, name):
     assert torch.equal(out, ref)
     gaps = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
     assert all(g >= 0.0 for g in gaps), gaps
+
+
+@pytest.mark.parametrize("shape", [dict(), dict(T=32, E=4, H=256, I=256, k=2)])
+def test_y_beyond_fp16_flagged(rl, shape):
+    """Down weights whose products exceed the fp16 range of y (every T1 down block: d = 1e4,
+    sub-scales 7, digits +1, so each weight is 7e4) set bit 2 of the status flags and make the
+    output non-finite; the same layer with its own weights leaves the bit clear.  Shapes: the
+    tiny layer (I = 64) and one with I = 256 (the down kernel with activations in LDS)."""
+    import torch
+
+    wl = make_workload("tiny", seed=30, types="t1", **shape)
+    ex = wl.experts
+    x, ids, w, ex_dev = to_device(wl)
+    ws = rl.alloc_workspace(wl.T, wl.k, ex_dev)
+    rl.prefill(x, ids, w, ex_dev, ws=ws)
+    assert rl.status(ws)[0] & 4 == 0
+    arena = ex.arena.copy()
+    nblk = ex.H * ex.I // 256
+    blk = np.concatenate([np.frombuffer(np.float16(1.0e4).tobytes(), np.uint8), np.full(3, 0xFF, np.uint8),
+                          np.full(52, 242, np.uint8)])
+    assert blk.size == BLOCK_BYTES[QTYPE_T1]
+    for e in range(ex.E):
+        off = int(ex.desc["down_off"][e])
+        arena[off:off + nblk * blk.size] = np.tile(blk, nblk)
+    bad = rl.DeviceExperts(arena, ex.desc, ex.E, ex.H, ex.I)
+    out = rl.prefill(x, ids, w, bad, ws=ws)
+    flags = rl.status(ws)
+    assert flags[0] & 4, flags
+    assert not torch.isfinite(out).all()
 
 
 def test_empty_input(rl, cases):
