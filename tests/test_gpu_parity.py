@@ -119,6 +119,10 @@ CASES = {
     "i256_mixed_k1": lambda: _medium("mixed_2048", 28, T=130, E=8, H=768, I=256, k=1),
     # I > 512: h split by its own kernel and down on the streamed-activation kernel
     "i1024_t1": lambda: _medium("t1_2048", 29, T=64, E=8, H=1024, I=1024, k=3),
+    # the largest k and E: many experts with no or few pairs
+    "k16_e1024_mixed": lambda: _medium("mixed_2048", 31, T=96, E=1024, H=256, I=256, k=16),
+    # one token
+    "t1_one_token": lambda: _medium("t1_2048", 32, T=1, E=64, H=2048, I=512, k=10),
 }
 
 
