@@ -5,8 +5,8 @@ experts (~1.78 bits/weight), bf16 activations, seeded synthetic inputs (the refe
 measure one layer of a real model file, which is not available here; the synthetic layer has
 the same shapes and ~40 pairs per expert).
 
-A step is one rl_moe_prefill call (grouping, fused dequant + gate/up + SwiGLU, fused dequant +
-down, ordered combine) over the resident inputs.  Weight sets rotate over several arena
+A step is one rl_moe_prefill call (grouping with the split of x, fused dequant + gate/up +
+SwiGLU, split of h, fused dequant + down, ordered combine) over the resident inputs.  Weight sets rotate over several arena
 copies at different addresses so that every step reads its weights from HBM rather than from
 the 256 MB Infinity Cache.  Prints one JSON line.
 """

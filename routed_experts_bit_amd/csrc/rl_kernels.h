@@ -1,13 +1,18 @@
-// HIP kernels of the routed-expert MoE layer for gfx950 (wave64, MFMA 16x16x32).
+// HIP kernels of the routed-expert MoE layer for gfx950 (wave64).
 //
-//   k_group_*    token-expert pairs grouped per expert (stable, deterministic), plus the
-//                per-type expert work lists, longest expert first
-//   k_gateup     fused block decode + gate/up grouped GEMM (bf16 MFMA) + SwiGLU -> h (fp16)
-//   k_down       fused block decode + down grouped GEMM (fp16 MFMA) -> y per pair (fp16)
-//   k_combine    out_t = sum_j w[t][j] * y_{t,j}, j ascending (selection order)
-//   k_gv_gateup  1-2 row matrix-vector gate/up + SwiGLU (fp32 VALU, 16 lanes per row)
-//   k_gv_down    1-2 row matrix-vector down + ordered combine in one dispatch
-//   k_dequant    block decode to fp32 through the same fragment decoder
+//   k_count_split    pair histograms per tile of the grouping, and (other work-groups of the same
+//                    launch) the split of x into hi/lo fp8 rows for the T1 experts
+//   k_group_scatter  stable placement of the pairs by expert, offsets, per-type work lists
+//   k_t1_f8          T1 experts on the fp8 MFMA (16x16x128): gate/up + SwiGLU -> h (fp16); also
+//                    down for I > 512 (streamed split-h activations)
+//   k_split          split of h into hi/lo fp8 rows for the T1 down kernels
+//   k_t1_dn          T1 down for I <= 512, a chunk's split h rows held in LDS -> y (fp16)
+//   k_gateup         Q2B experts: decode + gate/up on bf16 MFMA + SwiGLU
+//   k_down           Q2B experts, and T1 experts with I < 256: decode + down on fp16 MFMA -> y (fp16)
+//   k_combine        out_t = sum_j w[t][j] * y_{t,j}, j ascending (selection order)
+//   k_gv_gateup      1-2 row matrix-vector gate/up + SwiGLU (packed bf16 dot products)
+//   k_gv_down        1-2 row matrix-vector down + ordered combine in one dispatch
+//   k_dequant        block decode to fp32 through the same fragment decoder
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -680,7 +685,6 @@ struct T1F8Args {
     int k;                    // pairs per token (gate/up: token of pair index q is q / k)
     int P;                    // pairs (k_t1_dn: y has a spare row P for padding rows)
 };
-typedef T1F8Args GateUpF8Args;
 
 // Work item of the T1 gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and
 // the same NTI tiles of up (NT = 2*NTI weight strips per lane); an item covers 16*NTI*GU_NW
