@@ -474,4 +474,91 @@ struct T1Dec8 {
     }
 };
 
+// ------------------------------------------------------------------ Q2B strips for the 16-bit MFMA
+// The 16x16x32 bf16/fp16 MFMA contracts 32 k per instruction, 8 per lane group.  A 256-value
+// Q2B block takes two steps of four MFMAs, and lane group g owns the 64 consecutive values
+// 64g .. 64g+63 (code bytes 16g .. 16g+15, sub-scales 4g .. 4g+3): operand j (0..3) of step h
+// holds values 64g + 32h + 8j .. +7 in order, two per dword (the lower value in the low half).
+// The activations use the same order, which for them is plain row order in 16-byte pieces.
+__host__ __device__ constexpr int q2_kmap(int g, int h, int j, int i) { return 64 * g + 32 * h + 8 * j + i; }
+
+// Selector table: entry b (a byte of four 2-bit codes c0..c3, c0 in the low bits) holds the
+// v_perm selectors that pick the 16-bit operands of (c0, c1) [low dword] and (c2, c3) [high
+// dword] from an 8-byte value row in which code c's operand sits at bytes 2c, 2c+1.
+constexpr int QSEL_ENTRIES = 256;
+__host__ __device__ inline uint64_t qsel_entry(int b) {
+    uint64_t v = 0;
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t c = ((uint32_t)b >> (2 * i)) & 3u;
+        v |= (2 * c) << (16 * i);
+        v |= (2 * c + 1) << (16 * i + 8);
+    }
+    return v;
+}
+
+// Value row of sub-scale s (0..15): the 16-bit operands s*(2c - 3), c = 0..3, exact in bf16 and fp16.
+constexpr int Q2ROW_ENTRIES = 16;
+template <bool F16>
+__host__ __device__ inline uint64_t q2row_entry(int s) {
+    uint64_t v = 0;
+    for (int c = 0; c < 4; ++c) v |= (uint64_t)int_to_op16<F16>(s * (2 * c - 3)) << (16 * c);
+    return v;
+}
+
+// Raw bytes of one lane's share of a Q2B block (d, the two scale bytes of its sub-scales, its 16
+// code bytes), cut out of an 80-byte window of dwords that starts at the dword boundary at or
+// below the block start (m = block start % 4); the window holds the whole 74-byte block.
+struct Q2Raw16 {
+    uint32_t h;     // low 16 bits: d
+    uint32_t sc;    // low 16 bits: scale bytes 2+2g and 3+2g
+    uint32_t c[4];  // code bytes 16g .. 16g+15
+    template <class Win>
+    __host__ __device__ inline void load_window(const Win& win, uint32_t m, int g) {
+        h = funnel(win[1], win[0], m);
+        const uint32_t os = m + 2u + 2u * (uint32_t)g, ds = os >> 2, ss = os & 3u;
+        sc = funnel(win[ds + 1], win[ds], ss);
+        const uint32_t o = m + 10u + 16u * (uint32_t)g, d = o >> 2, s = o & 3u;
+        const uint32_t w0 = win[d], w1 = win[d + 1], w2 = win[d + 2], w3 = win[d + 3], w4 = win[d + 4];
+        c[0] = funnel(w1, w0, s);
+        c[1] = funnel(w2, w1, s);
+        c[2] = funnel(w3, w2, s);
+        c[3] = funnel(w4, w3, s);
+    }
+};
+
+// Decoder of one lane's share of a Q2B block: prep() keeps the code bytes and the value rows of
+// the lane's four sub-scales; half(h, p, ...) returns operands 2p and 2p+1 of step h (8 dwords),
+// so that a kernel holds half a step's operands at a time.  d is the block scale of the integer
+// dot products (half the fp16 d, as s*(2c - 3) = 2*s*(c - 1.5)).  A block with d = 0 decodes to
+// zero operands.
+struct Q2Dec16 {
+    uint32_t c[4];
+    uint32_t TL[4], TH[4];  // value row of sub-scale 4g+i: operands of codes 0, 1 | 2, 3
+    float d;
+    __host__ __device__ inline void prep(const Q2Raw16& raw, const uint64_t* q2row, bool live = true) {
+        d = live ? half_bits_to_float(raw.h & 0xFFFFu) * 0.5f : 0.0f;
+        uint32_t sw = raw.sc & 0xFFFFu;  // nibble i: sub-scale 4g+i
+        if (d == 0.0f) sw = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t r = q2row[(sw >> (4 * i)) & 15u];
+            TL[i] = (uint32_t)r;
+            TH[i] = (uint32_t)(r >> 32);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = raw.c[i];
+    }
+    __host__ __device__ inline void half(int h, int p, const uint64_t* qsel, uint32_t b[8]) const {
+        const int sb = 2 * h + p;  // operands 2p, 2p+1 of step h: values 32h + 16p .. +15, one sub-scale
+        const uint32_t w = c[sb];
+        const uint32_t tl = TL[sb], th = TH[sb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t e = qsel[(w >> (8 * i)) & 255u];
+            b[2 * i] = perm2(th, tl, (uint32_t)e);
+            b[2 * i + 1] = perm2(th, tl, (uint32_t)(e >> 32));
+        }
+    }
+};
+
 }  // namespace rl

@@ -5,10 +5,12 @@
 //   k_group_scatter  stable placement of the pairs by expert, offsets, per-type work lists
 //   k_t1_f8          T1 experts on the fp8 MFMA (16x16x128): gate/up + SwiGLU -> h (fp16); also
 //                    down for I > 512 (streamed split-h activations)
+//   k_q2_mm          Q2B experts on the 16-bit MFMA (16x16x32), same structure: gate/up on bf16 x,
+//                    down for I > 512 on fp16 h
 //   k_split          split of h into hi/lo fp8 rows for the T1 down kernels
 //   k_t1_dn          T1 down for I <= 512, a chunk's split h rows held in LDS -> y (fp16)
-//   k_gateup         Q2B experts: decode + gate/up on bf16 MFMA + SwiGLU
-//   k_down           Q2B experts, and T1 experts with I < 256: decode + down on fp16 MFMA -> y (fp16)
+//   k_q2_dn          Q2B down for I <= 512, a chunk's fp16 h rows held in LDS -> y (fp16)
+//   k_down           both types with I < 256: decode + down on fp16 MFMA -> y (fp16)
 //   k_combine        out_t = sum_j w[t][j] * y_{t,j}, j ascending (selection order)
 //   k_gv_gateup      1-2 row matrix-vector gate/up + SwiGLU (packed bf16 dot products)
 //   k_gv_down        1-2 row matrix-vector down + ordered combine in one dispatch
@@ -373,162 +375,9 @@ struct Stager {
     }
 };
 
-struct GateUpArgs {
-    const uint16_t* x;
-    const uint8_t* arena;
-    const rl_expert_desc* desc;
-    const int32_t* offsets;
-    const int32_t* pair_src;
-    const int32_t* worklist;  // this type's list
-    const int32_t* wl_len;    // this type's list length (device)
-    int32_t* counters;        // 8 per-XCD item counters
-    uint16_t* hbuf;           // [P][I] fp16, sorted-pair order
-    int H, I, k, ns;
-};
-
-// K loop of one 64-pair chunk with MT 16-row tiles, NT weight tiles per wave (NTI gate + NTI
-// up), 256-value blocks in two chunks of 4 MFMA steps.
-template <int QT, int NW, int NTI, int MT>
-__device__ __forceinline__ void gateup_chunk(const GateUpArgs& a, const DecodeTables<QT, false>& tab,
-                                             uint16_t (*As)[64 * ChunkShape<4, 64 * NW>::LDA], const BufSrc& srcx,
-                                             const BufSrc& srcg, const BufSrc& srcu, Stager<4, 64 * NW>& sx,
-                                             const uint32_t* roff, int nkb, f32x4 (&acc)[4][2 * NTI],
-                                             RunScale* rs) {
-    constexpr int NT = 2 * NTI;
-    constexpr int BB = Fmt<QT>::BYTES;
-    using CH = ChunkShape<4, 64 * NW>;
-    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
-    StripRaw<QT, 64> raw[NT];
-    Strip<QT, 64> st[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) raw[t].load(t < NTI ? srcg : srcu, roff[t], 64 * g);
-    sx.load(srcx, 0u, tid);
-    __syncthreads();  // the previous chunk's readers are done with As
-    sx.store(As[0], tid);
-    sx.load(srcx, 64u, tid);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            st[t].prepare(raw[t], tab.tern);
-            const float r = rs[t].step(st[t].d);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
-            __builtin_amdgcn_sched_barrier(0);  // one tile's table lookups in flight at a time
-        }
-        if (kb + 1 < nkb) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                raw[t].load(t < NTI ? srcg : srcu, roff[t] + (uint32_t)(kb + 1) * BB, 64 * g);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint16_t* Ab = As[half];
-#pragma unroll
-            for (int f4 = 0; f4 < 4; ++f4) {
-                u32x4 b[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) b[t] = st[t].frag(4 * half + f4, tab.val);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const u32x4 av = *(const u32x4*)&Ab[(mt * 16 + n) * CH::LDA + 32 * g + 8 * f4];
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[mt][t] = mfma_bf16(av, b[t], acc[mt][t]);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight to one step
-            }
-            // chunk c = 2kb + half is done: stage c+1 into the other buffer, fetch c+2
-            const int c = 2 * kb + half;
-            if (c + 1 < 2 * nkb) sx.store(As[half ^ 1], tid);
-            if (c + 2 < 2 * nkb) sx.load(srcx, 2u * (uint32_t)(((c + 2) >> 1) * 256 + ((c + 2) & 1) * 32), tid);
-            __syncthreads();
-        }
-    }
-}
-
-// One work item = one expert x (16*NTI*NW) intermediate columns; wave w owns NTI gate tiles and
-// the NTI up tiles of the same columns, so SwiGLU is elementwise in registers.  For each
-// 64-pair chunk of the expert every weight of the slice is decoded exactly once (straight into
-// MFMA operands) and used for all of the chunk's 16-row pair tiles.  Lane (n, g) of a tile
-// decodes values 64g..64g+63 of each 256-value block of weight row n; the activation operand
-// of step f takes the same k positions (64g + 8f .. +7).  The next block's strips and the next
-// activation chunk are loaded into registers one stage ahead.
-template <int QT, int NW, int NTI>
-__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_gateup(GateUpArgs a) {
-    constexpr int NTHR = 64 * NW;
-    constexpr int NT = 2 * NTI;
-    constexpr int BB = Fmt<QT>::BYTES;
-    using CH = ChunkShape<4, NTHR>;
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * CH::LDA];
-    __shared__ DecodeTables<QT, false> tab;
-    __shared__ int item_sh;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-    tab.build(tid, NTHR);
-    __syncthreads();
-    const int n_ranks = uni(*a.wl_len);
-    const int nkb = a.H >> 8;
-    const uint32_t row_bytes = (uint32_t)nkb * BB;
-    const uint32_t mat_bytes = (uint32_t)a.I * row_bytes;
-    const BufSrc srcx(a.x, 0x7FFFFFF0u);
-    int rank, slice;
-    while (next_item(a.counters, a.ns, n_ranks, &item_sh, rank, slice)) {
-        const int e = uni(a.worklist[rank]);
-        const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
-        const BufSrc srcg(a.arena + uni64(a.desc[e].gate_off), mat_bytes);
-        const BufSrc srcu(a.arena + uni64(a.desc[e].up_off), mat_bytes);
-        const int colw = slice * (16 * NTI * NW) + wave * (16 * NTI);
-        uint32_t roff[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
-
-        for (int mc = 0; mc < ne; mc += 64) {
-            const int rows = min(64, ne - mc);
-            const int mtiles = (rows + 15) >> 4;
-            Stager<4, NTHR> sx;
-#pragma unroll
-            for (int i = 0; i < CH::PER_THREAD; ++i) {
-                const int idx = tid + NTHR * i;
-                const int row = idx / CH::PIECES, pc = idx % CH::PIECES;
-                const int tok = a.pair_src[p0 + mc + (row < rows ? row : 0)] / a.k;
-                sx.off[i] = 2u * ((uint32_t)tok * (uint32_t)a.H + 64u * (pc >> 2) + 8u * (pc & 3));
-            }
-            f32x4 acc[4][NT];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            RunScale rs[NT];
-            switch (mtiles) {
-                case 1: gateup_chunk<QT, NW, NTI, 1>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
-                case 2: gateup_chunk<QT, NW, NTI, 2>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
-                case 3: gateup_chunk<QT, NW, NTI, 3>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
-                default: gateup_chunk<QT, NW, NTI, 4>(a, tab, As, srcx, srcg, srcu, sx, roff, nkb, acc, rs); break;
-            }
-            // SwiGLU: lane holds rows 4g..4g+3 of each 16-row tile, column n
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (mt < mtiles) {
-#pragma unroll
-                    for (int ti = 0; ti < NTI; ++ti)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = mt * 16 + 4 * g + i;
-                            if (r < rows) {
-                                const float gv = acc[mt][ti][i] * rs[ti].dprev;
-                                const float uv = acc[mt][NTI + ti][i] * rs[NTI + ti].dprev;
-                                a.hbuf[(size_t)(p0 + mc + r) * a.I + colw + 16 * ti + n] =
-                                    f32_to_f16_bits(silu_fast(gv) * uv);
-                            }
-                        }
-                }
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------------------
 // T1 gate/up on the fp8 MFMA (16x16x128).  T1 operands s*t (|s*t| <= 7) are exact in fp8
-// e4m3; the decoder (T1Frag8) produces them with one LDS lookup per digit byte and one
+// e4m3; the decoder (T1Dec8) produces them with one LDS lookup per digit byte and one
 // byte-select per four weights.  The bf16 activations become an exact pair hi + lo of fp8
 // values after a per-token power-of-two scaling 2^sigma (max |x| * 2^sigma in [128, 256)):
 // hi = fp8(v), lo = fp8(v - hi) keeps all 8 significant bits of v except for elements below
@@ -666,14 +515,24 @@ __device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
 }
 
-// The two T1 expert GEMMs on the fp8 MFMA.  Gate/up: activations xq (split x, token rows,
-// gathered through the token pair_src[p] / k of each sorted pair p), weights gate and up [I][H], output h (fp16, SwiGLU, sorted-pair
-// rows).  Down: activations h8 (split h, sorted-pair rows), weights down [H][I], output y
-// (fp16, row = original pair index t*k + j).  K is the contracted length, N the output width.
-enum { T1_GATEUP = 0, T1_DOWN = 1 };
-struct T1F8Args {
-    const uint8_t* act;       // [rows][2K] split activations (hi/lo fp8, t1_kmap order)
-    const float* ascale;      // 2^-sigma of each activation row (gate/up: [T] per token; down: [P])
+// 16x16x32 MFMA on 16-bit operands: fp16 (F16) or bf16; b holds the B operand's four dwords.
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, const uint32_t* b, f32x4 c) {
+    const u32x4 bv = {b[0], b[1], b[2], b[3]};
+    return F16 ? mfma_f16(a, bv, c) : mfma_bf16(a, bv, c);
+}
+
+// The expert GEMMs with weight windows and activations staged in LDS, one instance per block
+// type: T1 on the fp8 MFMA (16x16x128; activations split into hi/lo e4m3 rows in t1_kmap order,
+// one 2^-sigma scale per row), Q2B on the 16-bit MFMA (16x16x32; gate/up reads x as bf16 and down
+// reads h as fp16, both as they are, rows in plain order).  Gate/up: activations gathered through
+// the token pair_src[p] / k of each sorted pair p, weights gate and up [I][H], output h (fp16,
+// SwiGLU, sorted-pair rows).  Down: activations in sorted-pair rows, weights down [H][I], output
+// y (fp16, row = original pair index t*k + j).  K is the contracted length, N the output width.
+enum { GU_GATEUP = 0, GU_DOWN = 1 };
+struct GuArgs {
+    const uint8_t* act;       // [rows][2K bytes] activations (see above)
+    const float* ascale;      // T1: 2^-sigma of each activation row (gate/up: [T] per token; down: [P])
     const int32_t* pair_src;  // original pair index t*k + j of each sorted pair
     const uint8_t* arena;
     const ItemRec* items;     // this type's work list, longest first
@@ -683,21 +542,21 @@ struct T1F8Args {
     int32_t* flags;           // status words (flags[0])
     int K, N, ns;
     int k;                    // pairs per token (gate/up: token of pair index q is q / k)
-    int P;                    // pairs (k_t1_dn: y has a spare row P for padding rows)
+    int P;                    // pairs (down: y has a spare row P for padding rows)
 };
 
-// Work item of the T1 gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and
-// the same NTI tiles of up (NT = 2*NTI weight strips per lane); an item covers 16*NTI*GU_NW
-// columns of I for one 64-pair chunk at a time.  All operands reach LDS by direct buffer-to-LDS
-// loads (no registers in flight):
+// Work item of the gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and the
+// same NTI tiles of up (NT = 2*NTI weight strips per lane); an item covers 16*NTI*GU_NW columns
+// of I for one 64-pair chunk at a time.  All operands reach LDS by direct buffer-to-LDS loads
+// (no registers in flight):
 //  - activations: a ring of 2 steps of 16 KB (two separate arrays, so that the compiler can
 //    tell their loads apart), each step loaded one step ahead and shared by the work-group;
 //  - weights: each wave loads the next block of its own rows into its own area, right after it
-//    has read the current block out of it: four consecutive lanes fetch one row's 64-byte
-//    window (a coalesced pattern; the lanes that decode a row are 16 apart, so loading into
-//    registers directly would not coalesce).  A strip's 16 windows are written by four loads
-//    of 16 active lanes (4 rows each) at GU_WQ-byte spacing, which puts the rows that one LDS
-//    read serves in distinct banks (a 64-byte row spacing would put them in four).
+//    has read the current block out of it: WL consecutive lanes fetch one row's window (a
+//    coalesced pattern; the lanes that decode a row are 16 apart, so loading into registers
+//    directly would not coalesce).  A strip's 16 windows are written by four loads of 4*WL
+//    active lanes (4 rows each) at WQ-byte spacing, which puts the rows that one LDS read
+//    serves in distinct banks (a plain window-size spacing would put them in fewer).
 // The waits on the shared ring are counted explicitly (vm_barrier).  Per wave, vector-memory
 // instructions are issued in the fixed order
 //   block kb: wts(kb+1) [4*NT] | step 2kb: act(2kb+1) [GU_DMA] | step 2kb+1: act(2kb+2) [GU_DMA]
@@ -708,11 +567,50 @@ struct T1F8Args {
 // block; those loads have completed by then (the odd step before waits for everything, and
 // the chunk prologue is followed by a full wait).  The compiler's own tracking of
 // buffer-to-LDS loads is not relied on: it can miss them.
-constexpr int GU_STEP = 64 * 256;  // one staged step: 64 rows x [4 groups][hi 32 | lo 32] bytes
+constexpr int GU_STEP = 64 * 256;  // one staged step: 64 rows x 256 bytes (128 values of k)
 constexpr int GU_NW = 4;
 constexpr int GU_DMA = GU_STEP / 1024 / GU_NW;  // 1 KB buffer-to-LDS loads per wave per step
-constexpr int GU_WQ = 4 * 64 + 16;               // bytes per 4-row quarter of a strip's windows
-constexpr int GU_WS = 4 * GU_WQ;                 // bytes per strip
+
+// Weight-window geometry of a block type: WIN bytes per row window (the whole block, from the
+// dword boundary at or below its start), fetched by WL lanes of 16 bytes each; a strip's 16
+// windows sit in four quarters of 4 rows, WQ bytes apart (16 bytes more than 4 windows).
+template <int QT>
+struct WinGeo;
+template <>
+struct WinGeo<QT_T1> {
+    static constexpr int WIN = 64, WL = 4, WQ = 4 * 64 + 16, WS = 4 * WQ;
+};
+template <>
+struct WinGeo<QT_Q2B> {
+    static constexpr int WIN = 80, WL = 5, WQ = 4 * 80 + 16, WS = 4 * WQ;
+};
+// for a fetching lane (< 4*WL): the row of its quarter it serves, and the byte offset of its 16
+// bytes in that row's window
+template <int QT>
+__device__ __forceinline__ uint32_t win_lane_row(int lane) {
+    return QT == QT_T1 ? (uint32_t)((lane >> 2) & 3) : (uint32_t)((lane / 5) & 3);
+}
+template <int QT>
+__device__ __forceinline__ uint32_t win_lane_byte(int lane) {
+    return QT == QT_T1 ? 16u * (uint32_t)(lane & 3) : 16u * (uint32_t)(lane % 5);
+}
+
+// A staged step of an activation row is 256 bytes in 16 pieces of 16 bytes; piece 4g + j
+// (lane group g, operand quarter j) sits at slot (4g + j) ^ (row % 16) of the row (spreading the
+// rows that one LDS read serves over the banks), so the loading lane of slot s fetches piece
+// s ^ (row % 16).  act_piece_off(P) is piece P's byte offset in the row relative to
+// act_step_off(c), the offset of step c:
+//   T1 (split rows, already in t1_kmap order): 256c + 16P;
+//   Q2B (plain 16-bit rows): piece 4g + j of step c holds values 256(c/2) + 64g + 32(c%2) + 8j
+//   .. +7 (q2_kmap), i.e. bytes 512(c/2) + 64(c%2) + 128g + 16j.
+template <int QT>
+__device__ __forceinline__ uint32_t act_piece_off(int P) {
+    return QT == QT_T1 ? 16u * (uint32_t)P : 128u * (uint32_t)(P >> 2) + 16u * (uint32_t)(P & 3);
+}
+template <int QT>
+__device__ __forceinline__ uint32_t act_step_off(int c) {
+    return QT == QT_T1 ? (uint32_t)c * 256u : 512u * (uint32_t)(c >> 1) + 64u * (uint32_t)(c & 1);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -731,11 +629,38 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 struct GuShared {
     uint8_t* ring[2];
-    uint8_t* wts;  // [GU_NW][NT][GU_WS]: per wave and strip, 16 64-byte row windows
-    const uint64_t* tsel;
+    uint8_t* wts;  // [GU_NW][NT][WS]: per wave and strip, 16 row windows
+    const uint64_t* tsel;   // T1 tables
     const uint32_t* tbl8;
     float* rscale;
     int32_t* rdst;
+    const uint64_t* qsel;   // Q2B tables
+    const uint64_t* q2row;
+};
+
+// Decoder tables of a block type in LDS (T1: digit selectors and fp8 scale tables; Q2B: code
+// selectors and the 16-bit value rows, bf16 or fp16 after F16), built by the work-group.
+template <int QT, bool F16>
+struct GuTables {
+    static constexpr int N64 = QT == QT_T1 ? TSEL_ENTRIES : QSEL_ENTRIES + Q2ROW_ENTRIES;
+    __device__ static inline void build(uint64_t* t64, uint32_t* tbl8, int tid, int nthr) {
+        if constexpr (QT == QT_T1) {
+            for (int i = tid; i < TSEL_ENTRIES; i += nthr) t64[i] = tsel_entry(i);
+            if (tid < 8) {  // [e(-s), e(0), e(+s), 0] with the hardware's fp8 encoding; s = 0 -> all zero
+                const float sv = (float)tid;
+                const uint32_t pos = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv, 0.f, 0, false) & 255u;
+                const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
+                tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
+            }
+        } else {
+            for (int i = tid; i < N64; i += nthr)
+                t64[i] = i < QSEL_ENTRIES ? qsel_entry(i) : q2row_entry<F16>(i - QSEL_ENTRIES);
+        }
+    }
+    __device__ static inline GuShared shared(uint8_t* r0, uint8_t* r1, uint8_t* wts, const uint64_t* t64,
+                                             const uint32_t* tbl8, float* rscale, int32_t* rdst) {
+        return GuShared{{r0, r1}, wts, t64, tbl8, rscale, rdst, t64, t64 + QSEL_ENTRIES};
+    }
 };
 
 // Static schedule of one XCD's share of a type's work list: ranks r = xcd (mod 8), each cut
@@ -772,10 +697,92 @@ __device__ __forceinline__ ItemRec load_item(const ItemRec* items, int rank) {
     return r;
 }
 
-template <int NMAT, int NTI, int MT>
+// Decoder of one strip: the T1 byte-strip decoder or the Q2B 16-bit one.
+template <int QT>
+struct StripDec;
+template <>
+struct StripDec<QT_T1> {
+    typedef T1Dec8 type;
+};
+template <>
+struct StripDec<QT_Q2B> {
+    typedef Q2Dec16 type;
+};
+
+// decoder state of one strip from its row window (m = block start % 4)
+template <int QT>
+__device__ __forceinline__ void strip_prep(typename StripDec<QT>::type& dec, const uint32_t* win, uint32_t m, int g,
+                                           const T1Lane8& ln, const GuShared& sh) {
+    if constexpr (QT == QT_T1) {
+        T1Raw8 raw;
+        raw.load_window(win, m, g);
+        dec.prep(raw, ln, sh.tbl8);
+    } else {
+        Q2Raw16 raw;
+        raw.load_window(win, m, g);
+        dec.prep(raw, sh.q2row);
+    }
+}
+
+// The MFMAs of one staged step h for MT row tiles x NT strips (activation step in `ring`, rows
+// of 256 bytes); F16 picks fp16 over bf16 operands on the 16-bit path.
+template <int QT, bool F16, int MT, int NT, int H>
+__device__ __forceinline__ void step_mfma(const typename StripDec<QT>::type* dec, const T1Lane8& ln,
+                                          const GuShared& sh, const uint8_t* ring, int m, int g, f32x4 (&acc)[MT][NT]) {
+    if constexpr (QT == QT_T1) {
+        uint32_t b[NT][8];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            dec[t].step(H, ln, sh.tsel, b[t]);
+            __builtin_amdgcn_sched_barrier(0);  // one strip's lookups in flight at a time
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint8_t* rp = ring + (mt * 16 + m) * 256;
+            uint32_t ahi[8], alo[8];
+            *(u32x4*)&ahi[0] = *(const u32x4*)(rp + (((4 * g + 0) ^ m) << 4));
+            *(u32x4*)&ahi[4] = *(const u32x4*)(rp + (((4 * g + 1) ^ m) << 4));
+            *(u32x4*)&alo[0] = *(const u32x4*)(rp + (((4 * g + 2) ^ m) << 4));
+            *(u32x4*)&alo[4] = *(const u32x4*)(rp + (((4 * g + 3) ^ m) << 4));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
+                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one M tile's activation operands at a time
+        }
+    } else {
+        // two halves of two 16x16x32 MFMAs each (operands 2p, 2p+1: one sub-scale)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            uint32_t b[NT][8];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                dec[t].half(H, p, sh.qsel, b[t]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t* rp = ring + (mt * 16 + m) * 256;
+                const u32x4 a0 = *(const u32x4*)(rp + (((4 * g + 2 * p) ^ m) << 4));
+                const u32x4 a1 = *(const u32x4*)(rp + (((4 * g + 2 * p + 1) ^ m) << 4));
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    acc[mt][t] = mfma16<F16>(a0, &b[t][0], acc[mt][t]);
+                    acc[mt][t] = mfma16<F16>(a1, &b[t][4], acc[mt][t]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+}
+
+template <int QT, int NMAT, int NTI, int MT>
 struct GuChunk {
     static constexpr int NT = NMAT * NTI;
-    static constexpr int BB = Fmt<QT_T1>::BYTES;
+    static constexpr int BB = Fmt<QT>::BYTES;
+    static constexpr bool F16 = NMAT == 1;  // Q2B: down reads fp16 h, gate/up bf16 x
+    typedef WinGeo<QT> G;
 
     const GuShared& sh;
     const BufSrc &srcx, &srcg, &srcu;
@@ -790,14 +797,14 @@ struct GuChunk {
     uint32_t rowb;           // bytes per weight row
     bool pf_next;            // load the next chunk's first windows and activation step
     bool pf_have;            // this chunk's were loaded by the chunk before
-    T1Dec8 dec[NT];
+    typename StripDec<QT>::type dec[NT];
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * GU_WS; }
+    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * G::WS; }
     // window of row r (0..15) of strip t
     __device__ __forceinline__ const uint32_t* win(int t, int r) const {
-        return (const uint32_t*)(wts(t) + GU_WQ * (r >> 2) + 64 * (r & 3));
+        return (const uint32_t*)(wts(t) + G::WQ * (r >> 2) + G::WIN * (r & 3));
     }
 
     // step c of the activations into ring slot `slot`; c = NS: step 0 of the next chunk
@@ -805,22 +812,22 @@ struct GuChunk {
         if (c < NS || pf_next) {
             uint8_t* base = sh.ring[slot] + wave * (GU_DMA * 1024);
             const uint32_t* xo = c < NS ? xoff : xon;
-            const uint32_t so = c < NS ? (uint32_t)c * 256u : 0u;
+            const uint32_t so = c < NS ? act_step_off<QT>(c) : 0u;
 #pragma unroll
             for (int i = 0; i < GU_DMA; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(base + i * 1024), 16, xo[i], so, 0, 0);
         }
     }
-    // the 64-byte windows of block kb (clamped to the last block, so that the number of loads
-    // is fixed) of this wave's rows: in quarter q, lane L < 16 fetches bytes 16*(L%4).. of the
-    // window of row 4q + L/4 (woff[t] holds lane L's offset for q = 0; rows are row_bytes apart)
+    // the windows of block kb (clamped to the last block, so that the number of loads is
+    // fixed) of this wave's rows: in quarter q, lane L < 4*WL fetches its 16 bytes of the window
+    // of row 4q + win_lane_row(L) (woff[t] holds lane L's offset for q = 0; rows are row_bytes apart)
     __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo, uint32_t blk) {
-        if ((threadIdx.x & 63) < 16) {
+        if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? sg : su).r, (lds_void*)(wts(t) + GU_WQ * q),
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? sg : su).r, (lds_void*)(wts(t) + G::WQ * q),
                                                              16, (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
         }
     }
@@ -833,9 +840,7 @@ struct GuChunk {
         const uint32_t blk = (uint32_t)kb * BB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            T1Raw8 raw;
-            raw.load_window(win(t, m), (roff[t] + blk) & 3u, g);
-            dec[t].prep(raw, ln, sh.tbl8);
+            strip_prep<QT>(dec[t], win(t, m), (roff[t] + blk) & 3u, g, ln, sh);
             const float r = rs[t].step(dec[t].d);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
@@ -857,28 +862,7 @@ struct GuChunk {
         // loads issued here are waited for by the next (odd) step's full wait
         if (c == NS - 2) hook();
         mem_fence_compiler();
-        uint32_t b[NT][8];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            dec[t].step(H, ln, sh.tsel, b[t]);
-            __builtin_amdgcn_sched_barrier(0);  // one strip's lookups in flight at a time
-        }
-        const uint8_t* ring = sh.ring[H];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint8_t* rp = ring + (mt * 16 + m) * 256;
-            uint32_t ahi[8], alo[8];
-            *(u32x4*)&ahi[0] = *(const u32x4*)(rp + (((4 * g + 0) ^ m) << 4));
-            *(u32x4*)&ahi[4] = *(const u32x4*)(rp + (((4 * g + 1) ^ m) << 4));
-            *(u32x4*)&alo[0] = *(const u32x4*)(rp + (((4 * g + 2) ^ m) << 4));
-            *(u32x4*)&alo[4] = *(const u32x4*)(rp + (((4 * g + 3) ^ m) << 4));
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
-                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
-            }
-            __builtin_amdgcn_sched_barrier(0);  // one M tile's activation operands at a time
-        }
+        step_mfma<QT, F16, MT, NT, H>(dec, ln, sh, sh.ring[H], m, g, acc);
         // the step's MFMAs are issued before the next step's barrier (not sunk past it, which
         // would keep two steps' operands live)
 #pragma unroll
@@ -910,17 +894,17 @@ struct GuChunk {
 };
 
 // One 64-pair chunk of a work item: K loop, then the epilogue (gate/up: SwiGLU into h; down:
-// fp32 rows of y).  During the chunk's next-to-last step the hook gathers the next chunk's
-// activation row offsets (xon), this chunk's per-row activation scales (ps) and, for down, the
-// rows' original pair indices (one row per thread of the first wave).
-template <int MODE, int NTI, int MT>
-__device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, const BufSrc& srcx,
+// fp16 rows of y).  During the chunk's next-to-last step the hook gathers the next chunk's
+// activation row offsets (xon), this chunk's per-row activation scales (ps; 1 for Q2B) and, for
+// down, the rows' original pair indices (one row per thread of the first wave).
+template <int QT, int MODE, int NTI, int MT>
+__device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, const BufSrc& srcx,
                                          const BufSrc& srcg, const BufSrc& srcu, const BufSrc& srcg_n,
                                          const BufSrc& srcu_n, const uint32_t* xoff, const uint32_t* roff,
                                          const uint32_t* woff, const uint32_t* woff_n, const T1Lane8& ln, int nkb,
                                          int pc, int rows, int colw, bool has_next, bool pf_have, int pn,
                                          int rows_n, uint32_t* xon) {
-    constexpr int NMAT = MODE == T1_GATEUP ? 2 : 1;
+    constexpr int NMAT = MODE == GU_GATEUP ? 2 : 1;
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     float ps = 0.f;
     int pdst = 0;
@@ -930,26 +914,26 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
             for (int i = 0; i < GU_DMA; ++i) {
                 const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
                 const int pr = pn + (row < rows_n ? row : 0);
-                const int arow = MODE == T1_GATEUP ? a.pair_src[pr] / a.k : pr;
-                xon[i] = (uint32_t)arow * (uint32_t)(2 * a.K) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+                const int arow = MODE == GU_GATEUP ? a.pair_src[pr] / a.k : pr;
+                xon[i] = (uint32_t)arow * (uint32_t)(2 * a.K) + act_piece_off<QT>((lane & 15) ^ (row & 15));
             }
         }
         if (tid < rows) {
-            if constexpr (MODE == T1_GATEUP) {
-                ps = a.ascale[a.pair_src[pc + tid] / a.k];
+            if constexpr (MODE == GU_GATEUP) {
+                ps = QT == QT_T1 ? a.ascale[a.pair_src[pc + tid] / a.k] : 1.0f;
             } else {
-                ps = a.ascale[pc + tid];
+                ps = QT == QT_T1 ? a.ascale[pc + tid] : 1.0f;
                 pdst = a.pair_src[pc + tid];
             }
         }
     };
-    GuChunk<NMAT, NTI, MT> ch{sh,     srcx,    srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, xon, ln, nkb,
-                              2 * nkb, wave,   n,    g,    (uint32_t)nkb * (uint32_t)Fmt<QT_T1>::BYTES,
-                              has_next, pf_have};
+    GuChunk<QT, NMAT, NTI, MT> ch{sh,     srcx,    srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, xon, ln, nkb,
+                                  2 * nkb, wave,   n,    g,    (uint32_t)nkb * (uint32_t)Fmt<QT>::BYTES,
+                                  has_next, pf_have};
     ch.run(hook);
     if (tid < 64) {
         sh.rscale[tid] = ps;
-        if constexpr (MODE == T1_DOWN) sh.rdst[tid] = pdst;
+        if constexpr (MODE == GU_DOWN) sh.rdst[tid] = pdst;
     }
     lds_barrier();
     bool ovf = false;
@@ -961,7 +945,7 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
             const int r = mt * 16 + 4 * g + i;
             if (r < rows) {
                 const float xs = sh.rscale[r];
-                if constexpr (MODE == T1_GATEUP) {
+                if constexpr (MODE == GU_GATEUP) {
 #pragma unroll
                     for (int ti = 0; ti < NTI; ++ti) {
                         const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
@@ -975,42 +959,38 @@ __device__ __forceinline__ void t1_chunk(const T1F8Args& a, const GuShared& sh, 
                 }
             }
         }
-    if constexpr (MODE == T1_DOWN) y_range_flag(ovf, a.flags);
+    if constexpr (MODE == GU_DOWN) y_range_flag(ovf, a.flags);
     // rscale and rdst are rewritten only after the next chunk's step barriers
 }
 
-template <int MODE, int NTI>
-__global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
+// Body of the gate/up kernels (and of the streamed down kernels for I > 512).
+template <int QT, int MODE, int NTI>
+__device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     constexpr int NTHR = 64 * GU_NW;
-    constexpr int NT = (MODE == T1_GATEUP ? 2 : 1) * NTI;
-    constexpr int BB = Fmt<QT_T1>::BYTES;
-    // the selector table sits at the bottom of LDS (largest alignment first), so that its
+    constexpr int NT = (MODE == GU_GATEUP ? 2 : 1) * NTI;
+    constexpr int BB = Fmt<QT>::BYTES;
+    typedef GuTables<QT, MODE == GU_DOWN> Tab;
+    // the decoder tables sit at the bottom of LDS (largest alignment first), so that their
     // constant offsets fit the 16-bit offset of LDS instructions
-    __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
+    __shared__ __attribute__((aligned(32768))) uint64_t t64[Tab::N64];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
     __shared__ int32_t rdst[64];
-    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * GU_WS];
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * WinGeo<QT>::WS];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     const StaticSched sc(uni(*a.wl_len), a.ns);
     if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
-    for (int i = tid; i < TSEL_ENTRIES; i += NTHR) tsel[i] = tsel_entry(i);
-    if (tid < 8) {  // [e(-s), e(0), e(+s), 0] with the hardware's fp8 encoding; s = 0 -> all zero
-        const float sv = (float)tid;
-        const uint32_t pos = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv, 0.f, 0, false) & 255u;
-        const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
-        tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
-    }
-    const GuShared sh{{ring0, ring1}, wts, tsel, tbl8, rscale, rdst};
+    Tab::build(t64, tbl8, tid, NTHR);
+    const GuShared sh = Tab::shared(ring0, ring1, wts, t64, tbl8, rscale, rdst);
     T1Lane8 ln;
     ln.init(g);
     const int nkb = a.K >> 8;
     const uint32_t row_bytes = (uint32_t)nkb * BB;
     const uint32_t mat_bytes = (uint32_t)a.N * row_bytes;
     const BufSrc srcx(a.act, 0x7FFFFFF0u);
-    auto arow = [&](int p) { return MODE == T1_GATEUP ? a.pair_src[p] / a.k : p; };
+    auto arow = [&](int p) { return MODE == GU_GATEUP ? a.pair_src[p] / a.k : p; };
 
     // first chunk: record and activation rows; later chunks are prefetched by their predecessor
     int q = 0, ix = sc.item(0), mc = 0;
@@ -1023,7 +1003,7 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
         for (int i = 0; i < GU_DMA; ++i) {
             const int row = 4 * (wave * GU_DMA + i) + (lane >> 4);
             const int ar = arow(rec.p0 + (row < rows ? row : 0));
-            xoff[i] = (uint32_t)ar * (uint32_t)(2 * a.K) + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+            xoff[i] = (uint32_t)ar * (uint32_t)(2 * a.K) + act_piece_off<QT>((lane & 15) ^ (row & 15));
         }
     }
     __syncthreads();  // tables
@@ -1041,9 +1021,9 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
         }
         const int rows = min(64, rec.ne - mc);
         const int rows_n = has_next ? min(64, recn.ne - mcn) : 1;
-        const BufSrc srcg(a.arena + rec.off[MODE == T1_GATEUP ? 0 : 2], mat_bytes);
+        const BufSrc srcg(a.arena + rec.off[MODE == GU_GATEUP ? 0 : 2], mat_bytes);
         const BufSrc srcu(a.arena + rec.off[1], mat_bytes);
-        const BufSrc srcg_n(a.arena + recn.off[MODE == T1_GATEUP ? 0 : 2], mat_bytes);
+        const BufSrc srcg_n(a.arena + recn.off[MODE == GU_GATEUP ? 0 : 2], mat_bytes);
         const BufSrc srcu_n(a.arena + recn.off[1], mat_bytes);
         const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
         const int colw_n = sc.slice(ixn) * (16 * NTI * GU_NW) + wave * (16 * NTI);
@@ -1051,19 +1031,23 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
-            woff[t] = (uint32_t)(colw + 16 * (t % NTI) + ((lane >> 2) & 3)) * row_bytes + 16u * (uint32_t)(lane & 3);
-            woff_n[t] = (uint32_t)(colw_n + 16 * (t % NTI) + ((lane >> 2) & 3)) * row_bytes + 16u * (uint32_t)(lane & 3);
+            woff[t] = ((uint32_t)(colw + 16 * (t % NTI)) + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
+            woff_n[t] = ((uint32_t)(colw_n + 16 * (t % NTI)) + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
         }
         uint32_t xon[GU_DMA];
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
         const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
+#define RL_GU_CHUNK(MT_)                                                                                               \
+    gu_chunk<QT, MODE, NTI, MT_>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, \
+                                 colw, has_next, pf_have, pn, rows_n, xon)
         switch ((rows + 15) >> 4) {
-            case 1: t1_chunk<MODE, NTI, 1>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
-            case 2: t1_chunk<MODE, NTI, 2>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
-            case 3: t1_chunk<MODE, NTI, 3>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
-            default: t1_chunk<MODE, NTI, 4>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, colw, has_next, pf_have, pn, rows_n, xon); break;
+            case 1: RL_GU_CHUNK(1); break;
+            case 2: RL_GU_CHUNK(2); break;
+            case 3: RL_GU_CHUNK(3); break;
+            default: RL_GU_CHUNK(4); break;
         }
+#undef RL_GU_CHUNK
         if (!has_next) break;
         pf_have = true;
         q = qn;
@@ -1075,23 +1059,35 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(T1F8Args a) {
     }
 }
 
+// T1 experts on the fp8 MFMA: gate/up + SwiGLU (MODE GU_GATEUP), or down for I > 512 (GU_DOWN)
+template <int MODE, int NTI>
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(GuArgs a) {
+    gu_kernel<QT_T1, MODE, NTI>(a);
+}
+// Q2B experts on the 16-bit MFMA: the same two uses
+template <int MODE, int NTI>
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_q2_mm(GuArgs a) {
+    gu_kernel<QT_Q2B, MODE, NTI>(a);
+}
+
 // ---------------------------------------------------------------------------------------
-// T1 down on the fp8 MFMA with the activations held in LDS (K = I <= 512).  A work item is
+// Down with the activations held in LDS (K = I <= 512), both block types.  A work item is
 // (expert, group of columns of H).  For each chunk of up to DN_ROWS of the expert's sorted pairs
-// the work-group stages the chunk's split h rows once for all of K; then every wave sweeps its
+// the work-group stages the chunk's activation rows once for all of K; then every wave sweeps its
 // own columns, 16*DN_NT at a time, without work-group synchronisation: only its own weight
-// windows move (the same windows, decoder and MFMA steps as k_t1_f8).  y rows are fp32 at the
-// pairs' original index; padding rows of a tile go to the spare row P of y.
+// windows move (the same windows, decoders and MFMA steps as the gate/up kernels).  y rows are
+// fp16 at the pairs' original index; padding rows of a tile go to the spare row P of y.
 constexpr int DN_ROWS = 48;
 constexpr int DN_NT = 4;                     // strips of 16 columns per wave per sweep
 constexpr int DN_SW = 16 * DN_NT * GU_NW;    // columns per sweep of the work-group
 constexpr int DN_KMAX = 512;
-constexpr int DN_ACT = DN_ROWS * 256;        // staged bytes per 128-value step (hi/lo fp8)
+constexpr int DN_ACT = DN_ROWS * 256;        // staged bytes per 128-value step
 
-template <int MT>
+template <int QT, int MT>
 struct DnSweep {
     static constexpr int NT = DN_NT;
-    static constexpr int BB = Fmt<QT_T1>::BYTES;
+    static constexpr int BB = Fmt<QT>::BYTES;
+    typedef WinGeo<QT> G;
 
     const GuShared& sh;         // ring[0]: the chunk's activations [K/128 steps][DN_ROWS][256 B]
     const BufSrc &srcw, &srcw_n;  // down matrix of this sweep and of the next one
@@ -1103,21 +1099,21 @@ struct DnSweep {
     uint32_t rowb;
     bool pf_next;               // load the next sweep's first windows during the last block
     bool pf_have;               // this sweep's first windows were loaded by the sweep before
-    T1Dec8 dec[NT];
+    typename StripDec<QT>::type dec[NT];
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * GU_WS; }
+    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * G::WS; }
     __device__ __forceinline__ const uint32_t* win(int t, int r) const {
-        return (const uint32_t*)(wts(t) + GU_WQ * (r >> 2) + 64 * (r & 3));
+        return (const uint32_t*)(wts(t) + G::WQ * (r >> 2) + G::WIN * (r & 3));
     }
     __device__ __forceinline__ void wload_from(const BufSrc& sw, const uint32_t* wo, uint32_t blk) {
-        if ((threadIdx.x & 63) < 16) {
+        if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wts(t) + GU_WQ * q), 16,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wts(t) + G::WQ * q), 16,
                                                              (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
         }
     }
@@ -1127,9 +1123,7 @@ struct DnSweep {
         const uint32_t blk = (uint32_t)kb * BB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            T1Raw8 raw;
-            raw.load_window(win(t, m), (roff[t] + blk) & 3u, g);
-            dec[t].prep(raw, ln, sh.tbl8);
+            strip_prep<QT>(dec[t], win(t, m), (roff[t] + blk) & 3u, g, ln, sh);
             const float r = rs[t].step(dec[t].d);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
@@ -1142,28 +1136,7 @@ struct DnSweep {
     }
     template <int H>
     __device__ __forceinline__ void step(int c) {
-        uint32_t b[NT][8];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            dec[t].step(H, ln, sh.tsel, b[t]);
-            __builtin_amdgcn_sched_barrier(0);  // one strip's lookups in flight at a time
-        }
-        const uint8_t* act = sh.ring[0] + c * DN_ACT;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint8_t* rp = act + (mt * 16 + m) * 256;
-            uint32_t ahi[8], alo[8];
-            *(u32x4*)&ahi[0] = *(const u32x4*)(rp + (((4 * g + 0) ^ m) << 4));
-            *(u32x4*)&ahi[4] = *(const u32x4*)(rp + (((4 * g + 1) ^ m) << 4));
-            *(u32x4*)&alo[0] = *(const u32x4*)(rp + (((4 * g + 2) ^ m) << 4));
-            *(u32x4*)&alo[4] = *(const u32x4*)(rp + (((4 * g + 3) ^ m) << 4));
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
-                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        step_mfma<QT, true, MT, NT, H>(dec, ln, sh, sh.ring[0] + c * DN_ACT, m, g, acc);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -1184,8 +1157,8 @@ struct DnSweep {
 };
 
 // All sweeps of one chunk (MT row tiles) of a work item: columns cbase + s*DN_SW, s < nsw.
-template <int MT>
-__device__ __forceinline__ void dn_chunk(const T1F8Args& a, const GuShared& sh, const BufSrc& srcw,
+template <int QT, int MT>
+__device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, const BufSrc& srcw,
                                          const BufSrc& srcw_next_item, const T1Lane8& ln, int nkb, uint32_t rowb,
                                          int cbase, int nsw, int cbase_next, bool next_item) {
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -1198,11 +1171,11 @@ __device__ __forceinline__ void dn_chunk(const T1F8Args& a, const GuShared& sh, 
 #pragma unroll
         for (int t = 0; t < DN_NT; ++t) {
             roff[t] = (uint32_t)(col0 + 16 * t + n) * rowb;
-            woff[t] = (uint32_t)(col0 + 16 * t + ((lane >> 2) & 3)) * rowb + 16u * (uint32_t)(lane & 3);
-            woff_n[t] = (uint32_t)(col0n + 16 * t + ((lane >> 2) & 3)) * rowb + 16u * (uint32_t)(lane & 3);
+            woff[t] = ((uint32_t)(col0 + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
+            woff_n[t] = ((uint32_t)(col0n + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
         }
-        DnSweep<MT> sw{sh, srcw, last ? srcw_next_item : srcw, roff, woff, woff_n, ln, nkb, wave, n, g, rowb,
-                       !last || next_item, pf_have};
+        DnSweep<QT, MT> sw{sh,  srcw, last ? srcw_next_item : srcw, roff, woff, woff_n, ln, nkb, wave, n, g, rowb,
+                           !last || next_item, pf_have};
         sw.run();
         // y rows of the tile (padding rows to the spare row)
         bool ovf = false;
@@ -1221,26 +1194,23 @@ __device__ __forceinline__ void dn_chunk(const T1F8Args& a, const GuShared& sh, 
     }
 }
 
-__global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
+template <int QT>
+__device__ __forceinline__ void dn_kernel(const GuArgs& a) {
     constexpr int NTHR = 64 * GU_NW;
-    constexpr int BB = Fmt<QT_T1>::BYTES;
-    __shared__ __attribute__((aligned(32768))) uint64_t tsel[TSEL_ENTRIES];
+    constexpr int BB = Fmt<QT>::BYTES;
+    typedef WinGeo<QT> G;
+    typedef GuTables<QT, true> Tab;
+    __shared__ __attribute__((aligned(32768))) uint64_t t64[Tab::N64];
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[DN_ROWS];
     __shared__ int32_t rdst[DN_ROWS];
-    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * DN_NT * GU_WS];
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * DN_NT * G::WS];
     __shared__ __attribute__((aligned(16))) uint8_t actb[(DN_KMAX / 128) * DN_ACT];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, g = lane >> 4;
     const StaticSched sc(uni(*a.wl_len), a.ns);
     if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
-    for (int i = tid; i < TSEL_ENTRIES; i += NTHR) tsel[i] = tsel_entry(i);
-    if (tid < 8) {
-        const float sv = (float)tid;
-        const uint32_t pos = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv, 0.f, 0, false) & 255u;
-        const uint32_t neg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(-sv, 0.f, 0, false) & 255u;
-        tbl8[tid] = tid == 0 ? 0u : (neg | (pos << 16));
-    }
-    const GuShared sh{{actb, actb}, wts, tsel, tbl8, rscale, rdst};
+    Tab::build(t64, tbl8, tid, NTHR);
+    const GuShared sh = Tab::shared(actb, actb, wts, t64, tbl8, rscale, rdst);
     T1Lane8 ln;
     ln.init(g);
     const int nkb = a.K >> 8, NS = 2 * nkb;
@@ -1261,12 +1231,12 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
             const int c = J / 12, rg = J % 12;
             const int row = 4 * rg + (lane >> 4);
             const int pr = pc + (row < rows ? row : 0);
-            const uint32_t off = (uint32_t)pr * (uint32_t)(2 * a.K) + (uint32_t)c * 256u +
-                                 16u * (uint32_t)((lane & 15) ^ (row & 15));
+            const uint32_t off = (uint32_t)pr * (uint32_t)(2 * a.K) + act_step_off<QT>(c) +
+                                 act_piece_off<QT>((lane & 15) ^ (row & 15));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(actb + c * DN_ACT + rg * 1024), 16, off, 0, 0, 0);
         }
         if (tid < DN_ROWS) {
-            rscale[tid] = tid < rows ? a.ascale[pc + tid] : 0.f;
+            rscale[tid] = tid < rows ? (QT == QT_T1 ? a.ascale[pc + tid] : 1.0f) : 0.f;
             rdst[tid] = tid < rows ? a.pair_src[pc + tid] : P;
         }
     };
@@ -1293,13 +1263,14 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
         stage(rec.p0 + mc, rows);
         if (first) {  // the first sweep's windows (later ones are loaded by the sweep before)
             const int col0 = cbase + wave * (16 * DN_NT);
-            if ((lane & 63) < 16) {
+            if ((lane & 63) < 4 * G::WL) {
 #pragma unroll
                 for (int t = 0; t < DN_NT; ++t)
 #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {
-                        const uint32_t wo = (uint32_t)(col0 + 16 * t + ((lane >> 2) & 3)) * rowb + 16u * (uint32_t)(lane & 3);
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wts + (wave * DN_NT + t) * GU_WS + GU_WQ * qq),
+                        const uint32_t wo = ((uint32_t)(col0 + 16 * t) + win_lane_row<QT>(lane)) * rowb +
+                                            win_lane_byte<QT>(lane);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wts + (wave * DN_NT + t) * G::WS + G::WQ * qq),
                                                                  16, (wo + 4u * (uint32_t)qq * rowb) & ~3u, 0, 0, 0);
                     }
             }
@@ -1308,9 +1279,9 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // the chunk's activations and row tables
         switch ((rows + 15) >> 4) {
-            case 1: dn_chunk<1>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
-            case 2: dn_chunk<2>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
-            default: dn_chunk<3>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+            case 1: dn_chunk<QT, 1>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+            case 2: dn_chunk<QT, 2>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+            default: dn_chunk<QT, 3>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
         }
         if (!has_next) break;
         q = qn;
@@ -1319,6 +1290,10 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(T1F8Args a) {
         rec = recn;
     }
 }
+
+// T1 down on the fp8 MFMA, and Q2B down on the fp16 MFMA, for I <= 512
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_dn(GuArgs a) { dn_kernel<QT_T1>(a); }
+__global__ __launch_bounds__(64 * GU_NW, 2) void k_q2_dn(GuArgs a) { dn_kernel<QT_Q2B>(a); }
 
 struct DownArgs {
     const uint16_t* hbuf;  // [P][I] fp16, sorted-pair order

@@ -162,32 +162,40 @@ int grid_cap(int grid, int n_experts, int ns) {
     return grid < items ? grid : items;
 }
 
-// Gate/up: 8 waves x (1 gate + 1 up tile) = 128 intermediate columns per work item when
-// I % 128 == 0, else 4 waves (64 columns).  Down: 8 waves x 2 tiles = 256 output columns.
+// The LDS-window kernels of a block type (T1 on the fp8 MFMA, Q2B on the 16-bit MFMA).
+template <int QT, int MODE, int NTI>
+constexpr auto mm_kernel() {
+    if constexpr (QT == QT_T1)
+        return &k_t1_f8<MODE, NTI>;
+    else
+        return &k_q2_mm<MODE, NTI>;
+}
 template <int QT>
-void launch_gateup_t(const GateUpArgs& a, int n_experts, hipStream_t s) {
-    GateUpArgs b = a;
-    if (a.I % 128 == 0) {
-        b.ns = a.I / 128;
-        const int grid = grid_cap(resident_grid<k_gateup<QT, 8, 1>>(512), n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup<QT, 8, 1>), dim3(grid), dim3(512), 0, s, b);
-    } else {
-        b.ns = a.I / 64;
-        const int grid = grid_cap(resident_grid<k_gateup<QT, 4, 1>>(256), n_experts, b.ns);
-        hipLaunchKernelGGL((k_gateup<QT, 4, 1>), dim3(grid), dim3(256), 0, s, b);
-    }
+constexpr auto dn_kernel_of() {
+    if constexpr (QT == QT_T1)
+        return &k_t1_dn;
+    else
+        return &k_q2_dn;
 }
 
-void launch_gateup_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
-    T1F8Args b = a;
+template <int QT, int MODE, int NTI>
+void launch_mm(const GuArgs& b, int n_experts, hipStream_t s) {
+    constexpr auto K = mm_kernel<QT, MODE, NTI>();
+    const int grid = grid_cap(resident_grid<K>(64 * GU_NW), n_experts, b.ns);
+    hipLaunchKernelGGL(K, dim3(grid), dim3(64 * GU_NW), 0, s, b);
+}
+
+// Gate/up: 4 waves x (2 gate + 2 up tiles) = 128 intermediate columns per work item when
+// I % 128 == 0, else 64 columns (1 + 1 tiles per wave).
+template <int QT>
+void launch_gateup_mm(const GuArgs& a, int n_experts, hipStream_t s) {
+    GuArgs b = a;
     if (a.N % 128 == 0) {
         b.ns = a.N / 128;
-        const int grid = grid_cap(resident_grid<k_t1_f8<T1_GATEUP, 2>>(64 * GU_NW), n_experts, b.ns);
-        hipLaunchKernelGGL((k_t1_f8<T1_GATEUP, 2>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
+        launch_mm<QT, GU_GATEUP, 2>(b, n_experts, s);
     } else {
         b.ns = a.N / 64;
-        const int grid = grid_cap(resident_grid<k_t1_f8<T1_GATEUP, 1>>(64 * GU_NW), n_experts, b.ns);
-        hipLaunchKernelGGL((k_t1_f8<T1_GATEUP, 1>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
+        launch_mm<QT, GU_GATEUP, 1>(b, n_experts, s);
     }
 }
 
@@ -216,9 +224,8 @@ void launch_split(const SplitArgs& a, hipStream_t s) {
 #undef RL_SPLIT
 }
 
-// T1 down on the fp8 MFMA (I a multiple of 256): split h, then 4 waves x 4 tiles = 256 output
-// columns per work item.
-void launch_hsplit(const T1F8Args& a, int P, hipStream_t s) {
+// Split of h into hi/lo fp8 rows for the T1 down kernels.
+void launch_hsplit(const GuArgs& a, int P, hipStream_t s) {
     SplitArgs sa = {};
     sa.src = a.hbuf;
     sa.dst = const_cast<uint8_t*>(a.act);
@@ -227,18 +234,21 @@ void launch_hsplit(const T1F8Args& a, int P, hipStream_t s) {
     sa.scale = const_cast<float*>(a.ascale);
     launch_split<SPLIT_H>(sa, s);
 }
-void launch_down_f8(const T1F8Args& a, int n_experts, hipStream_t s) {
-    T1F8Args b = a;
-    if (a.K <= DN_KMAX) {  // activations held in LDS; items of up to 1024 columns
+// Down on the LDS-window kernels (I a multiple of 256): for I <= 512 the activations are held in
+// LDS, items of up to 1024 columns; else 4 waves x 4 tiles = 256 output columns per item.
+template <int QT>
+void launch_down_mm(const GuArgs& a, int n_experts, hipStream_t s) {
+    GuArgs b = a;
+    if (a.K <= DN_KMAX) {
         const int cw = a.N % 1024 == 0 ? 1024 : (a.N % 512 == 0 ? 512 : 256);
         b.ns = a.N / cw;
-        const int grid = grid_cap(resident_grid<k_t1_dn>(64 * GU_NW), n_experts, b.ns);
-        hipLaunchKernelGGL(k_t1_dn, dim3(grid), dim3(64 * GU_NW), 0, s, b);
+        constexpr auto K = dn_kernel_of<QT>();
+        const int grid = grid_cap(resident_grid<K>(64 * GU_NW), n_experts, b.ns);
+        hipLaunchKernelGGL(K, dim3(grid), dim3(64 * GU_NW), 0, s, b);
         return;
     }
     b.ns = a.N / 256;
-    const int grid = grid_cap(resident_grid<k_t1_f8<T1_DOWN, 4>>(64 * GU_NW), n_experts, b.ns);
-    hipLaunchKernelGGL((k_t1_f8<T1_DOWN, 4>), dim3(grid), dim3(64 * GU_NW), 0, s, b);
+    launch_mm<QT, GU_DOWN, 4>(b, n_experts, s);
 }
 
 template <int QT>
@@ -322,37 +332,28 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
                  at<int32_t>(ws, L.tile_hist), items, s, present[QT_T1] ? &sa : nullptr);
     mark(1);
-    GateUpArgs a;
-    a.x = x;
-    a.arena = static_cast<const uint8_t*>(ex->arena);
-    a.desc = ex->desc;
-    a.offsets = offsets;
-    a.pair_src = pair_src;
-    a.hbuf = hdst;
-    a.H = ex->H;
-    a.I = ex->I;
-    a.k = k;
-    a.ns = 1;
-    if (present[QT_Q2B]) {
-        a.worklist = worklist + (QT_Q2B - 1) * ex->E;
-        a.wl_len = flags + 8 + QT_Q2B;
-        a.counters = flags + counter_set(0, QT_Q2B);
-        launch_gateup_t<QT_Q2B>(a, present[QT_Q2B], s);
+    GuArgs b = {};
+    b.pair_src = pair_src;
+    b.k = k;
+    b.arena = static_cast<const uint8_t*>(ex->arena);
+    b.hbuf = hdst;
+    b.K = ex->H;
+    b.N = ex->I;
+    b.ns = 1;
+    if (present[QT_Q2B]) {  // x as it is (bf16)
+        GuArgs q = b;
+        q.act = reinterpret_cast<const uint8_t*>(x);
+        q.items = items + (QT_Q2B - 1) * ex->E;
+        q.wl_len = flags + 8 + QT_Q2B;
+        launch_gateup_mm<QT_Q2B>(q, present[QT_Q2B], s);
     }
-    if (present[QT_T1]) {
-        T1F8Args b = {};
-        b.act = xq;
-        b.ascale = xscale;
-        b.pair_src = pair_src;
-        b.k = k;
-        b.arena = a.arena;
-        b.items = items + (QT_T1 - 1) * ex->E;
-        b.wl_len = flags + 8 + QT_T1;
-        b.hbuf = hdst;
-        b.K = ex->H;
-        b.N = ex->I;
-        b.ns = 1;
-        launch_gateup_f8(b, present[QT_T1], s);
+    if (present[QT_T1]) {  // the split of x
+        GuArgs q = b;
+        q.act = xq;
+        q.ascale = xscale;
+        q.items = items + (QT_T1 - 1) * ex->E;
+        q.wl_len = flags + 8 + QT_T1;
+        launch_gateup_mm<QT_T1>(q, present[QT_T1], s);
     }
     mark(2);
 }
@@ -397,33 +398,44 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     d.H = experts->H;
     d.I = experts->I;
     d.ns = 1;
-    const bool t1_f8 = present[QT_T1] && experts->I % 256 == 0;
-    T1F8Args b = {};
-    if (t1_f8) {
+    // I a multiple of 256: the LDS-window down kernels (T1 reads h split into hi/lo fp8, Q2B reads
+    // h as it is); I = 64 or 128: k_down
+    const bool mm_dn = experts->I % 256 == 0;
+    GuArgs b = {};
+    b.pair_src = pair_src;
+    b.arena = d.arena;
+    b.hbuf = hbuf;
+    b.yslot = yslot;
+    b.flags = flags;
+    b.K = experts->I;
+    b.N = experts->H;
+    b.P = T * k;
+    if (mm_dn && present[QT_T1]) {
         b.act = at<uint8_t>(workspace, L.h8);
         b.ascale = at<float>(workspace, L.hscale);
-        b.pair_src = pair_src;
-        b.arena = d.arena;
-        b.items = at<ItemRec>(workspace, L.items) + (QT_T1 - 1) * experts->E;
-        b.wl_len = flags + 8 + QT_T1;
-        b.hbuf = hbuf;
-        b.yslot = yslot;
-        b.flags = flags;
-        b.K = experts->I;
-        b.N = experts->H;
-        b.P = T * k;
         launch_hsplit(b, T * k, s);
     }
     mark(3);
     for (int q = QT_Q2B; q <= QT_T1; ++q) {
         if (!present[q]) continue;
+        if (mm_dn) {
+            GuArgs bq = b;
+            bq.items = at<ItemRec>(workspace, L.items) + (q - 1) * experts->E;
+            bq.wl_len = flags + 8 + q;
+            if (q == QT_Q2B) {
+                bq.act = reinterpret_cast<const uint8_t*>(hbuf);
+                bq.ascale = nullptr;
+                launch_down_mm<QT_Q2B>(bq, present[q], s);
+            } else {
+                launch_down_mm<QT_T1>(bq, present[q], s);
+            }
+            continue;
+        }
         d.worklist = worklist + (q - 1) * experts->E;
         d.wl_len = flags + 8 + q;
         d.counters = flags + counter_set(1, q);
         if (q == QT_Q2B)
             launch_down_t<QT_Q2B>(d, present[q], s);
-        else if (t1_f8)
-            launch_down_f8(b, present[q], s);
         else
             launch_down_t<QT_T1>(d, present[q], s);
     }

@@ -90,6 +90,46 @@ extern "C" int hd_t1f8(const uint8_t* blocks, int64_t nblocks, float* out) {
     return 0;
 }
 
+// 16-bit operands of the Q2B strips of the 16-bit MFMA path for every lane group, mapped back to
+// block positions through q2_kmap and scaled by d.
+extern "C" int hd_q2w(const uint8_t* blocks, int64_t nblocks, int f16, float* out) {
+    const uint8_t* base4 = (const uint8_t*)((uintptr_t)blocks & ~(uintptr_t)3);
+    const PtrSrc src4{base4};
+    std::vector<uint64_t> qsel(QSEL_ENTRIES);
+    for (int i = 0; i < QSEL_ENTRIES; ++i) qsel[i] = qsel_entry(i);
+    uint64_t q2row[Q2ROW_ENTRIES];
+    for (int i = 0; i < Q2ROW_ENTRIES; ++i) q2row[i] = f16 ? q2row_entry<true>(i) : q2row_entry<false>(i);
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const uint32_t blk = (uint32_t)(b * Fmt<QT_Q2B>::BYTES) + (uint32_t)(blocks - base4);
+        uint32_t win[20];  // 80-byte window from the dword boundary at or below the block start
+        for (int i = 0; i < 20; ++i) win[i] = src4.dw((blk & ~3u) + 4u * (uint32_t)i);
+        for (int g = 0; g < 4; ++g) {
+            Q2Raw16 raw;
+            raw.load_window(win, blk & 3u, g);
+            Q2Dec16 dec;
+            dec.prep(raw, q2row);
+            for (int h = 0; h < 2; ++h)
+                for (int p = 0; p < 2; ++p) {
+                    uint32_t op[8];
+                    dec.half(h, p, qsel.data(), op);
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = 2 * p + e / 8, i = e % 8;
+                        const uint32_t bits = (op[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        float v;
+                        if (f16) {
+                            v = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+                        } else {
+                            const uint32_t u = bits << 16;
+                            memcpy(&v, &u, 4);
+                        }
+                        out[b * 256 + q2_kmap(g, h, j, i)] = dec.d * v;
+                    }
+                }
+        }
+    }
+    return 0;
+}
+
 extern "C" int hd_decode(int qtype, int f16, int strip, const uint8_t* blocks, int64_t nblocks, float* out) {
 #define RL_CASE(Q, F, S) \
     if (qtype == Q && f16 == F && strip == S) { run<Q, F, S>(blocks, nblocks, out); return 0; }

@@ -27,6 +27,8 @@ def harness(tmp_path_factory):
     L.hd_decode.restype = C.c_int
     L.hd_t1f8.argtypes = [C.c_void_p, C.c_int64, C.c_void_p]
     L.hd_t1f8.restype = C.c_int
+    L.hd_q2w.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p]
+    L.hd_q2w.restype = C.c_int
     return L
 
 
@@ -82,5 +84,25 @@ def test_t1_fp8_byte_strips(orc, harness, mis):
     out = np.full(nb * 256, np.nan, np.float32)
     assert harness.hd_t1f8(buf.ctypes.data + mis, nb, out.ctypes.data) == 0
     ref = orc.dequant(QTYPE_T1, blk, nb * 256)
+    assert not np.isnan(out).any()
+    assert np.array_equal(out.astype(np.float64), ref), np.nonzero(out != ref)[0][:10]
+
+
+@pytest.mark.parametrize("f16", [0, 1])
+@pytest.mark.parametrize("mis", [0, 1, 2, 3])
+def test_q2b_16bit_strips(orc, harness, f16, mis):
+    """The bf16 / fp16 operands of the Q2B path on the 16-bit MFMA: every block position is
+    covered exactly once through q2_kmap, with the right code and sub-scale, at every block
+    misalignment (a 4-aligned matrix only has 0 and 2); zero-scale blocks decode to zero."""
+    blk, nb = _blocks(QTYPE_Q2B, 40, seed=78 + f16)
+    blk = blk.reshape(nb, BLOCK_BYTES[QTYPE_Q2B]).copy()
+    blk[7, 0:2] = 0  # d = 0 (fp16 +0) with non-zero codes and sub-scales
+    blk[8, 0:2] = [0x00, 0x80]  # d = -0
+    blk = blk.ravel()
+    buf = np.zeros(blk.size + 32, np.uint8)
+    buf[mis: mis + blk.size] = blk
+    out = np.full(nb * 256, np.nan, np.float32)
+    assert harness.hd_q2w(buf.ctypes.data + mis, nb, f16, out.ctypes.data) == 0
+    ref = orc.dequant(QTYPE_Q2B, blk, nb * 256)
     assert not np.isnan(out).any()
     assert np.array_equal(out.astype(np.float64), ref), np.nonzero(out != ref)[0][:10]

@@ -119,6 +119,7 @@ CASES = {
     "i256_mixed_k1": lambda: _medium("mixed_2048", 28, T=130, E=8, H=768, I=256, k=1),
     # I > 512: h split by its own kernel and down on the streamed-activation kernel
     "i1024_t1": lambda: _medium("t1_2048", 29, T=64, E=8, H=1024, I=1024, k=3),
+    "i1024_q2b": lambda: _medium("q2b_1090", 33, T=64, E=8, H=1024, I=1024, k=3, types="q2b"),
     # the largest k and E: many experts with no or few pairs
     "k16_e1024_mixed": lambda: _medium("mixed_2048", 31, T=96, E=1024, H=256, I=256, k=16),
     # one token
@@ -253,15 +254,17 @@ def test_timed_hook_matches_prefill(rl, cases, name):
     assert all(g >= 0.0 for g in gaps), gaps
 
 
+@pytest.mark.parametrize("types", ["t1", "q2b"])
 @pytest.mark.parametrize("shape", [dict(), dict(T=32, E=4, H=256, I=256, k=2)])
-def test_y_beyond_fp16_flagged(rl, shape):
-    """Down weights whose products exceed the fp16 range of y (every T1 down block: d = 1e4,
-    sub-scales 7, digits +1, so each weight is 7e4) set bit 2 of the status flags and make the
-    output non-finite; the same layer with its own weights leaves the bit clear.  Shapes: the
-    tiny layer (I = 64) and one with I = 256 (the down kernel with activations in LDS)."""
+def test_y_beyond_fp16_flagged(rl, shape, types):
+    """Down weights whose products exceed the fp16 range of y set bit 2 of the status flags and
+    make the output non-finite; the same layer with its own weights leaves the bit clear.  Every
+    down block is replaced: T1 d = 1e4, sub-scales 7, digits +1 (weights 7e4); Q2B d = 1e4,
+    sub-scales 15, codes 3 (weights 2.25e5).  Shapes: the tiny layer (I = 64) and one with I = 256
+    (the down kernels with activations in LDS)."""
     import torch
 
-    wl = make_workload("tiny", seed=30, types="t1", **shape)
+    wl = make_workload("tiny", seed=30, types=types, **shape)
     ex = wl.experts
     x, ids, w, ex_dev = to_device(wl)
     ws = rl.alloc_workspace(wl.T, wl.k, ex_dev)
@@ -269,9 +272,13 @@ def test_y_beyond_fp16_flagged(rl, shape):
     assert rl.status(ws)[0] & 4 == 0
     arena = ex.arena.copy()
     nblk = ex.H * ex.I // 256
-    blk = np.concatenate([np.frombuffer(np.float16(1.0e4).tobytes(), np.uint8), np.full(3, 0xFF, np.uint8),
-                          np.full(52, 242, np.uint8)])
-    assert blk.size == BLOCK_BYTES[QTYPE_T1]
+    d = np.frombuffer(np.float16(1.0e4).tobytes(), np.uint8)
+    if types == "t1":
+        blk = np.concatenate([d, np.full(3, 0xFF, np.uint8), np.full(52, 242, np.uint8)])
+        assert blk.size == BLOCK_BYTES[QTYPE_T1]
+    else:
+        blk = np.concatenate([d, np.full(72, 0xFF, np.uint8)])
+        assert blk.size == BLOCK_BYTES[QTYPE_Q2B]
     for e in range(ex.E):
         off = int(ex.desc["down_off"][e])
         arena[off:off + nblk * blk.size] = np.tile(blk, nblk)
