@@ -573,7 +573,10 @@ constexpr int GU_DMA = GU_STEP / 1024 / GU_NW;  // 1 KB buffer-to-LDS loads per 
 
 // Weight-window geometry of a block type: WIN bytes per row window (the whole block, from the
 // dword boundary at or below its start), fetched by WL lanes of 16 bytes each; a strip's 16
-// windows sit in four quarters of 4 rows, WQ bytes apart (16 bytes more than 4 windows).
+// windows sit in four quarters of 4 rows, WQ bytes apart.  WQ (a multiple of 16) is chosen so
+// that the decoders' reads of the 16 rows of a strip spread over the LDS banks: T1 4 windows + 16
+// bytes (a quarter of the conflicts of a plain 4-window spacing), Q2B 4 windows + 32 bytes (a
+// third fewer than at + 16 bytes).
 template <int QT>
 struct WinGeo;
 template <>
@@ -582,7 +585,7 @@ struct WinGeo<QT_T1> {
 };
 template <>
 struct WinGeo<QT_Q2B> {
-    static constexpr int WIN = 80, WL = 5, WQ = 4 * 80 + 16, WS = 4 * WQ;
+    static constexpr int WIN = 80, WL = 5, WQ = 4 * 80 + 32, WS = 4 * WQ;
 };
 // for a fetching lane (< 4*WL): the row of its quarter it serves, and the byte offset of its 16
 // bytes in that row's window
