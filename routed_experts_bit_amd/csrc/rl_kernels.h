@@ -1447,21 +1447,26 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
     }
 }
 
-// out[t][c] = sum over j = 0..k-1 (ascending) of w[t][j] * y[t*k + j][c]; one work-group per
-// token, four columns per thread (16-byte loads).
+// out[t][c] = sum over j = 0..K-1 (ascending) of w[t][j] * y[t*K + j][c]; one work-group per
+// token, eight columns per thread (16-byte loads of fp16 y), one instance per K (1..16).
+template <int K>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yslot, const float* __restrict__ w,
-                                                 float* __restrict__ out, int k, int H) {
+                                                 float* __restrict__ out, int H) {
     const int t = blockIdx.x;
-    const float* wt = w + (size_t)t * k;
+    const float* wt = w + (size_t)t * K;
     for (int c = 8 * threadIdx.x; c < H; c += 8 * 256) {
+        // the K rows' loads are all in flight before the first product
+        u32x4 y[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) y[j] = *(const u32x4*)(yslot + ((size_t)t * K + j) * H + c);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
             const float wj = wt[j];
-            const u32x4 y = *(const u32x4*)(yslot + ((size_t)t * k + j) * H + c);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __fmaf_rn(wj, half_bits_to_float(y[i] & 0xFFFFu), acc[2 * i]);
-                acc[2 * i + 1] = __fmaf_rn(wj, half_bits_to_float(y[i] >> 16), acc[2 * i + 1]);
+                acc[2 * i] = __fmaf_rn(wj, half_bits_to_float(y[j][i] & 0xFFFFu), acc[2 * i]);
+                acc[2 * i + 1] = __fmaf_rn(wj, half_bits_to_float(y[j][i] >> 16), acc[2 * i + 1]);
             }
         }
         f32x4* o = (f32x4*)(out + (size_t)t * H + c);

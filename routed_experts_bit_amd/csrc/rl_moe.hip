@@ -267,6 +267,22 @@ void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
     }
 }
 
+// ordered combine, one kernel instance per k (1..16)
+template <int K>
+void launch_combine_k(const uint16_t* y, const float* w, float* out, int T, int H, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine<K>, dim3(T), dim3(256), 0, s, y, w, out, H);
+}
+void launch_combine(const uint16_t* y, const float* w, float* out, int T, int k, int H, hipStream_t s) {
+    switch (k) {
+#define RL_CB(K) \
+    case K: launch_combine_k<K>(y, w, out, T, H, s); break;
+        RL_CB(1) RL_CB(2) RL_CB(3) RL_CB(4) RL_CB(5) RL_CB(6) RL_CB(7) RL_CB(8)
+        RL_CB(9) RL_CB(10) RL_CB(11) RL_CB(12) RL_CB(13) RL_CB(14) RL_CB(15) RL_CB(16)
+#undef RL_CB
+        default: break;  // k is checked to be in [1, 16] before any launch
+    }
+}
+
 bool gv_dim_ok(int d) { return d == 256 || d == 512 || (d % 1024 == 0); }
 
 template <int QMASK>
@@ -440,7 +456,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
             launch_down_t<QT_T1>(d, present[q], s);
     }
     mark(4);
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, yslot, topk_w, out, k, experts->H);
+    launch_combine(yslot, topk_w, out, T, k, experts->H, s);
     mark(5);
     return hip_status();
 }
