@@ -160,16 +160,19 @@ def main():
     gpu_out = out.cpu().numpy().astype(np.float64)
 
     # the 1-2 row path (decode and 2-row verify) on the same experts: each step its own seeded
-    # routing and x, weight sets rotating as above; weight bytes = distinct experts x 3 matrices
-    from workload.gen import _routing, gen_x
+    # routing and x, weight sets rotating as above; weight bytes = the distinct experts' 3 matrices
+    from workload.gen import _routing, gen_x, matrix_bytes
+
+    qt = ex0.qtypes
 
     dec = {}
     nd = 100
     for R in (1, 2):
-        xs_d, ids_d, w_d, uniq = [], [], [], []
+        xs_d, ids_d, w_d, wb = [], [], [], []
         for s in range(nd):
             i_np, w_np = _routing(R, E, k, args.seed + 100 + s)
-            uniq.append(len(set(i_np.ravel().tolist())))
+            # weight bytes of the step: each distinct expert's gate, up and down matrices once
+            wb.append(sum(3 * matrix_bytes(I, H, int(qt[e])) for e in set(i_np.ravel().tolist())))
             ids_d.append(torch.from_numpy(i_np).cuda())
             w_d.append(torch.from_numpy(w_np).cuda())
             xs_d.append(torch.from_numpy(gen_x(R, H, args.seed + 300 + s).view(np.int16).copy()).cuda())
@@ -184,7 +187,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / nd * 1e3
-        wbytes = float(np.mean(uniq)) * 3 * H * I / 256 * 57
+        wbytes = float(np.mean(wb))
         dec[f"rows_{R}"] = {"us_per_step": round(us, 2), "weight_bytes": round(wbytes), "GB_s": round(wbytes / us / 1e3, 1),
                             "pct_hbm_peak": round(100 * wbytes / us / 1e3 / PEAK_HBM_GBS, 2)}
     log("[bench] 1-2 row path: " + "; ".join(f"{k_}: {v['us_per_step']} us/step, {v['GB_s']} GB/s" for k_, v in dec.items()))
