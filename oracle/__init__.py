@@ -13,4 +13,5 @@ from .oracle import (  # noqa: F401
     group_pairs,
     moe_prefill,
     moe_workload,
+    route,
 )

@@ -51,6 +51,8 @@ def load():
     lib.orc_moe_prefill.argtypes = [P, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P,
                                     C.c_int]
     lib.orc_moe_prefill.restype = C.c_int
+    lib.orc_route.argtypes = [P, C.c_int, C.c_int, C.c_int, P, P]
+    lib.orc_route.restype = C.c_int
     _lib = lib
     return lib
 
@@ -125,3 +127,16 @@ def moe_workload(wl, tokens=None, want_h=False, threads=None):
     ex = wl.experts
     return moe_prefill(wl.x, wl.ids, wl.w, ex.arena, ex.desc, ex.E, ex.H, ex.I, tokens=tokens, want_h=want_h,
                        threads=threads)
+
+
+def route(logits: np.ndarray, k: int):
+    """Router: (ids int32 [T, k], w float64 [T, k]) from fp32 logits [T, E] (orc_route)."""
+    lib = load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.empty((max(T, 1), k), np.int32)
+    w = np.empty((max(T, 1), k), np.float64)
+    rc = lib.orc_route(_ptr(lg), T, E, int(k), _ptr(ids), _ptr(w))
+    if rc:
+        raise ValueError(f"orc_route failed ({rc})")
+    return ids[:T], w[:T]

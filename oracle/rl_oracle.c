@@ -14,6 +14,8 @@
  *     (the MoE tail sums the expert outputs in the row's selection order).
  * Expert weights are 256-value blocks of the Q2B / T1 formats and are decoded here with
  * scalar loops straight from the format definition.
+ * Also the router, the step before the path: softmax over the experts, the k most probable in
+ * descending order (ties to the lower id), renormalised weights (orc_route).
  *
  * Precision: every floating-point step is IEEE double; the decoded weights d*s*c are exact
  * in double, x is bf16 (exact in double), silu uses the C library exp.
@@ -326,5 +328,58 @@ int orc_moe_prefill(const uint16_t* x, const int32_t* ids, const float* w, const
     }
     free(y);
     free(all);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- router (the step before the path) */
+
+/* Router of one layer (reading of the MoE routing the pages take as given: softmax over the
+ * experts, the k most probable experts in descending order, their probabilities renormalised
+ * to sum to one; Red Lite dev72 "2-row verify" section keeps each row's selection order).
+ *   logits[T][E]   fp32 router logits
+ *   ids[T][k]      column j = the j-th selection: descending probability, ties to the lower id
+ *   w[T][k]        p_{ids[t][j]} / (sum over j' = 0..k-1, in selection order, of p_{ids[t][j']})
+ * with p = softmax(logits[t]) over all E experts, in double: m = max logit,
+ * p_e = exp(l_e - m) / sum_e' exp(l_e' - m) (e' ascending).  p is strictly increasing in the
+ * logit, so "descending probability" is "descending logit": the selection compares the fp32
+ * logits themselves (exact), and equal logits are equal probabilities (ties).
+ * Selection is k passes of a plain scan for the best remaining expert.
+ * Returns 0; -1 on a bad shape (E < 1, k < 1 or k > E); -3 on allocation failure. */
+int orc_route(const float* logits, int T, int E, int k, int32_t* ids, double* w) {
+    if (E < 1 || k < 1 || k > E) return -1;
+    double* p = (double*)malloc((size_t)E * sizeof(double));
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    if (!p || !taken) {
+        free(p);
+        free(taken);
+        return -3;
+    }
+    for (int t = 0; t < T; ++t) {
+        const float* l = logits + (int64_t)t * E;
+        double m = (double)l[0];
+        for (int e = 1; e < E; ++e)
+            if ((double)l[e] > m) m = (double)l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            z += p[e];
+        }
+        for (int e = 0; e < E; ++e) p[e] /= z;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e; /* strict: an equal logit keeps the lower id */
+            }
+            taken[best] = 1;
+            ids[(int64_t)t * k + j] = best;
+        }
+        double s = 0.0;
+        for (int j = 0; j < k; ++j) s += p[ids[(int64_t)t * k + j]];
+        for (int j = 0; j < k; ++j) w[(int64_t)t * k + j] = p[ids[(int64_t)t * k + j]] / s;
+    }
+    free(p);
+    free(taken);
     return 0;
 }

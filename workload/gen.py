@@ -253,6 +253,15 @@ class Workload:
         return self.ids.shape[1]
 
 
+def gen_logits(T: int, E: int, seed: int, bias=None) -> np.ndarray:
+    """Router logits as fp32 [T, E]: N(0,1) (+ a per-expert bias), the inputs of the router row."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    logits = rng.standard_normal((T, E))
+    if bias is not None:
+        logits = logits + bias[None, :]
+    return logits.astype(np.float32)
+
+
 def _routing(T, E, k, seed, bias=None):
     rng = np.random.Generator(np.random.PCG64(seed))
     logits = rng.standard_normal((T, E))
