@@ -136,6 +136,21 @@ int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk
                    const rl_expert_blobs* experts, uint16_t* h_out, int32_t T, int32_t k,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* Router, the step before the layer (the MoE routing that the pages take as given; dev72
+ * "2-row verify" keeps each row's selection order): for every token t, softmax over the E
+ * experts of logits[t], the k most probable experts in descending order, ties to the lower
+ * id, and their probabilities renormalised to sum to one (summed in selection order):
+ *   logits   [dev] float [T][E]
+ *   topk_ids [dev] int32 [T][k], overwritten; column j = the j-th selection
+ *   topk_w   [dev] float [T][k], overwritten; p_j / sum_{j'} p_{j'}
+ * The probability is strictly increasing in the logit, so the selection compares the fp32
+ * logits themselves (decisions exact); the weights are computed in fp32 as
+ * exp(l_j - max) / sum_{j' in selection order} exp(l_j' - max).  Logits are finite.
+ * T >= 0 (T = 0 launches nothing), E in [1, 1024], k in [1, 16] and k <= E (RL_ESHAPE
+ * otherwise); RL_EINVAL if a pointer is NULL with T > 0.  One kernel, asynchronous. */
+int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                 void* stream);
+
 /* Device status flags of the last call that used `workspace` [dev]; the caller must have
  * synchronised the stream.  flags_out [host] int32 [4].  Blocking copy. */
 int rl_moe_status(const void* workspace, int32_t* flags_out);

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     gate_up,
     group_pairs,
     dequant,
+    route,
     status,
     strerror,
 )

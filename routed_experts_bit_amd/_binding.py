@@ -22,6 +22,7 @@ EXPORTS = (
     "rl_moe_group_pairs",
     "rl_moe_dequant",
     "rl_moe_gate_up",
+    "rl_moe_route",
     "rl_moe_status",
     "rl_moe_strerror",
 )
@@ -70,6 +71,8 @@ def lib():
     L.rl_moe_group_pairs.restype = C.c_int
     L.rl_moe_dequant.argtypes = [I32, P, C.c_int64, P, P]
     L.rl_moe_dequant.restype = C.c_int
+    L.rl_moe_route.argtypes = [P, I32, I32, I32, P, P, P]
+    L.rl_moe_route.restype = C.c_int
     L.rl_moe_status.argtypes = [P, P]
     L.rl_moe_status.restype = C.c_int
     L.rl_moe_strerror.argtypes = [C.c_int]
@@ -236,6 +239,18 @@ def dequant(qtype: int, blocks_u8, n_values: int, out=None):
         out = torch.empty(max(n_values, 1), dtype=torch.float32, device=blocks_u8.device)
     _check(lib().rl_moe_dequant(int(qtype), _ptr(blocks_u8), int(n_values), _ptr(out), _stream()), "rl_moe_dequant")
     return out[:n_values]
+
+
+def route(logits, k: int, ids=None, w=None):
+    """Router on the GPU: (topk_ids int32 [T, k], topk_w float32 [T, k]) from fp32 logits [T, E]."""
+    torch = _torch()
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().rl_moe_route(_ptr(logits), T, E, int(k), _ptr(ids), _ptr(w), _stream()), "rl_moe_route")
+    return ids, w
 
 
 def status(ws):

@@ -517,6 +517,16 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
     return hip_status();
 }
 
+int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                 void* stream) {
+    if (T < 0 || E < 1 || E > MAX_E || k < 1 || k > 16 || k > E) return RL_ESHAPE;
+    if (T == 0) return RL_OK;
+    if (!logits || !topk_ids || !topk_w) return RL_EINVAL;
+    hipLaunchKernelGGL(k_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), logits,
+                       T, E, k, topk_ids, topk_w);
+    return hip_status();
+}
+
 int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets, int32_t* pair_src,
                        int32_t* inv, void* workspace, size_t ws_bytes, void* stream) {
     if (T < 0 || k < 1 || k > 16 || E < 1 || E > MAX_E || (int64_t)T * k > (1 << 24)) return RL_ESHAPE;

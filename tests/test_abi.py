@@ -107,3 +107,16 @@ def test_strerror(L):
 
     for code in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(rl.strerror(code), str) and rl.strerror(code)
+
+
+def test_route_codes(L):
+    p = C.c_void_p(0x100)
+    assert L.rl_moe_route(p, 4, 0, 1, p, p, None) == -2      # E < 1
+    assert L.rl_moe_route(p, 4, 1025, 2, p, p, None) == -2   # E > 1024
+    assert L.rl_moe_route(p, 4, 8, 0, p, p, None) == -2      # k < 1
+    assert L.rl_moe_route(p, 4, 64, 17, p, p, None) == -2    # k > 16
+    assert L.rl_moe_route(p, 4, 5, 6, p, p, None) == -2      # k > E
+    assert L.rl_moe_route(p, -1, 8, 2, p, p, None) == -2     # T < 0
+    assert L.rl_moe_route(None, 0, 8, 2, None, None, None) == 0   # T = 0: nothing to do
+    assert L.rl_moe_route(None, 4, 8, 2, p, p, None) == -1
+    assert L.rl_moe_route(p, 4, 8, 2, p, None, None) == -1
