@@ -191,6 +191,44 @@ def main():
         dec[f"rows_{R}"] = {"us_per_step": round(us, 2), "weight_bytes": round(wbytes), "GB_s": round(wbytes / us / 1e3, 1),
                             "pct_hbm_peak": round(100 * wbytes / us / 1e3 / PEAK_HBM_GBS, 2)}
     log("[bench] 1-2 row path: " + "; ".join(f"{k_}: {v['us_per_step']} us/step, {v['GB_s']} GB/s" for k_, v in dec.items()))
+
+    # the router (the step before the layer): fp32 logits [T][E] -> ids and weights [T][k], on
+    # seeded logits of the workload's shape (with its per-expert bias, if any)
+    from workload import gen_logits, zipf_bias
+
+    bias = zipf_bias(E, args.seed + 3) if wl.meta.get("bias") == "zipf" else None
+    lg_np = gen_logits(T, E, args.seed + 2, bias)
+    lg = torch.from_numpy(lg_np).cuda()
+    r_ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    r_w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        rl.route(lg, k, r_ids, r_w)
+    nr = 10 * args.steps
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(nr):
+        rl.route(lg, k, r_ids, r_w)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    r_us = e0.elapsed_time(e1) / nr * 1e3
+    # the same calls replayed from a captured HIP graph: the GPU's own time per call, without
+    # the host's launch pacing (one small kernel per call)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(nr):
+            rl.route(lg, k, r_ids, r_w)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    r_us_g = e0.elapsed_time(e1) / nr * 1e3
+    r_bytes = T * E * 4 + T * k * 8
+    router = {"us_per_call": round(r_us, 2), "us_per_call_graph": round(r_us_g, 2), "bytes": r_bytes,
+              "GB_s_graph": round(r_bytes / r_us_g / 1e3, 1),
+              "pct_hbm_peak_graph": round(100 * r_bytes / r_us_g / 1e3 / PEAK_HBM_GBS, 2)}
+    log(f"[bench] router: {r_us:.2f} us per call, {r_us_g:.2f} us per call from a graph ({router['GB_s_graph']} GB/s)")
     tflops = flops / (ms_step * 1e-3) / 1e12
     gu_tflops = flops_gateup / (st_ms["gate_up"] * 1e-3) / 1e12
     log(f"[bench] {ms_step * 1e3:.1f} us/layer = {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 "
@@ -220,6 +258,7 @@ def main():
         "ms_per_layer_warm": round(ms_warm, 5),
         "stage_ms": {k_: round(v, 5) for k_, v in st_ms.items()},
         "decode_path": dec,
+        "router": router,
         "roofline": {
             "kernel": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU)",
             "bound": "mfma",
@@ -245,6 +284,10 @@ def main():
                                             f"C, float64, {nthr} threads"}
         result["parity_rel_l2_vs_oracle"] = err
         log(f"[bench] oracle {cpu_s:.1f}s on {nthr} threads; GPU vs oracle rel_l2 {err:.3e}")
+        o_ids, o_w = oracle.route(lg_np, k)
+        g_ids, g_w = r_ids.cpu().numpy(), r_w.cpu().numpy()
+        router["ids_match_oracle"] = bool(np.array_equal(g_ids, o_ids))
+        router["max_w_rel_err_vs_oracle"] = float(np.max(np.abs(g_w - o_w) / o_w))
     print(json.dumps(result), flush=True)
 
 

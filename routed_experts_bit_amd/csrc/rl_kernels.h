@@ -1704,64 +1704,6 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// Router: one wave per token.  Lane l holds logits l, l + 64, ... (E <= 1024: at most 16).
-// Selection j takes the largest remaining logit, ties to the lower id: each lane offers its
-// best remaining candidate (ascending ids, so a strict comparison keeps the lower id) and an
-// xor butterfly over (value descending, id ascending) leaves the winner in every lane; the
-// lane that holds it drops it.  Lane j keeps selection j.  Weights: exp(l_j - max) over their
-// sum taken in selection order (every lane adds the same k terms in the same order).
-constexpr int RT_MAXR = MAX_E / 64;
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
-                                               int32_t* __restrict__ ids, float* __restrict__ w) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (t >= T) return;  // uniform over the wave
-    const float* lt = logits + (size_t)t * E;
-    float v[RT_MAXR];
-    uint32_t live = 0;
-#pragma unroll
-    for (int r = 0; r < RT_MAXR; ++r) {
-        const int e = lane + 64 * r;
-        v[r] = e < E ? lt[e] : 0.f;
-        if (e < E) live |= 1u << r;
-    }
-    int my_id = 0;
-    float my_v = 0.f, m = 0.f;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int r = 0; r < RT_MAXR; ++r)
-            if (((live >> r) & 1u) && (bi == 0x7FFFFFFF || v[r] > bv)) {
-                bv = v[r];
-                bi = lane + 64 * r;
-            }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            const float ov = __shfl_xor(bv, d, 64);
-            const int oi = __shfl_xor(bi, d, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
-        if (lane == j) {
-            my_id = bi;
-            my_v = bv;
-        }
-        if (j == 0) m = bv;
-    }
-    const float ex = lane < k ? expf(my_v - m) : 0.f;
-    float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, j, 64);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_id;
-        w[(size_t)t * k + lane] = ex / sum;
-    }
-}
-
 // Four threads per block, each decoding a 64-value strip through the same decoder as the
 // matrix kernels: out = (s*c) * block scale, exact in fp32.
 template <int QT>

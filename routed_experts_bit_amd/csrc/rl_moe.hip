@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "rl_kernels.h"
+#include "rl_route.h"
 #include "rl_moe.h"
 
 namespace {
@@ -522,8 +523,20 @@ int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
     if (T < 0 || E < 1 || E > MAX_E || k < 1 || k > 16 || k > E) return RL_ESHAPE;
     if (T == 0) return RL_OK;
     if (!logits || !topk_ids || !topk_w) return RL_EINVAL;
-    hipLaunchKernelGGL(k_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), logits,
-                       T, E, k, topk_ids, topk_w);
+    const dim3 grid((unsigned)((T + 3) / 4));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+#define RL_RT(NR) hipLaunchKernelGGL(k_route<NR>, grid, dim3(256), 0, s, logits, T, E, k, topk_ids, topk_w)
+    if (E <= 64)
+        RL_RT(1);
+    else if (E <= 128)
+        RL_RT(2);
+    else if (E <= 256)
+        RL_RT(4);
+    else if (E <= 512)
+        RL_RT(8);
+    else
+        RL_RT(16);
+#undef RL_RT
     return hip_status();
 }
 
