@@ -121,33 +121,46 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     __shared__ int32_t scan[MAX_E];
     __shared__ int32_t whist[NW][MAX_E];
     __shared__ int32_t bins[2][NBIN];
+    __shared__ int32_t wsum[NW];
     __shared__ int32_t bad_sh;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tile = blockIdx.x;
     const bool lister = tile == a.ntiles;  // the offsets and work lists; no pairs (n <= 0)
     const int E = a.E;
     const int p0 = tile * GT, n = min(a.P - p0, GT);
+    // the work-list builder's expert descriptors (e = tid + GROUP_NTHR * i), loaded before the
+    // scans so that their latency overlaps them
+    constexpr int EPL = MAX_E / GROUP_NTHR;
+    rl_expert_desc dl[EPL];
+    if (lister && a.desc != nullptr) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = tid + GROUP_NTHR * i;
+            if (e < E) dl[i] = a.desc[e];
+        }
+    }
     if (tid == 0) bad_sh = 0;
     for (int i = tid; i < GT; i += GROUP_NTHR) ids_sh[i] = i < n ? a.ids[p0 + i] : -1;
     {
         // pairs of each expert in earlier tiles and in all tiles; the histogram loads are issued
-        // eight tiles at a time so that their latencies overlap
+        // HB tiles at a time so that their latencies overlap
         constexpr int EPT = MAX_E / GROUP_NTHR;
+        constexpr int HB = 8;
         int b[EPT], t[EPT];
 #pragma unroll
         for (int i = 0; i < EPT; ++i) b[i] = t[i] = 0;
-        for (int tl0 = 0; tl0 < a.ntiles; tl0 += 8) {
-            int c[EPT][8];
+        for (int tl0 = 0; tl0 < a.ntiles; tl0 += HB) {
+            int c[EPT][HB];
 #pragma unroll
             for (int i = 0; i < EPT; ++i) {
                 const int e = tid + GROUP_NTHR * i;
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < HB; ++u)
                     c[i][u] = (e < E && tl0 + u < a.ntiles) ? a.tile_hist[(size_t)(tl0 + u) * E + e] : 0;
             }
 #pragma unroll
             for (int i = 0; i < EPT; ++i)
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < HB; ++u) {
                     b[i] += tl0 + u < tile ? c[i][u] : 0;
                     t[i] += c[i][u];
                 }
@@ -162,18 +175,26 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     }
     for (int i = tid; i < NW * MAX_E; i += GROUP_NTHR) (&whist[0][0])[i] = 0;
     __syncthreads();
-    // inclusive scan of the totals (Hillis-Steele, four elements per thread)
-    for (int off = 1; off < MAX_E; off <<= 1) {
-        int v[MAX_E / GROUP_NTHR];
+    // inclusive scan of the totals: thread tid owns entries 4*tid .. 4*tid+3, a shuffle scan over
+    // the lanes of each wave, then the sums of the waves before (one barrier)
+    {
+        static_assert(MAX_E == 4 * GROUP_NTHR, "four scan entries per thread");
+        const int b = 4 * tid;
+        const int s0 = tot[b], s1 = s0 + tot[b + 1], s2 = s1 + tot[b + 2], s3 = s2 + tot[b + 3];
+        int incl = s3;
 #pragma unroll
-        for (int i = 0; i < MAX_E / GROUP_NTHR; ++i) {
-            const int e = tid + GROUP_NTHR * i;
-            v[i] = e >= off ? scan[e - off] : 0;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
         }
+        if (lane == 63) wsum[wave] = incl;
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < MAX_E / GROUP_NTHR; ++i) scan[tid + GROUP_NTHR * i] += v[i];
-        __syncthreads();
+        int ex = incl - s3;
+        for (int w = 0; w < wave; ++w) ex += wsum[w];
+        scan[b] = ex + s0;
+        scan[b + 1] = ex + s1;
+        scan[b + 2] = ex + s2;
+        scan[b + 3] = ex + s3;
     }
     // wave-local counts of the tile
     const int r_begin = wave * SUB, r_end = min(r_begin + SUB, n);
@@ -230,8 +251,11 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     if (lister && a.desc != nullptr) {
         for (int i = tid; i < 2 * NBIN; i += GROUP_NTHR) (&bins[0][0])[i] = 0;
         __syncthreads();
-        for (int e = tid; e < E; e += GROUP_NTHR) {
-            const int q = a.desc[e].qtype, c = tot[e];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = tid + GROUP_NTHR * i;
+            if (e >= E) continue;
+            const int q = dl[i].qtype, c = tot[e];
             before[e] = -1;  // reused: list bin of e
             if (c == 0) continue;
             if (q != QT_Q2B && q != QT_T1) {
@@ -267,7 +291,10 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             if (l == 63) a.flags[8 + QT_Q2B + q] = incl;
         }
         __syncthreads();
-        for (int e = tid; e < E; e += GROUP_NTHR) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = tid + GROUP_NTHR * i;
+            if (e >= E) continue;
             const int key = before[e];
             if (key < 0) continue;
             const int q0 = key / NBIN, b = key % NBIN;
@@ -276,9 +303,9 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             ItemRec r;
             r.p0 = scan[e] - tot[e];
             r.ne = tot[e];
-            r.off[0] = a.desc[e].gate_off;
-            r.off[1] = a.desc[e].up_off;
-            r.off[2] = a.desc[e].down_off;
+            r.off[0] = dl[i].gate_off;
+            r.off[1] = dl[i].up_off;
+            r.off[2] = dl[i].down_off;
             a.items[pos] = r;
         }
         __syncthreads();
