@@ -170,7 +170,6 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             const int e = tid + GROUP_NTHR * i;
             before[e] = b[i];
             tot[e] = t[i];
-            scan[e] = t[i];
         }
     }
     for (int i = tid; i < NW * MAX_E; i += GROUP_NTHR) (&whist[0][0])[i] = 0;

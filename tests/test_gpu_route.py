@@ -40,7 +40,7 @@ def _run(rl, lg, k):
 @pytest.mark.parametrize(
     "T,E,k,bias",
     [(64, 8, 2, False), (1090, 512, 10, True), (2048, 512, 10, False), (33, 1024, 16, False), (7, 13, 13, False),
-     (5, 1, 1, False), (130, 100, 3, False)],
+     (5, 1, 1, False), (130, 100, 3, False), (50, 200, 7, False), (17, 700, 12, False)],
 )
 def test_route_parity(orc, rl, T, E, k, bias):
     log(f"route parity T={T} E={E} k={k} bias={bias}")
@@ -90,4 +90,31 @@ def test_route_then_layer_matches_oracle_routing(orc, rl):
                           wl.experts.H, wl.experts.I)
     err = rel_l2(out, ref)
     log(f"  routed tiny layer rel_l2 {err:.3e}")
+    assert err <= 2e-3 and rl.status(ws)[0] == 0
+
+
+@pytest.mark.parametrize("k", [5, 7, 9])
+def test_routed_layer_other_k(orc, rl, k):
+    """Router then layer for k values that the other layer tests do not use (one combine
+    instance per k): E = 16 experts, H = 256, I = 64 (Q2B), 80 tokens."""
+    import torch
+
+    from gpu_util import rel_l2
+    from workload import make_experts
+
+    T, E, H, I = 80, 16, 256, 64
+    ex = make_experts(E, H, I, 1, seed=40 + k)
+    from workload import gen_x
+
+    x = gen_x(T, H, seed=50 + k)
+    lg = gen_logits(T, E, seed=60 + k)
+    ids, w = rl.route(torch.from_numpy(lg).cuda(), k)
+    rids, rw = orc.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    dev = rl.DeviceExperts.from_workload(ex)
+    ws = rl.alloc_workspace(T, k, dev)
+    out = rl.prefill(torch.from_numpy(x.view(np.int16).copy()).cuda(), ids, w, dev, ws=ws).cpu().numpy()
+    ref = orc.moe_prefill(x, rids, rw.astype(np.float32), ex.arena, ex.desc, E, H, I)
+    err = rel_l2(out, ref)
+    log(f"  k={k} routed layer rel_l2 {err:.3e}")
     assert err <= 2e-3 and rl.status(ws)[0] == 0
