@@ -103,7 +103,15 @@ def main():
     ids = torch.from_numpy(wl.ids).cuda()
     w = torch.from_numpy(wl.w).cuda()
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    ws = rl.alloc_workspace(T, k, dev)
+    # a layer of T tokens is taken as consecutive calls of at most `chunk` tokens (one call unless
+    # the workload names a chunk size), all on one stream and one workspace
+    chunk = int(wl.meta.get("chunk") or T)
+    spans = [(c0, min(T, c0 + chunk)) for c0 in range(0, T, chunk)]
+    ws = rl.alloc_workspace(min(T, chunk), k, dev)
+
+    def layer(exps):
+        for c0, c1 in spans:
+            rl.prefill(x[c0:c1], ids[c0:c1], w[c0:c1], exps, out=out[c0:c1], ws=ws)
 
     flops = 6.0 * H * I * T * k
     flops_gateup = 4.0 * H * I * T * k
@@ -119,7 +127,7 @@ def main():
 
     # warm-up
     for i in range(args.warmup):
-        rl.prefill(x, ids, w, sets[i % len(sets)], out=out, ws=ws)
+        layer(sets[i % len(sets)])
     torch.cuda.synchronize()
     assert rl.status(ws)[0] == 0
 
@@ -130,29 +138,33 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        rl.prefill(x, ids, w, sets[i % len(sets)], out=out, ws=ws)
+        layer(sets[i % len(sets)])
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
     # same number of steps with events between the kernels (on the stream the kernels run on)
+    # (per chunk; a step's stage time is the sum over its chunks)
     ne = rl.TIMED_EVENTS
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in range(args.steps)]
-    for row in evs:  # torch creates the HIP event on its first record
-        for e in row:
-            e.record(stream)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in spans] for _ in range(args.steps)]
+    for step_evs in evs:  # torch creates the HIP event on its first record
+        for row in step_evs:
+            for e in row:
+                e.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        rl.prefill_timed(x, ids, w, sets[i % len(sets)], out, ws, evs[i])
+        for (c0, c1), row in zip(spans, evs[i]):
+            rl.prefill_timed(x[c0:c1], ids[c0:c1], w[c0:c1], sets[i % len(sets)], out[c0:c1], ws, row)
     torch.cuda.synchronize()
-    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(ne - 1)] for i in range(args.steps)])
+    stage = np.array([[sum(row[j].elapsed_time(row[j + 1]) for row in evs[i]) for j in range(ne - 1)]
+                      for i in range(args.steps)])
     st_ms = dict(zip(STAGES, stage.mean(axis=0)))
 
     # warm (same weights every step) for context
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        rl.prefill(x, ids, w, dev, out=out, ws=ws)
+        layer(dev)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_warm = e0.elapsed_time(e1) / args.steps
@@ -250,7 +262,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{args.config}: {T} tokens x {E} experts x top-{k}, hidden {H}, intermediate {I}, "
-                        f"{'T1' if args.config.startswith('t1') else wl.meta['types']} experts, bf16 activations",
+                        f"{'T1' if args.config.startswith('t1') else wl.meta['types']} experts, bf16 activations"
+                        + (f", as {len(spans)} calls of {chunk} tokens" if len(spans) > 1 else ""),
             "tokens": T, "experts": E, "top_k": k, "hidden": H, "intermediate": I, "pairs": T * k,
             "seed": args.seed, "weight_sets_rotated": len(sets),
         },
@@ -260,7 +273,10 @@ def main():
         "decode_path": dec,
         "router": router,
         "roofline": {
-            "kernel": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU)",
+            "kernel": {"t1": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU)",
+                       "q2b": "k_q2_mm<gate/up> (fused Q2B decode + gate/up grouped GEMM on bf16 MFMA + SwiGLU)",
+                       "mixed": "k_q2_mm<gate/up> + k_t1_f8<gate/up> (both gate/up stage kernels, one per block "
+                                "type)"}[wl.meta["types"]],
             "bound": "mfma",
             "achieved": round(gu_tflops, 3),
             "peak": PEAK_BF16_TFLOPS,

@@ -361,3 +361,33 @@ def test_full_size_sampled_parity(orc, rl, name):
     log(f"  rel_l2={err:.3e}")
     assert err <= TOL
     assert np.all(np.isfinite(out))
+
+
+def test_chunked_layer_bit_identical_to_one_call(orc, rl):
+    """A layer taken as consecutive calls of at most 128 tokens (the 8,192-token workload runs as
+    four 2,048-token calls) gives bit-identical outputs to one call over all its tokens: every
+    output row's arithmetic (its decode, MFMA accumulation, scales, ordered combine) depends only
+    on its own pairs, never on which rows share its tiles.  Mixed block types, a ragged last
+    chunk; also checked against the oracle."""
+    import torch
+
+    from workload import make_workload
+
+    wl = make_workload("tiny", seed=21, T=600, H=512, E=64, I=256, k=6, types="mixed")
+    x, ids, w, dev = to_device(wl)
+    T, H = wl.T, wl.experts.H
+    log(f"chunked layer T={T} H={H} E={wl.experts.E} I={wl.experts.I} k={wl.k} chunks of 128")
+    ws = rl.alloc_workspace(T, wl.k, dev)
+    whole = rl.prefill(x, ids, w, dev, ws=ws).cpu().numpy()
+    assert rl.status(ws)[0] == 0
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws_c = rl.alloc_workspace(128, wl.k, dev)
+    for c0 in range(0, T, 128):
+        c1 = min(T, c0 + 128)
+        rl.prefill(x[c0:c1], ids[c0:c1], w[c0:c1], dev, out=out[c0:c1], ws=ws_c)
+    chunked = out.cpu().numpy()
+    assert rl.status(ws_c)[0] == 0
+    assert np.array_equal(chunked.view(np.uint32), whole.view(np.uint32))
+    err = rel_l2(chunked, orc.moe_workload(wl))
+    log(f"  rel_l2 vs oracle {err:.3e}")
+    assert err <= TOL

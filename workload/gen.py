@@ -276,6 +276,8 @@ CONFIGS = {
     "q2b_1090": dict(T=1090, H=2048, E=512, I=512, k=10, types="q2b", bias="zipf"),
     "t1_2048": dict(T=2048, H=2048, E=512, I=512, k=10, types="t1", bias=None),
     "mixed_2048": dict(T=2048, H=2048, E=512, I=512, k=10, types="mixed", bias=None),
+    # 8,192 tokens taken as four consecutive 2,048-token calls (chunk: tokens per call)
+    "mixed_8192": dict(T=8192, H=2048, E=512, I=512, k=10, types="mixed", bias=None, chunk=2048),
     "decode_t1": dict(T=2, H=2048, E=512, I=512, k=10, types="t1", bias=None),
 }
 
