@@ -178,7 +178,7 @@ def main():
     qt = ex0.qtypes
 
     dec = {}
-    nd = 100
+    nd = 1000  # steps per row count, each with its own seeded routing and x
     for R in (1, 2):
         xs_d, ids_d, w_d, wb = [], [], [], []
         for s in range(nd):
