@@ -86,6 +86,8 @@ size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, in
  *   out      [dev] float [T][H], overwritten
  *   T >= 0 (T = 0 launches nothing), k in [1, 16]
  *   workspace [dev], 256-byte aligned, ws_bytes >= rl_moe_workspace_bytes(T, k, E, H, I).
+ * Alignment (RL_EINVAL otherwise): x and out 16-byte aligned, topk_ids and topk_w 4-byte
+ * aligned, experts->desc 8-byte aligned (rows of any T-row slice of such buffers stay aligned).
  * Launches: pair grouping, one fused dequant + gate/up + SwiGLU kernel per block type
  * present, one dequant + down kernel per type, the ordered combine.  Asynchronous. */
 int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
@@ -147,7 +149,8 @@ int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk
  * logits themselves (decisions exact); the weights are computed in fp32 as
  * exp(l_j - max) / sum_{j' in selection order} exp(l_j' - max).  Logits are finite.
  * T >= 0 (T = 0 launches nothing), E in [1, 1024], k in [1, 16] and k <= E (RL_ESHAPE
- * otherwise); RL_EINVAL if a pointer is NULL with T > 0.  One kernel, asynchronous. */
+ * otherwise); RL_EINVAL if a pointer is NULL or not 4-byte aligned with T > 0.  One kernel,
+ * asynchronous. */
 int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
                  void* stream);
 

@@ -85,6 +85,10 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
     if (!shape_ok(T, k, ex->E, ex->H, ex->I)) return RL_ESHAPE;
     if (T == 0) return RL_OK;
     if (!x || !ids || !w || !out || !ex->arena || !ex->desc || !ex->desc_host) return RL_EINVAL;
+    // the kernels move x and out in 16-byte pieces and ids, w and descriptors in 4- and 8-byte words
+    if (((uintptr_t)x | (uintptr_t)out) & 15) return RL_EINVAL;
+    if (((uintptr_t)ids | (uintptr_t)w) & 3) return RL_EINVAL;
+    if ((uintptr_t)ex->desc & 7) return RL_EINVAL;
     if (!ws || ((uintptr_t)ws % ALIGN)) return RL_EWORKSPACE;
     if (ws_bytes < layout(T, k, ex->E, ex->H, ex->I).total) return RL_EWORKSPACE;
     if ((uintptr_t)ex->arena & 3) return RL_EINVAL;
@@ -523,6 +527,7 @@ int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
     if (T < 0 || E < 1 || E > MAX_E || k < 1 || k > 16 || k > E) return RL_ESHAPE;
     if (T == 0) return RL_OK;
     if (!logits || !topk_ids || !topk_w) return RL_EINVAL;
+    if (((uintptr_t)logits | (uintptr_t)topk_ids | (uintptr_t)topk_w) & 3) return RL_EINVAL;
     const dim3 grid((unsigned)((T + 3) / 4));
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define RL_RT(NR) hipLaunchKernelGGL(k_route<NR>, grid, dim3(256), 0, s, logits, T, E, k, topk_ids, topk_w)

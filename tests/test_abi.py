@@ -66,6 +66,11 @@ def test_validation_codes(L, fn):
     assert _call(L, fn, bad, T=T) == RL_ESHAPE
     assert _call(L, fn, b, T=T, x=0) == RL_EINVAL
     assert _call(L, fn, b, T=T, out=0) == RL_EINVAL
+    # alignment: x and out 16 bytes, ids and w 4 bytes
+    assert _call(L, fn, b, T=T, x=0x108) == RL_EINVAL
+    assert _call(L, fn, b, T=T, out=0x404) == RL_EINVAL
+    assert _call(L, fn, b, T=T, ids=0x202) == RL_EINVAL
+    assert _call(L, fn, b, T=T, w=0x301) == RL_EINVAL
     assert _call(L, fn, b, T=T, ws=0) == RL_EWORKSPACE
     assert _call(L, fn, b, T=T, ws=0x10010) == RL_EWORKSPACE  # not 256-byte aligned
     assert _call(L, fn, b, T=T, ws_bytes=1024) == RL_EWORKSPACE
@@ -120,3 +125,5 @@ def test_route_codes(L):
     assert L.rl_moe_route(None, 0, 8, 2, None, None, None) == 0   # T = 0: nothing to do
     assert L.rl_moe_route(None, 4, 8, 2, p, p, None) == -1
     assert L.rl_moe_route(p, 4, 8, 2, p, None, None) == -1
+    assert L.rl_moe_route(C.c_void_p(0x102), 4, 8, 2, p, p, None) == -1   # logits not 4-byte aligned
+    assert L.rl_moe_route(p, 4, 8, 2, C.c_void_p(0x101), p, None) == -1
