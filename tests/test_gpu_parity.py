@@ -124,6 +124,9 @@ CASES = {
     "k16_e1024_mixed": lambda: _medium("mixed_2048", 31, T=96, E=1024, H=256, I=256, k=16),
     # one token
     "t1_one_token": lambda: _medium("t1_2048", 32, T=1, E=64, H=2048, I=512, k=10),
+    # the largest supported hidden size and expert intermediate size, both block types
+    "max_h_mixed": lambda: _medium("mixed_2048", 34, T=40, E=6, H=8192, I=256, k=2),
+    "max_i_mixed": lambda: _medium("mixed_2048", 35, T=40, E=4, H=256, I=4096, k=2),
 }
 
 
@@ -336,6 +339,23 @@ def test_decode_rows_parity_and_bit_identity(orc, rl, types):
     # the matrix-vector path and the prefill path agree within the same bar
     pre = rl.prefill(x, ids, w, ex)
     assert rel_l2(two.cpu().numpy(), pre.cpu().numpy()) <= TOL
+
+
+@pytest.mark.parametrize("H,I", [(8192, 256), (256, 4096)])
+def test_decode_rows_max_dims(orc, rl, H, I):
+    """The 1-2 row path at the largest hidden and intermediate sizes (mixed block types)."""
+    import torch
+
+    ex_np = make_experts(6, H, I, [QTYPE_Q2B] * 3 + [QTYPE_T1] * 3, seed=42)
+    wl = make_workload("decode_t1", seed=43, T=2, experts=ex_np, E=6, H=H, I=I, k=3)
+    x, ids, w, ex = to_device(wl)
+    log(f"decode max dims H={H} I={I}")
+    two = rl.decode(x, ids, w, ex)
+    one1 = rl.decode(x[1:], ids[1:], w[1:], ex)
+    assert torch.equal(two[1], one1[0])
+    err = rel_l2(two.cpu().numpy(), orc.moe_workload(wl))
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
 
 
 # ----------------------------------------------------------------------------- full size
