@@ -2,6 +2,7 @@
 //
 //   k_count_split    pair histograms per tile of the grouping, and (other work-groups of the same
 //                    launch) the split of x into hi/lo fp8 rows for the T1 experts
+//   k_group_count    the pair histograms alone (layers without T1 experts, the grouping hook)
 //   k_group_scatter  stable placement of the pairs by expert, offsets, per-type work lists
 //   k_t1_f8          T1 experts on the fp8 MFMA (16x16x128): gate/up + SwiGLU -> h (fp16); also
 //                    down for I > 512 (streamed split-h activations)
@@ -15,6 +16,7 @@
 //   k_gv_gateup      1-2 row matrix-vector gate/up + SwiGLU (packed bf16 dot products)
 //   k_gv_down        1-2 row matrix-vector down + ordered combine in one dispatch
 //   k_dequant        block decode to fp32 through the same fragment decoder
+// (The router, the step before the layer, is k_route in rl_route.h.)
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
 // Scheduling of the expert GEMMs.  Work item = (expert rank, column slice); ranks come from the
 // per-type work list, longest expert first.  Work-groups are dispatched round-robin over the 8
 // XCDs, so blockIdx % 8 is the XCD; every XCD owns the ranks r = xcd (mod 8) and hands them out
-// in order through its own counter (zeroed by k_group_count), so all slices of one expert run on the
+// in order through its own counter (zeroed by the grouping's first launch), so all slices of one expert run on the
 // same XCD (its gathered activation rows are read through one L2) and the XCD's work-groups
 // balance themselves.
 // flags[16 + 8*(2*stage + type - 1) + xcd]: per-XCD item counters, one set per stage and type
