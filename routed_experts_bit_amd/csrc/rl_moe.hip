@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "rl_kernels.h"
 #include "rl_route.h"
 #include "rl_moe.h"
@@ -152,14 +154,21 @@ void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_
 // per kernel), a multiple of 8 so that every XCD gets the same number.
 template <auto K>
 int resident_grid(int block) {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, cus = 256, per_cu = 1;
-        if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // per device (the current one), computed once; concurrent first calls compute the same value
+    constexpr int MAXDEV = 64;
+    static std::atomic<int> cached[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>& slot = cached[dev < MAXDEV ? dev : MAXDEV - 1];
+    int grid = slot.load(std::memory_order_relaxed);
+    if (grid == 0) {
+        int cus = 256, per_cu = 1;
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
-        cached = ((cus * per_cu + 7) / 8) * 8;
+        grid = ((cus * per_cu + 7) / 8) * 8;
+        slot.store(grid, std::memory_order_relaxed);
     }
-    return cached;
+    return grid;
 }
 
 int grid_cap(int grid, int n_experts, int ns) {
