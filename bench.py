@@ -85,7 +85,7 @@ def main():
     import torch
 
     import routed_experts_bit_amd as rl
-    from workload import make_workload
+    from workload import make_workload, matrix_bytes
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -114,6 +114,9 @@ def main():
             rl.prefill(x[c0:c1], ids[c0:c1], w[c0:c1], exps, out=out[c0:c1], ws=ws)
 
     flops = 6.0 * H * I * T * k
+    qts = ex0.qtypes
+    touched = np.unique(wl.ids)
+    layer_bytes = int(sum(3 * matrix_bytes(I, H, int(qts[e])) for e in touched) + T * H * 2 + T * k * 8 + T * H * 4)
     flops_gateup = 4.0 * H * I * T * k
     flops_down = 2.0 * H * I * T * k
 
@@ -142,6 +145,17 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-step times (one event pair around each step's calls; each interval also holds one
+    # event's overhead) for the median and the minimum
+    ev_steps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev_steps[i][0].record(stream)
+        layer(sets[i % len(sets)])
+        ev_steps[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a_.elapsed_time(b_) for a_, b_ in ev_steps])
 
     # same number of steps with events between the kernels (on the stream the kernels run on)
     # (per chunk; a step's stage time is the sum over its chunks)
@@ -268,6 +282,12 @@ def main():
             "seed": args.seed, "weight_sets_rotated": len(sets),
         },
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 3),
+        "ms_per_layer_median": round(float(np.median(per_step)), 5),
+        "ms_per_layer_min": round(float(per_step.min()), 5),
+        # algorithmic bytes of the layer: every touched expert's three matrices once, x read,
+        # ids and weights read, out written; at 8 TB/s
+        "layer_bytes": layer_bytes,
+        "pct_hbm_roofline": round(100 * layer_bytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 3),
         "ms_per_layer_warm": round(ms_warm, 5),
         "stage_ms": {k_: round(v, 5) for k_, v in st_ms.items()},
         "decode_path": dec,
