@@ -66,7 +66,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the GPU takes some tens of ms of load to reach its steady clocks)")
     ap.add_argument("--config", default="t1_2048")
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--rotate", type=int, default=3, help="distinct arena copies cycled through")
