@@ -587,14 +587,14 @@ struct GuArgs {
 //    serves in distinct banks (a plain window-size spacing would put them in fewer).
 // The waits on the shared ring are counted explicitly (vm_barrier).  Per wave, vector-memory
 // instructions are issued in the fixed order
-//   block kb: wts(kb+1) [4*NT] | step 2kb: act(2kb+1) [GU_DMA] | step 2kb+1: act(2kb+2) [GU_DMA]
+//   step 2kb: act(2kb+1) [GU_DMA], wts(kb+1) [4*NT] | step 2kb+1: act(2kb+2) [GU_DMA]
 // (prologue: act(0), wts(0); in place of the last block's wts(nkb) and act(NS) a chunk loads the
 // next chunk's wts(0) and act(0), and the next chunk then starts with a full wait only), so when
-// step c waits for act(c) at most 4*NT (c even) or 0 (c odd)
-// later loads may still be in flight.  A wave reads the windows of block kb at the top of the
-// block; those loads have completed by then (the odd step before waits for everything, and
-// the chunk prologue is followed by a full wait).  The compiler's own tracking of
-// buffer-to-LDS loads is not relied on: it can miss them.
+// step c waits for act(c) at most 0 (c even) or 4*NT (c odd) later loads may still be in
+// flight, and no activation wait covers the windows.  A wave reads the windows of block kb at
+// the top of the block, after waiting until at most GU_DMA of its loads (the activation step
+// issued after those windows) are outstanding; the windows thus have two steps to land.  The
+// compiler's own tracking of buffer-to-LDS loads is not relied on: it can miss them.
 constexpr int GU_STEP = 64 * 256;  // one staged step: 64 rows x 256 bytes (128 values of k)
 constexpr int GU_NW = 4;
 constexpr int GU_DMA = GU_STEP / 1024 / GU_NW;  // 1 KB buffer-to-LDS loads per wave per step
@@ -868,6 +868,9 @@ struct GuChunk {
     // top of block kb: decoder state from this wave's windows, block scale into the
     // accumulators; then (its windows read) the next block's windows
     __device__ __forceinline__ void block_top(int kb) {
+        // this block's windows were issued in the step before the last one; only that last
+        // step's activation loads (GU_DMA) were issued after them
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GU_DMA) : "memory");
         const uint32_t blk = (uint32_t)kb * BB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -877,21 +880,26 @@ struct GuChunk {
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // windows read before they are replaced
-        if (kb + 1 < nkb || !pf_next)
-            wload(kb + 1);
-        else
-            wload_from(srcg_n, srcu_n, woff_n, 0u);  // block 0 of the next chunk
     }
-    // step c = 2*kb + H staged in ring slot H
+    // step c = 2*kb + H staged in ring slot H.  Even steps issue the next activation step and
+    // then the next block's windows (so that no activation wait covers the windows, and they have
+    // two steps to land); odd steps issue the next activation step only.
     template <int H, class Hook>
     __device__ __forceinline__ void step(int c, Hook& hook) {
         if (H == 0)
-            vm_barrier<4 * NT>();
-        else
             vm_barrier<0>();
-        act(c + 1, 1 - H);
-        // loads issued here are waited for by the next (odd) step's full wait
+        else
+            vm_barrier<4 * NT>();
+        // the hook's loads complete before the next step's wait
         if (c == NS - 2) hook();
+        act(c + 1, 1 - H);
+        if (H == 0) {
+            const int kb = c >> 1;
+            if (kb + 1 < nkb || !pf_next)
+                wload(kb + 1);
+            else
+                wload_from(srcg_n, srcu_n, woff_n, 0u);  // block 0 of the next chunk
+        }
         mem_fence_compiler();
         step_mfma<QT, F16, MT, NT, H>(dec, ln, sh, sh.ring[H], m, g, acc);
         // the step's MFMAs are issued before the next step's barrier (not sunk past it, which
@@ -1148,9 +1156,15 @@ struct DnSweep {
                                                              (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
         }
     }
-    // windows of block kb: the wave's own loads, so a wait on its own counter suffices
+    // windows of block kb: the wave's own loads, so a wait on its own counter suffices.  At the
+    // first block of a sweep the previous sweep's epilogue has issued exactly 16*MT y stores (and
+    // at most one flag atomic) after this sweep's windows: waiting down to 16*MT outstanding
+    // operations completes the windows without waiting for those stores.
     __device__ __forceinline__ void block_top(int kb) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (kb == 0)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(16 * MT) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const uint32_t blk = (uint32_t)kb * BB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
