@@ -532,15 +532,20 @@ __global__ __launch_bounds__(256) void k_count_split(GroupArgs g, SplitArgs a) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f32x4 c) {
+// sa: this lane's E8M0 scale (2^(sa-127)) for A; B is unscaled.  As measured on gfx950, the
+// scale of row i and 32-value k-block s comes from lane 16s + i, and block s is dwords
+// 4*(s >> 1) .. +3 of lane groups 2*(s & 1) and 2*(s & 1) + 1.  The two halves of lane group g's
+// operand are thus scaled by lane groups g >> 1 and 2 + (g >> 1), which lane groups g and g ^ 1
+// share: lane group L supplies the scale of the k-group pair {2*(L & 1), 2*(L & 1) + 1}.
+__device__ __forceinline__ f32x4 mfma_f8(const uint32_t* a, const uint32_t* b, f32x4 c, int sa) {
     i32x8 av, bv;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         av[i] = (int)a[i];
         bv[i] = (int)b[i];
     }
-    // formats 0/0 = fp8 e4m3 for both operands; unit E8M0 scales (127)
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    // formats 0/0 = fp8 e4m3 for both operands; B's E8M0 scale is 1 (127)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, sa, 0, 127);
 }
 
 // 16x16x32 MFMA on 16-bit operands: fp16 (F16) or bf16; b holds the B operand's four dwords.
@@ -566,6 +571,9 @@ struct GuArgs {
     const ItemRec* items;     // this type's work list, longest first
     const int32_t* wl_len;    // its length (device)
     uint16_t* hbuf;           // gate/up output [P][N] fp16
+    uint8_t* h8;              // T1 gate/up, I <= 512: h written here as hi/lo fp8 rows instead (null: hbuf)
+    uint32_t* hsc;            // with h8, and read by the T1 down kernel: byte 2*kb + p of word r = E8M0
+                              // scale of k-groups 2p, 2p+1 of block kb of h row r
     uint16_t* yslot;          // down output [P+1][N] fp16
     int32_t* flags;           // status words (flags[0])
     int K, N, ns;
@@ -667,6 +675,7 @@ struct GuShared {
     int32_t* rdst;
     const uint64_t* qsel;   // Q2B tables
     const uint64_t* q2row;
+    float* hred;            // T1 gate/up: [GU_NW][64] per-wave row maxima of h
 };
 
 // Decoder tables of a block type in LDS (T1: digit selectors and fp8 scale tables; Q2B: code
@@ -756,10 +765,12 @@ __device__ __forceinline__ void strip_prep(typename StripDec<QT>::type& dec, con
 }
 
 // The MFMAs of one staged step h for MT row tiles x NT strips (activation step in `ring`, rows
-// of 256 bytes); F16 picks fp16 over bf16 operands on the 16-bit path.
+// of 256 bytes); F16 picks fp16 over bf16 operands on the 16-bit path.  T1: sa[mt] is the E8M0
+// scale of the lane's activation values in row tile mt (127 = 1).
 template <int QT, bool F16, int MT, int NT, int H>
 __device__ __forceinline__ void step_mfma(const typename StripDec<QT>::type* dec, const T1Lane8& ln,
-                                          const GuShared& sh, const uint8_t* ring, int m, int g, f32x4 (&acc)[MT][NT]) {
+                                          const GuShared& sh, const uint8_t* ring, int m, int g, f32x4 (&acc)[MT][NT],
+                                          const int (&sa)[MT]) {
     if constexpr (QT == QT_T1) {
         uint32_t b[NT][8];
 #pragma unroll
@@ -777,8 +788,8 @@ __device__ __forceinline__ void step_mfma(const typename StripDec<QT>::type* dec
             *(u32x4*)&alo[4] = *(const u32x4*)(rp + (((4 * g + 3) ^ m) << 4));
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t]);
-                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t]);
+                acc[mt][t] = mfma_f8(ahi, b[t], acc[mt][t], sa[mt]);
+                acc[mt][t] = mfma_f8(alo, b[t], acc[mt][t], sa[mt]);
             }
             __builtin_amdgcn_sched_barrier(0);  // one M tile's activation operands at a time
         }
@@ -808,6 +819,18 @@ __device__ __forceinline__ void step_mfma(const typename StripDec<QT>::type* dec
     }
 }
 
+// Output column order of the T1 gate/up kernel: position q = 256*kb + 64*g + j computes h
+// column 256*kb + t1_kmap(g, j), i.e. block kb of h in the down kernel's k order.  A 128-position
+// work item is then the pair of k-groups {2p, 2p+1} of one block kb (p = (q >> 6) & 2), which is
+// what one A scale of the down kernel's fp8 MFMA covers, so the item can scale each (row, block,
+// pair) by itself.  Tiles of 16 positions are 16 consecutive columns, except that rows 12..15 of
+// the tile at j = 48 are the group's four tail columns.  For I not a multiple of 256 (64, 128:
+// no fp8 down kernel) the order is the identity.
+__device__ __forceinline__ int t1_hcol(int q, int I) {
+    if (I & 255) return q;
+    return 256 * (q >> 8) + t1_kmap((q >> 6) & 3, q & 63);
+}
+
 template <int QT, int NMAT, int NTI, int MT>
 struct GuChunk {
     static constexpr int NT = NMAT * NTI;
@@ -822,6 +845,8 @@ struct GuChunk {
     const uint32_t* roff;    // per lane: byte offset of the row it decodes, per strip
     const uint32_t* woff;    // per lane: byte offset of its 16 bytes of a row window, per strip
     const uint32_t* woff_n;  // the same for the next chunk
+    const uint32_t* wx;      // per strip: bytes added to quarter 3's offset beyond 12 rows (uniform)
+    const uint32_t* wx_n;    // the same for the next chunk
     const uint32_t* xon;     // xoff of the next chunk (written by the hook)
     const T1Lane8& ln;
     int nkb, NS, wave, m, g;
@@ -851,19 +876,22 @@ struct GuChunk {
     }
     // the windows of block kb (clamped to the last block, so that the number of loads is
     // fixed) of this wave's rows: in quarter q, lane L < 4*WL fetches its 16 bytes of the window
-    // of row 4q + win_lane_row(L) (woff[t] holds lane L's offset for q = 0; rows are row_bytes apart)
-    __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo, uint32_t blk) {
+    // of row 4q + win_lane_row(L) (woff[t] holds lane L's offset for q = 0; rows are row_bytes
+    // apart, except that quarter 3 of a strip may start wx[t] bytes further on)
+    __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo,
+                                               const uint32_t* wxx, uint32_t blk) {
         if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds((t < NTI ? sg : su).r, (lds_void*)(wts(t) + G::WQ * q),
-                                                             16, (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        (t < NTI ? sg : su).r, (lds_void*)(wts(t) + G::WQ * q), 16,
+                        (wo[t] + 4u * (uint32_t)q * rowb + (q == 3 ? wxx[t] : 0u) + blk) & ~3u, 0, 0, 0);
         }
     }
     __device__ __forceinline__ void wload(int kb) {
-        wload_from(srcg, srcu, woff, (uint32_t)min(kb, nkb - 1) * BB);
+        wload_from(srcg, srcu, woff, wx, (uint32_t)min(kb, nkb - 1) * BB);
     }
     // top of block kb: decoder state from this wave's windows, block scale into the
     // accumulators; then (its windows read) the next block's windows
@@ -898,10 +926,13 @@ struct GuChunk {
             if (kb + 1 < nkb || !pf_next)
                 wload(kb + 1);
             else
-                wload_from(srcg_n, srcu_n, woff_n, 0u);  // block 0 of the next chunk
+                wload_from(srcg_n, srcu_n, woff_n, wx_n, 0u);  // block 0 of the next chunk
         }
         mem_fence_compiler();
-        step_mfma<QT, F16, MT, NT, H>(dec, ln, sh, sh.ring[H], m, g, acc);
+        int sa[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sa[mt] = 127;  // x rows: the per-row scale is applied after the K loop
+        step_mfma<QT, F16, MT, NT, H>(dec, ln, sh, sh.ring[H], m, g, acc, sa);
         // the step's MFMAs are issued before the next step's barrier (not sunk past it, which
         // would keep two steps' operands live)
 #pragma unroll
@@ -932,6 +963,92 @@ struct GuChunk {
     }
 };
 
+// T1 gate/up output for the fp8 down kernel: h = silu(gate) * up of the chunk's rows goes straight
+// into hi/lo fp8 rows in the down kernel's k order ([kb][h][g][hi 32 | lo 32], as the split of
+// activation rows), scaled by 2^sigma per (row, work item) with max |h| * 2^sigma in [128, 256)
+// over the item's 128 columns (block kb, k-groups 2p and 2p+1: one scale of the down MFMA);
+// byte 2*kb + p of hsc[row] = 127 - sigma.  The maximum is a reduction over 16 lanes, then over
+// the work-group's waves in LDS.
+// maximum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1: no LDS round trips)
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+    return x;
+}
+
+template <int MT, int NTI, class Ch>
+__device__ __forceinline__ void t1_h_split_out(const GuArgs& a, const GuShared& sh, const Ch& ch, int pc, int rows,
+                                               int colw, int wave, int n, int g) {
+    // lane indices made opaque here, so that the compiler does not hoist the epilogue's
+    // addresses out of the K loop (they would be spilled there)
+    asm volatile("" : "+v"(n), "+v"(g));
+    const int sb = colw >> 7;  // the item's scale byte, 2*kb + p
+    float v[MT][4][NTI], pm[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float xs = sh.rscale[mt * 16 + 4 * g + i];  // 0 for rows past the chunk
+            pm[mt][i] = 0.f;
+#pragma unroll
+            for (int ti = 0; ti < NTI; ++ti) {
+                const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
+                const float uv = ch.acc[mt][NTI + ti][i] * ch.rs[NTI + ti].dprev * xs;
+                v[mt][i][ti] = silu_fast(gv) * uv;
+                pm[mt][i] = fmaxf(pm[mt][i], fabsf(v[mt][i][ti]));
+            }
+        }
+    // the 16 lanes n of lane group g hold the same rows
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm[mt][i] = row16_max(pm[mt][i]);
+    if (n == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sh.hred[wave * 64 + mt * 16 + 4 * g + i] = pm[mt][i];
+    }
+    lds_barrier();
+    float am[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            am[mt][i] = fmaxf(fmaxf(sh.hred[r], sh.hred[64 + r]), fmaxf(sh.hred[128 + r], sh.hred[192 + r]));
+        }
+    static_assert(GU_NW == 4, "the work item's maximum spans the four waves");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = mt * 16 + 4 * g + i;
+            if (r < rows) {
+                const float amax = am[mt][i];
+                const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 255u) - 127 : 7;
+                int sigma = 7 - ex;
+                sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
+                const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
+                uint8_t* drow = a.h8 + (size_t)(pc + r) * (size_t)(2 * a.N);
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti) {
+                    const int qc = colw + 16 * ti + n, j = qc & 63;
+                    const int off = 512 * (qc >> 8) + 256 * (j >> 5) + 64 * ((qc >> 6) & 3) + (j & 31);
+                    const float x = v[mt][i][ti] * sc;
+                    const int hb = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false);
+                    const int lb = __builtin_amdgcn_cvt_pk_fp8_f32(x - __builtin_amdgcn_cvt_f32_fp8(hb, 0), 0.f, 0, false);
+                    drow[off] = (uint8_t)hb;
+                    drow[off + 32] = (uint8_t)lb;
+                }
+                if (n == 0 && wave == 0) ((uint8_t*)a.hsc)[(size_t)(pc + r) * 4 + sb] = (uint8_t)(127 - sigma);
+            }
+        }
+    // hred is rewritten only after the next chunk's step barriers
+}
+
 // One 64-pair chunk of a work item: K loop, then the epilogue (gate/up: SwiGLU into h; down:
 // fp16 rows of y).  During the chunk's next-to-last step the hook gathers the next chunk's
 // activation row offsets (xon), this chunk's per-row activation scales (ps; 1 for Q2B) and, for
@@ -940,9 +1057,9 @@ template <int QT, int MODE, int NTI, int MT>
 __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, const BufSrc& srcx,
                                          const BufSrc& srcg, const BufSrc& srcu, const BufSrc& srcg_n,
                                          const BufSrc& srcu_n, const uint32_t* xoff, const uint32_t* roff,
-                                         const uint32_t* woff, const uint32_t* woff_n, const T1Lane8& ln, int nkb,
-                                         int pc, int rows, int colw, bool has_next, bool pf_have, int pn,
-                                         int rows_n, uint32_t* xon) {
+                                         const uint32_t* woff, const uint32_t* woff_n, const uint32_t* wx,
+                                         const uint32_t* wx_n, const T1Lane8& ln, int nkb, int pc, int rows,
+                                         int colw, bool has_next, bool pf_have, int pn, int rows_n, uint32_t* xon) {
     constexpr int NMAT = MODE == GU_GATEUP ? 2 : 1;
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     float ps = 0.f;
@@ -966,15 +1083,21 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
             }
         }
     };
-    GuChunk<QT, NMAT, NTI, MT> ch{sh,     srcx,    srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, xon, ln, nkb,
-                                  2 * nkb, wave,   n,    g,    (uint32_t)nkb * (uint32_t)Fmt<QT>::BYTES,
-                                  has_next, pf_have};
+    GuChunk<QT, NMAT, NTI, MT> ch{sh,   srcx,   srcg,   srcu, srcg_n, srcu_n, xoff, roff, woff,
+                                  woff_n, wx,   wx_n,   xon,  ln,     nkb,    2 * nkb, wave, n,
+                                  g,      (uint32_t)nkb * (uint32_t)Fmt<QT>::BYTES, has_next, pf_have};
     ch.run(hook);
     if (tid < 64) {
         sh.rscale[tid] = ps;
         if constexpr (MODE == GU_DOWN) sh.rdst[tid] = pdst;
     }
     lds_barrier();
+    if constexpr (QT == QT_T1 && MODE == GU_GATEUP) {
+        if (a.h8 != nullptr) {
+            t1_h_split_out<MT, NTI>(a, sh, ch, pc, rows, colw, wave, n, g);
+            return;
+        }
+    }
     bool ovf = false;
     // lane holds rows 4g..4g+3 of each 16-row tile, column n
 #pragma unroll
@@ -989,7 +1112,8 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
                     for (int ti = 0; ti < NTI; ++ti) {
                         const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
                         const float uv = ch.acc[mt][NTI + ti][i] * ch.rs[NTI + ti].dprev * xs;
-                        a.hbuf[(size_t)(pc + r) * a.N + colw + 16 * ti + n] = f32_to_f16_bits(silu_fast(gv) * uv);
+                        const int hc = QT == QT_T1 ? t1_hcol(colw + 16 * ti + n, a.N) : colw + 16 * ti + n;
+                        a.hbuf[(size_t)(pc + r) * a.N + hc] = f32_to_f16_bits(silu_fast(gv) * uv);
                     }
                 } else {
                     uint16_t* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + colw + n;
@@ -1018,11 +1142,15 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * WinGeo<QT>::WS];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
+    constexpr bool HCOL = QT == QT_T1 && MODE == GU_GATEUP;  // output columns in t1_hcol order
+    __shared__ float hred[HCOL ? GU_NW * 64 : 1];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     const StaticSched sc(uni(*a.wl_len), a.ns);
     if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
     Tab::build(t64, tbl8, tid, NTHR);
-    const GuShared sh = Tab::shared(ring0, ring1, wts, t64, tbl8, rscale, rdst);
+    GuShared sh0 = Tab::shared(ring0, ring1, wts, t64, tbl8, rscale, rdst);
+    sh0.hred = hred;
+    const GuShared sh = sh0;
     T1Lane8 ln;
     ln.init(g);
     const int nkb = a.K >> 8;
@@ -1066,20 +1194,26 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
         const BufSrc srcu_n(a.arena + recn.off[1], mat_bytes);
         const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
         const int colw_n = sc.slice(ixn) * (16 * NTI * GU_NW) + wave * (16 * NTI);
-        uint32_t roff[NT], woff[NT], woff_n[NT];
+        // weight row of output position c; quarter 3 of a strip starting at position c0 begins
+        // at row col(c0 + 12), which for t1_hcol's tail tiles is not col(c0) + 12
+        auto col = [&](int c) { return HCOL ? t1_hcol(c, a.N) : c; };
+        uint32_t roff[NT], woff[NT], woff_n[NT], wx[NT], wx_n[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            roff[t] = (uint32_t)(colw + 16 * (t % NTI) + n) * row_bytes;
-            woff[t] = ((uint32_t)(colw + 16 * (t % NTI)) + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
-            woff_n[t] = ((uint32_t)(colw_n + 16 * (t % NTI)) + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
+            const int c0 = colw + 16 * (t % NTI), c0n = colw_n + 16 * (t % NTI);
+            roff[t] = (uint32_t)col(c0 + n) * row_bytes;
+            woff[t] = (uint32_t)col(c0 + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
+            woff_n[t] = (uint32_t)col(c0n + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
+            wx[t] = (uint32_t)(col(c0 + 12) - col(c0) - 12) * row_bytes;
+            wx_n[t] = (uint32_t)(col(c0n + 12) - col(c0n) - 12) * row_bytes;
         }
         uint32_t xon[GU_DMA];
 #pragma unroll
         for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
         const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
 #define RL_GU_CHUNK(MT_)                                                                                               \
-    gu_chunk<QT, MODE, NTI, MT_>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, ln, nkb, pc, rows, \
-                                 colw, has_next, pf_have, pn, rows_n, xon)
+    gu_chunk<QT, MODE, NTI, MT_>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, wx, wx_n, ln, nkb, \
+                                 pc, rows, colw, has_next, pf_have, pn, rows_n, xon)
         switch ((rows + 15) >> 4) {
             case 1: RL_GU_CHUNK(1); break;
             case 2: RL_GU_CHUNK(2); break;
@@ -1138,6 +1272,8 @@ struct DnSweep {
     uint32_t rowb;
     bool pf_next;               // load the next sweep's first windows during the last block
     bool pf_have;               // this sweep's first windows were loaded by the sweep before
+    uint32_t rw[MT];            // T1: the scale word (hsc) of the lane's A row, per row tile
+    int sa[MT];                 // T1: this block's A scale of the lane (127 = 1)
     typename StripDec<QT>::type dec[NT];
     RunScale rs[NT];
     f32x4 acc[MT][NT];
@@ -1173,6 +1309,10 @@ struct DnSweep {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= r;
         }
+        // lane group g supplies the scale of k-group pair g & 1 (see mfma_f8)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            sa[mt] = QT == QT_T1 ? (int)((rw[mt] >> (16 * kb + 8 * (g & 1))) & 255u) : 127;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // windows read before they are replaced
         if (kb + 1 < nkb)
             wload_from(srcw, woff, (uint32_t)(kb + 1) * BB);
@@ -1181,7 +1321,7 @@ struct DnSweep {
     }
     template <int H>
     __device__ __forceinline__ void step(int c) {
-        step_mfma<QT, true, MT, NT, H>(dec, ln, sh, sh.ring[0] + c * DN_ACT, m, g, acc);
+        step_mfma<QT, true, MT, NT, H>(dec, ln, sh, sh.ring[0] + c * DN_ACT, m, g, acc, sa);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -1205,9 +1345,13 @@ struct DnSweep {
 template <int QT, int MT>
 __device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, const BufSrc& srcw,
                                          const BufSrc& srcw_next_item, const T1Lane8& ln, int nkb, uint32_t rowb,
-                                         int cbase, int nsw, int cbase_next, bool next_item) {
+                                         int cbase, int nsw, int cbase_next, bool next_item, const uint32_t* rsc) {
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     bool pf_have = true;  // the first sweep's windows were loaded before the chunk's staging
+    // scale word of the lane's A row (row mt*16 + n) in each row tile
+    uint32_t rw[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) rw[mt] = rsc[mt * 16 + n];
     for (int s = 0; s < nsw; ++s) {
         const int col0 = cbase + s * DN_SW + wave * (16 * DN_NT);
         const bool last = s + 1 == nsw;
@@ -1221,6 +1365,8 @@ __device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, co
         }
         DnSweep<QT, MT> sw{sh,  srcw, last ? srcw_next_item : srcw, roff, woff, woff_n, ln, nkb, wave, n, g, rowb,
                            !last || next_item, pf_have};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sw.rw[mt] = rw[mt];
         sw.run();
         // y rows of the tile (padding rows to the spare row)
         bool ovf = false;
@@ -1229,10 +1375,9 @@ __device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, co
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = mt * 16 + 4 * g + i;
-                const float xs = sh.rscale[r];
                 uint16_t* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + col0 + n;
 #pragma unroll
-                for (int t = 0; t < DN_NT; ++t) yrow[16 * t] = y_bits(sw.acc[mt][t][i] * sw.rs[t].dprev * xs, ovf);
+                for (int t = 0; t < DN_NT; ++t) yrow[16 * t] = y_bits(sw.acc[mt][t][i] * sw.rs[t].dprev, ovf);
             }
         y_range_flag(ovf, a.flags);
         pf_have = true;
@@ -1247,7 +1392,7 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
     typedef GuTables<QT, true> Tab;
     __shared__ __attribute__((aligned(32768))) uint64_t t64[Tab::N64];
     __shared__ uint32_t tbl8[8];
-    __shared__ float rscale[DN_ROWS];
+    __shared__ uint32_t rsc[DN_ROWS];  // T1: the rows' scale words (hsc)
     __shared__ int32_t rdst[DN_ROWS];
     __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * DN_NT * G::WS];
     __shared__ __attribute__((aligned(16))) uint8_t actb[(DN_KMAX / 128) * DN_ACT];
@@ -1255,7 +1400,7 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
     const StaticSched sc(uni(*a.wl_len), a.ns);
     if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
     Tab::build(t64, tbl8, tid, NTHR);
-    const GuShared sh = Tab::shared(actb, actb, wts, t64, tbl8, rscale, rdst);
+    const GuShared sh = Tab::shared(actb, actb, wts, t64, tbl8, nullptr, rdst);
     T1Lane8 ln;
     ln.init(g);
     const int nkb = a.K >> 8, NS = 2 * nkb;
@@ -1281,7 +1426,7 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srcx.r, (lds_void*)(actb + c * DN_ACT + rg * 1024), 16, off, 0, 0, 0);
         }
         if (tid < DN_ROWS) {
-            rscale[tid] = tid < rows ? (QT == QT_T1 ? a.ascale[pc + tid] : 1.0f) : 0.f;
+            rsc[tid] = QT == QT_T1 && tid < rows ? a.hsc[pc + tid] : 0x7F7F7F7Fu;
             rdst[tid] = tid < rows ? a.pair_src[pc + tid] : P;
         }
     };
@@ -1324,9 +1469,9 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // the chunk's activations and row tables
         switch ((rows + 15) >> 4) {
-            case 1: dn_chunk<QT, 1>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
-            case 2: dn_chunk<QT, 2>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
-            default: dn_chunk<QT, 3>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next); break;
+            case 1: dn_chunk<QT, 1>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next, rsc); break;
+            case 2: dn_chunk<QT, 2>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next, rsc); break;
+            default: dn_chunk<QT, 3>(a, sh, srcw, srcw_n, ln, nkb, rowb, cbase, nsw, cbase_n, has_next, rsc); break;
         }
         if (!has_next) break;
         q = qn;

@@ -62,7 +62,7 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + (size_t)T * sizeof(float));
     L.h8 = off;  // fp8 hi/lo h of the T1 down path
     off = align_up(off + P * (size_t)2 * I);
-    L.hscale = off;  // scale of each row of h8
+    L.hscale = off;  // scale of each row of h8 (I > 512), or its four k-group scales (I <= 512)
     off = align_up(off + P * sizeof(float));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
@@ -338,10 +338,12 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
 #undef RL_GV2
 }
 
-// grouping + gate/up for every present type; returns the layout used
+// grouping + gate/up for every present type; returns the layout used.  With h8 (T1, I <= 512)
+// the T1 gate/up writes its h rows split for the fp8 down kernel (h8, with k-group scales hsc)
+// instead of fp16 rows of hdst.
 void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blobs* ex, int32_t T, int32_t k,
                       void* ws, const int present[3], uint16_t* hdst, hipStream_t s, Layout& L,
-                      void* const* events = nullptr) {
+                      void* const* events = nullptr, uint8_t* h8 = nullptr, uint32_t* hsc = nullptr) {
     auto mark = [&](int i) {
         if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
     };
@@ -381,6 +383,8 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         GuArgs q = b;
         q.act = xq;
         q.ascale = xscale;
+        q.h8 = h8;
+        q.hsc = hsc;
         q.items = items + (QT_T1 - 1) * ex->E;
         q.wl_len = flags + 8 + QT_T1;
         launch_gateup_mm<QT_T1>(q, present[QT_T1], s);
@@ -416,7 +420,12 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     uint16_t* yslot = at<uint16_t>(workspace, L.yslot);
     mark(0);
     Layout L2;  // same layout as L
-    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events);
+    // T1 with I <= 512: gate/up writes h already split for the down kernel (no split of h)
+    const bool t1_hsplit_fused = present[QT_T1] && experts->I % 256 == 0 && experts->I <= DN_KMAX;
+    uint8_t* h8 = at<uint8_t>(workspace, L.h8);
+    uint32_t* hsc = at<uint32_t>(workspace, L.hscale);
+    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events,
+                     t1_hsplit_fused ? h8 : nullptr, t1_hsplit_fused ? hsc : nullptr);
     DownArgs d;
     d.hbuf = hbuf;
     d.arena = static_cast<const uint8_t*>(experts->arena);
@@ -441,9 +450,10 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     b.N = experts->H;
     b.P = T * k;
     if (mm_dn && present[QT_T1]) {
-        b.act = at<uint8_t>(workspace, L.h8);
-        b.ascale = at<float>(workspace, L.hscale);
-        launch_hsplit(b, T * k, s);
+        b.act = h8;
+        b.ascale = at<float>(workspace, L.hscale);  // I > 512: one scale per row, from the split of h
+        b.hsc = hsc;                                // I <= 512: k-group scales from gate/up
+        if (!t1_hsplit_fused) launch_hsplit(b, T * k, s);
     }
     mark(3);
     for (int q = QT_Q2B; q <= QT_T1; ++q) {
