@@ -155,6 +155,30 @@ def test_prefill_parity(orc, rl, cases, name):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("I", [256, 512])
+def test_prefill_t1_row_scales(orc, rl, I):
+    """T1 experts with I <= 512 hand h to the down kernel as hi/lo fp8 under one power-of-two
+    scale per row, block and k-group pair.  Token rows scaled by 2^e, e in [-4, 3] (h then spans
+    ~14 binades across rows, and y stays in fp16's normal range): every output row must meet the
+    bar against its own norm, which a scale shared across rows, or taken from the wrong rows or
+    k-groups, would miss."""
+    import dataclasses
+
+    wl = make_workload("t1_2048", seed=37 + I, T=64, E=16, H=1024, I=I, k=4)
+    e = np.random.default_rng(I).integers(-4, 4, size=wl.T)
+    xf = (wl.x.astype(np.uint32) << 16).view(np.float32) * np.exp2(e)[:, None].astype(np.float32)
+    wl = dataclasses.replace(wl, x=(xf.view(np.uint32) >> 16).astype(np.uint16))  # exact: powers of two
+    log(f"prefill t1 row scales I={I} T={wl.T} k={wl.k} E={wl.experts.E} H={wl.experts.H}")
+    x, ids, w, ex = to_device(wl)
+    ws = rl.alloc_workspace(wl.T, wl.k, ex)
+    out = rl.prefill(x, ids, w, ex, ws=ws).cpu().numpy().astype(np.float64)
+    assert rl.status(ws)[0] == 0
+    ref = orc.moe_workload(wl)
+    per_row = np.linalg.norm(out - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    log(f"  rel_l2 per row: max {per_row.max():.3e} median {np.median(per_row):.3e}")
+    assert per_row.max() <= TOL
+
+
 @pytest.mark.parametrize("name", ["tiny_q2b", "med_t1", "med_mixed", "i64_q2b"])
 def test_gate_up_h_parity(orc, rl, cases, name):
     wl = _case(cases, name)
