@@ -294,7 +294,8 @@ def main():
         "decode_path": dec,
         "router": router,
         "roofline": {
-            "kernel": {"t1": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU)",
+            "kernel": {"t1": "k_t1_f8<gate/up> (fused T1 decode + gate/up grouped GEMM on fp8 MFMA + SwiGLU + split of h "
+                             "into hi/lo fp8 for the down kernel)",
                        "q2b": "k_q2_mm<gate/up> (fused Q2B decode + gate/up grouped GEMM on bf16 MFMA + SwiGLU)",
                        "mixed": "k_q2_mm<gate/up> + k_t1_f8<gate/up> (both gate/up stage kernels, one per block "
                                 "type)"}[wl.meta["types"]],
