@@ -238,11 +238,13 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
         } else if (i < r_end) {
             a.inv[p0 + i] = -1;
         }
-        // every lane's read of whist[wave][e] happens before the leaders' updates
-        __builtin_amdgcn_s_waitcnt(0);
+        // every lane's read of whist[wave][e] happens before the leaders' updates, and the
+        // updates before the next round's reads: LDS waits only (the pair_src / inv stores above
+        // need not complete here)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_wave_barrier();
         if (ok && (peers & lt_mask) == 0) whist[wave][e] += __popcll(peers);
-        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
