@@ -4,11 +4,12 @@
 //                    launch) the split of x into hi/lo fp8 rows for the T1 experts
 //   k_group_count    the pair histograms alone (layers without T1 experts, the grouping hook)
 //   k_group_scatter  stable placement of the pairs by expert, offsets, per-type work lists
-//   k_t1_f8          T1 experts on the fp8 MFMA (16x16x128): gate/up + SwiGLU -> h (fp16); also
-//                    down for I > 512 (streamed split-h activations)
+//   k_t1_f8          T1 experts on the fp8 MFMA (16x16x128): gate/up + SwiGLU -> h, for I <= 512
+//                    already split into hi/lo fp8 rows for k_t1_dn, else fp16; also down for
+//                    I > 512 (streamed split-h activations)
 //   k_q2_mm          Q2B experts on the 16-bit MFMA (16x16x32), same structure: gate/up on bf16 x,
 //                    down for I > 512 on fp16 h
-//   k_split          split of h into hi/lo fp8 rows for the T1 down kernels
+//   k_split          split of fp16 h into hi/lo fp8 rows for the T1 down kernel when I > 512
 //   k_t1_dn          T1 down for I <= 512, a chunk's split h rows held in LDS -> y (fp16)
 //   k_q2_dn          Q2B down for I <= 512, a chunk's fp16 h rows held in LDS -> y (fp16)
 //   k_down           both types with I < 256: decode + down on fp16 MFMA -> y (fp16)
