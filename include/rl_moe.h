@@ -62,20 +62,26 @@ typedef struct rl_expert_desc {
 } rl_expert_desc;
 
 /* The experts of one layer.  arena [dev]: packed blocks, 4-byte aligned, its allocation a
- * whole number of dwords; every matrix offset a multiple of 4 (RL_EINVAL otherwise).  desc
- * [dev]: E descriptors (read by the kernels).  desc_host [host]: the same E descriptors (read by the host to decide which
- * type-specialised kernels to launch).  E in [1, 1024].  H (hidden) a multiple of 256 in
- * [256, 8192].  I (expert intermediate) a multiple of 64 in [64, 4096] that is either a
- * multiple of 256 or one of 64 / 128. */
+ * whole number of dwords; arena_bytes its size: every matrix of every expert must lie inside it
+ * (offset a multiple of 4, offset + matrix bytes <= arena_bytes; RL_EINVAL otherwise).  desc
+ * [dev]: E descriptors (read by the kernels).  desc_host [host]: the same E descriptors (read by
+ * the host to decide which type-specialised kernels to launch and to check the offsets); the two
+ * copies must agree.  E in [1, 1024].  H (hidden) a multiple of 256 in [256, 8192].  I (expert
+ * intermediate) a multiple of 64 in [64, 4096] that is either a multiple of 256 or one of
+ * 64 / 128.  Matrix bytes: H * I / 256 blocks of 74 (Q2B) or 57 (T1) bytes. */
 typedef struct rl_expert_blobs {
     const void* arena;
     const rl_expert_desc* desc;
     const rl_expert_desc* desc_host;
     int32_t E, H, I;
+    uint64_t arena_bytes;
 } rl_expert_blobs;
 
 /* Bytes of workspace that rl_moe_prefill / rl_moe_decode / rl_moe_gate_up need for up to
- * T_max tokens with k selections each.  0 if the sizes are outside the supported set. */
+ * T_max tokens with k selections each.  0 if the sizes are outside the supported set, which
+ * besides the ranges above requires T * k <= 2^24 and that the kernels' 32-bit buffer offsets
+ * cannot wrap: T * 2 * H and T * k * 2 * I bytes (the activation rows of the gate/up and down
+ * GEMMs) at most 2^31 - 2^16. */
 size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, int32_t I);
 
 /* Routed-expert layer for T tokens (prompt ingestion).
@@ -127,16 +133,39 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t* pair_src, int32_t* inv, void* workspace, size_t ws_bytes, void* stream);
 
 /* Block decode alone (parity hook for the in-kernel weight decode): n_values (a multiple of
- * 256) consecutive values of `blocks` [dev] as float d * s * c into out [dev].  Uses the same
- * device decode routine as the matrix kernels. */
-int rl_moe_dequant(int32_t qtype, const void* blocks, int64_t n_values, float* out, void* stream);
+ * 256) consecutive values of `blocks` [dev] (any byte address) as float d * s * c into out [dev].
+ * `decoder` picks which of the library's device decoders runs, exactly as the kernels run it:
+ *   RL_DEC_STRIP        the strip decoder of the 1-2 row kernels and of the down kernel for
+ *                       I < 256 (64-value strips, bf16 operand table)
+ *   RL_DEC_MFMA_GATEUP  the MFMA operand decoder of the gate/up GEMMs (T1: fp8 operands, digit
+ *                       selector and fp8 scale tables built on the device; Q2B: bf16 operands);
+ *                       value k of a block is written where its operand byte / half stands for
+ *   RL_DEC_MFMA_DOWN    the same for the down GEMMs (T1: identical to gate/up; Q2B: fp16 operands)
+ * Every such product is exact in fp32, so any correct decode is bit-identical to the format's
+ * definition.  RL_EINVAL for an unknown qtype or decoder; RL_ESHAPE if the blocks span more than
+ * 2^32 - 16 bytes. */
+#define RL_DEC_STRIP 0
+#define RL_DEC_MFMA_GATEUP 1
+#define RL_DEC_MFMA_DOWN 2
+int rl_moe_dequant(int32_t qtype, int32_t decoder, const void* blocks, int64_t n_values, float* out, void* stream);
 
-/* Grouping + fused dequant/gate/up/SwiGLU alone (parity hook): writes h as fp16 bits
- * [T*k][I] in sorted-pair order (row = sorted position) to h_out [dev].  Arguments as
- * rl_moe_prefill. */
+/* Grouping + fused dequant/gate/up/SwiGLU alone (parity hook): the launches rl_moe_prefill makes
+ * before its down GEMM, with h left where the down GEMM would read it, rows in sorted-pair order
+ * (row = sorted position of the pair, as rl_moe_group_pairs orders them):
+ *   h16_out [dev] fp16 bits [T*k][I]: the rows of Q2B experts, and of T1 experts when the layer's
+ *           T1 gate/up writes fp16 h (I > 512 or I < 256)
+ *   h8_out  [dev] bytes [T*k][2*I], hsc_out [dev] uint32 [T*k]: the rows of T1 experts when I is
+ *           a multiple of 256 and at most 512.  Then gate/up writes h already split for the fp8
+ *           down GEMM: row r holds, for each 256-column block kb, lane group g (0..3) and half hh,
+ *           32 bytes hi then 32 bytes lo at byte 512*kb + 256*hh + 64*g (+32 for lo); byte p of
+ *           them stands for h column 256*kb + m(g, 32*hh + p), m(g, j) = 60g + j for j < 60, else
+ *           240 + 4g + (j - 60); hi and lo are e4m3; byte 2*kb + (g >> 1) of hsc_out[r] is the
+ *           E8M0 scale e of that block's lane groups {g, g^1}: h = (hi + lo) * 2^(e - 127).
+ * Rows of the other kind are left untouched.  h8_out / hsc_out may be NULL when no row uses
+ * them (RL_EINVAL if they are needed); h16_out likewise.  Other arguments as rl_moe_prefill. */
 int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
-                   const rl_expert_blobs* experts, uint16_t* h_out, int32_t T, int32_t k,
-                   void* workspace, size_t ws_bytes, void* stream);
+                   const rl_expert_blobs* experts, uint16_t* h16_out, uint8_t* h8_out, uint32_t* hsc_out,
+                   int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream);
 
 /* Router, the step before the layer (the MoE routing that the pages take as given; dev72
  * "2-row verify" keeps each row's selection order): for every token t, softmax over the E

@@ -21,6 +21,19 @@ def lib_path() -> str:
     return _LIB
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the cores this process may run on (its CPU affinity), capped
+    by OMP_NUM_THREADS when that is set (a shared GPU host gives each job a share of its cores)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc: -O2, no fast-math, no floating-point contraction."""
     if force or not os.path.exists(_LIB):
@@ -115,7 +128,7 @@ def moe_prefill(x, ids, w, arena, desc, E, H, I, tokens=None, want_h=False, thre
     n = tok.size
     out = np.empty((max(n, 1), H), np.float64)
     h = np.empty((max(n, 1), k, I), np.float64) if want_h else None
-    nthr = threads or (os.cpu_count() or 1)
+    nthr = threads or default_threads()
     rc = lib.orc_moe_prefill(_ptr(x), _ptr(ids), _ptr(w), _ptr(arena), _ptr(desc), E, H, I, T, k, _ptr(tok), n,
                              _ptr(out), _ptr(h) if h is not None else None, int(nthr))
     if rc:

@@ -9,6 +9,10 @@ from ._binding import (  # noqa: F401
     RL_OK,
     RL_QTYPE_Q2B,
     RL_QTYPE_T1,
+    RL_DEC_STRIP,
+    RL_DEC_MFMA_GATEUP,
+    RL_DEC_MFMA_DOWN,
+    t1_splits_h,
     RlError,
     DeviceExperts,
     lib,

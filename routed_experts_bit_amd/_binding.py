@@ -12,6 +12,10 @@ _LIB_PATH = os.path.join(_PKG, "librl_moe.so")
 RL_OK = 0
 RL_QTYPE_Q2B = 1
 RL_QTYPE_T1 = 2
+RL_DEC_STRIP = 0
+RL_DEC_MFMA_GATEUP = 1
+RL_DEC_MFMA_DOWN = 2
+_BLOCK_BYTES = {RL_QTYPE_Q2B: 74, RL_QTYPE_T1: 57}
 
 # every entry point declared in include/rl_moe.h
 EXPORTS = (
@@ -40,6 +44,7 @@ class _Blobs(C.Structure):
         ("E", C.c_int32),
         ("H", C.c_int32),
         ("I", C.c_int32),
+        ("arena_bytes", C.c_uint64),
     ]
 
 
@@ -62,14 +67,16 @@ def lib():
     L.rl_moe_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     L.rl_moe_workspace_bytes.restype = SZ
     layer = [P, P, P, C.POINTER(_Blobs), P, I32, I32, P, SZ, P]
-    for name in ("rl_moe_prefill", "rl_moe_decode", "rl_moe_gate_up"):
+    for name in ("rl_moe_prefill", "rl_moe_decode"):
         getattr(L, name).argtypes = layer
         getattr(L, name).restype = C.c_int
+    L.rl_moe_gate_up.argtypes = [P, P, P, C.POINTER(_Blobs), P, P, P, I32, I32, P, SZ, P]
+    L.rl_moe_gate_up.restype = C.c_int
     L.rl_moe_prefill_timed.argtypes = layer + [C.POINTER(C.c_void_p)]
     L.rl_moe_prefill_timed.restype = C.c_int
     L.rl_moe_group_pairs.argtypes = [P, I32, I32, I32, P, P, P, P, SZ, P]
     L.rl_moe_group_pairs.restype = C.c_int
-    L.rl_moe_dequant.argtypes = [I32, P, C.c_int64, P, P]
+    L.rl_moe_dequant.argtypes = [I32, I32, P, C.c_int64, P, P]
     L.rl_moe_dequant.restype = C.c_int
     L.rl_moe_route.argtypes = [P, I32, I32, I32, P, P, P]
     L.rl_moe_route.restype = C.c_int
@@ -110,24 +117,76 @@ def _ptr(t) -> C.c_void_p:
     return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
 
 
+def _need(name, t, dtypes, shape=None, device=None):
+    """Raise RlError unless `t` is a contiguous CUDA tensor of one of `dtypes`, of `shape` (None
+    entries match any size) and on `device`; the library reads and writes these buffers as dense
+    arrays of exactly that layout."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise RlError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise RlError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(want is not None and got != want for got, want in zip(t.shape, shape)):
+            raise RlError(f"{name}: shape {tuple(t.shape)}, expected {tuple('*' if v is None else v for v in shape)}")
+    if not t.is_contiguous():
+        raise RlError(f"{name}: must be contiguous")
+    if not t.is_cuda:
+        raise RlError(f"{name}: must be on a CUDA (HIP) device, is on {t.device}")
+    if device is not None and t.device != device:
+        raise RlError(f"{name}: on {t.device}, the call's other buffers are on {device}")
+    return t
+
+
+def _dt():
+    torch = _torch()
+    return dict(x=(torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16),
+                ids=(torch.int32,), w=(torch.float32,), out=(torch.float32,), ws=(torch.uint8,))
+
+
+def _check_layer_args(x, ids, w, ex, out, ws, rows=None):
+    """Shapes of one layer call: x [T, H] bf16 bits, ids int32 [T, k], w float32 [T, k], out
+    float32 [T, H], ws a uint8 buffer of at least workspace_bytes(T, k, ...) bytes."""
+    d = _dt()
+    _need("topk_ids", ids, d["ids"], (None, None))
+    T, k = ids.shape
+    if rows is not None and T not in rows:
+        raise RlError(f"topk_ids: {T} rows, expected one of {rows}")
+    dev = ids.device
+    _need("x", x, d["x"], (T, ex.H), dev)
+    _need("topk_w", w, d["w"], (T, k), dev)
+    if out is not None:
+        _need("out", out, d["out"], (T, ex.H), dev)
+    _need("workspace", ws, d["ws"], (None,), dev)
+    if ex.arena.device != dev or ex.desc.device != dev:
+        raise RlError(f"experts: on {ex.arena.device}, the call's buffers are on {dev}")
+    need = workspace_bytes(max(T, 1), k, ex.E, ex.H, ex.I)
+    if ws.numel() < need:
+        raise RlError(f"workspace: {ws.numel()} bytes, the call needs {need}")
+    return T, k
+
+
 class DeviceExperts:
     """Packed experts resident on the GPU: arena (uint8) and descriptors, plus the host copy
-    of the descriptors that the library reads to choose its type-specialised kernels."""
+    of the descriptors that the library reads to choose its type-specialised kernels.  Every
+    descriptor is checked against the arena here (block type known, offsets dword-aligned, each
+    matrix inside the arena); the library checks the same again on every call."""
 
     def __init__(self, arena_u8, desc_np: np.ndarray, E: int, H: int, I: int, device="cuda"):
         torch = _torch()
         self.E, self.H, self.I = int(E), int(H), int(I)
         if isinstance(arena_u8, np.ndarray):
             n = arena_u8.size
-            buf = torch.empty((n + 3) // 4 * 4, dtype=torch.uint8, device=device)
+            buf = torch.zeros((n + 3) // 4 * 4, dtype=torch.uint8, device=device)
             buf[:n].copy_(torch.from_numpy(np.ascontiguousarray(arena_u8)))
             self.arena = buf
         else:
-            self.arena = arena_u8
+            self.arena = _need("arena", arena_u8, (torch.uint8,), (None,))
         self.desc_host = np.ascontiguousarray(desc_np)
-        self.desc = torch.from_numpy(self.desc_host.view(np.uint8).copy()).to(device)
+        _check_descriptors(self.desc_host, self.E, self.H, self.I, self.arena.numel())
+        self.desc = torch.from_numpy(self.desc_host.view(np.uint8).copy()).to(self.arena.device)
         self._blobs = _Blobs(self.arena.data_ptr(), self.desc.data_ptr(), self.desc_host.ctypes.data, self.E, self.H,
-                             self.I)
+                             self.I, self.arena.numel())
 
     @classmethod
     def from_workload(cls, experts, device="cuda"):
@@ -135,15 +194,41 @@ class DeviceExperts:
 
     def with_arena(self, arena):
         """Same descriptors over another arena copy (another address, same content)."""
+        torch = _torch()
+        _need("arena", arena, (torch.uint8,), (None,))
+        if arena.numel() < self.arena.numel():
+            raise RlError("with_arena: the copy is smaller than the arena the descriptors were checked against")
         other = DeviceExperts.__new__(DeviceExperts)
         other.E, other.H, other.I = self.E, self.H, self.I
         other.arena, other.desc_host, other.desc = arena, self.desc_host, self.desc
-        other._blobs = _Blobs(arena.data_ptr(), self.desc.data_ptr(), self.desc_host.ctypes.data, self.E, self.H, self.I)
+        other._blobs = _Blobs(arena.data_ptr(), self.desc.data_ptr(), self.desc_host.ctypes.data, self.E, self.H, self.I,
+                              arena.numel())
         return other
 
     @property
     def blobs(self):
         return C.byref(self._blobs)
+
+    @property
+    def qtypes(self) -> np.ndarray:
+        return self.desc_host["qtype"]
+
+
+def _check_descriptors(desc: np.ndarray, E: int, H: int, I: int, arena_bytes: int):
+    if desc.shape != (E,) or desc.dtype.itemsize != 32:
+        raise RlError(f"descriptors: expected {E} records of 32 bytes, got {desc.shape} x {desc.dtype.itemsize}")
+    if H <= 0 or I <= 0 or (H * I) % 256:
+        raise RlError(f"experts: H={H} I={I} do not tile into 256-value blocks")
+    for e in range(E):
+        q = int(desc["qtype"][e])
+        if q not in _BLOCK_BYTES:
+            raise RlError(f"expert {e}: unknown block type {q}")
+        mb = H * I // 256 * _BLOCK_BYTES[q]
+        for which in ("gate_off", "up_off", "down_off"):
+            off = int(desc[which][e])
+            if off % 4 or off + mb > arena_bytes:
+                raise RlError(f"expert {e}: {which} {off} (+{mb} bytes) is not a dword-aligned matrix inside the "
+                              f"{arena_bytes}-byte arena")
 
 
 def workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
@@ -169,11 +254,13 @@ def _layer(fn, x, ids, w, ex: DeviceExperts, out, ws):
 def prefill(x, ids, w, ex: DeviceExperts, out=None, ws=None):
     """x: bf16 [T,H] (torch.bfloat16 or int16 bits), ids int32 [T,k], w float32 [T,k] -> float32 [T,H]."""
     torch = _torch()
+    _need("topk_ids", ids, (torch.int32,), (None, None))
     T = ids.shape[0]
     if out is None:
         out = torch.empty((T, ex.H), dtype=torch.float32, device=ids.device)
     if ws is None:
         ws = alloc_workspace(T, ids.shape[1], ex, device=ids.device)
+    _check_layer_args(x, ids, w, ex, out, ws)
     _check(_layer(lib().rl_moe_prefill, x, ids, w, ex, out, ws), "rl_moe_prefill")
     return out
 
@@ -184,7 +271,7 @@ TIMED_EVENTS = 6  # RL_TIMED_EVENTS
 def prefill_timed(x, ids, w, ex: DeviceExperts, out, ws, events):
     """rl_moe_prefill with TIMED_EVENTS torch.cuda.Event (enable_timing) recorded between its
     kernels: grouping (which also splits x) | gate/up | h split | down | combine."""
-    T, k = ids.shape
+    T, k = _check_layer_args(x, ids, w, ex, out, ws)
     if len(events) != TIMED_EVENTS:
         raise RlError(f"prefill_timed needs {TIMED_EVENTS} events")
     arr = (C.c_void_p * TIMED_EVENTS)(*[C.c_void_p(e.cuda_event) for e in events])
@@ -196,31 +283,60 @@ def prefill_timed(x, ids, w, ex: DeviceExperts, out, ws, events):
 
 def decode(x, ids, w, ex: DeviceExperts, out=None, ws=None):
     torch = _torch()
+    _need("topk_ids", ids, (torch.int32,), (None, None))
     T = ids.shape[0]
     if out is None:
         out = torch.empty((T, ex.H), dtype=torch.float32, device=ids.device)
     if ws is None:
         ws = alloc_workspace(T, ids.shape[1], ex, device=ids.device)
+    _check_layer_args(x, ids, w, ex, out, ws, rows=(1, 2))
     _check(_layer(lib().rl_moe_decode, x, ids, w, ex, out, ws), "rl_moe_decode")
     return out
 
 
-def gate_up(x, ids, w, ex: DeviceExperts, h=None, ws=None):
-    """h (fp16 bits as int16) [T*k, I] in sorted-pair order."""
+def t1_splits_h(ex: DeviceExperts) -> bool:
+    """Whether the layer's T1 gate/up writes h split into hi/lo fp8 rows (I a multiple of 256, at
+    most 512), as rl_moe_gate_up documents."""
+    return bool(np.any(ex.qtypes == RL_QTYPE_T1)) and ex.I % 256 == 0 and ex.I <= 512
+
+
+def gate_up(x, ids, w, ex: DeviceExperts, ws=None, h16=None, h8=None, hsc=None):
+    """The grouping and gate/up launches of rl_moe_prefill alone.  Returns (h16, h8, hsc): h16
+    fp16 bits (int16) [T*k, I] for the rows that gate/up writes in fp16, and for T1 layers whose
+    gate/up writes h split for the fp8 down GEMM, h8 uint8 [T*k, 2I] and hsc int32 [T*k] (E8M0
+    scale bytes); rows in sorted-pair order.  Buffers the layer does not use are None."""
     torch = _torch()
+    _need("topk_ids", ids, (torch.int32,), (None, None))
     T, k = ids.shape
-    if h is None:
-        h = torch.empty((T * k, ex.I), dtype=torch.int16, device=ids.device)
+    P, dev = T * k, ids.device
+    split = t1_splits_h(ex)
+    need16 = bool(np.any(ex.qtypes == RL_QTYPE_Q2B)) or (bool(np.any(ex.qtypes == RL_QTYPE_T1)) and not split)
+    if need16 and h16 is None:
+        h16 = torch.empty((P, ex.I), dtype=torch.int16, device=dev)
+    if split and h8 is None:
+        h8 = torch.empty((P, 2 * ex.I), dtype=torch.uint8, device=dev)
+    if split and hsc is None:
+        hsc = torch.empty((P,), dtype=torch.int32, device=dev)
     if ws is None:
-        ws = alloc_workspace(T, k, ex, device=ids.device)
-    _check(_layer(lib().rl_moe_gate_up, x, ids, w, ex, h, ws), "rl_moe_gate_up")
-    return h
+        ws = alloc_workspace(T, k, ex, device=dev)
+    _check_layer_args(x, ids, w, ex, None, ws)
+    if h16 is not None:
+        _need("h16", h16, (torch.int16, torch.float16), (P, ex.I), dev)
+    if h8 is not None:
+        _need("h8", h8, (torch.uint8,), (P, 2 * ex.I), dev)
+    if hsc is not None:
+        _need("hsc", hsc, (torch.int32,), (P,), dev)
+    rc = lib().rl_moe_gate_up(_ptr(x), _ptr(ids), _ptr(w), ex.blobs, _ptr(h16), _ptr(h8), _ptr(hsc), T, k, _ptr(ws),
+                              ws.numel(), _stream())
+    _check(rc, "rl_moe_gate_up")
+    return h16, h8, hsc
 
 
 def group_pairs(ids, E: int):
     """Returns (offsets[E+1], pair_src[T*k], inv[T*k], workspace) as device tensors; the
     workspace holds the status flags (see status())."""
     torch = _torch()
+    _need("topk_ids", ids, (torch.int32,), (None, None))
     T, k = ids.shape
     dev = ids.device
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
@@ -233,22 +349,35 @@ def group_pairs(ids, E: int):
     return offsets, pair_src[: T * k], inv[: T * k], ws
 
 
-def dequant(qtype: int, blocks_u8, n_values: int, out=None):
+def dequant(qtype: int, blocks_u8, n_values: int, out=None, decoder: int = RL_DEC_STRIP):
+    """Decode n_values values of the blocks starting at blocks_u8's first byte (any alignment)
+    with the library's `decoder` (RL_DEC_*); float32 [n_values]."""
     torch = _torch()
+    _need("blocks", blocks_u8, (torch.uint8,), (None,))
+    nb = n_values // 256
+    if n_values % 256 or blocks_u8.numel() < nb * _BLOCK_BYTES.get(int(qtype), 0):
+        raise RlError(f"dequant: {blocks_u8.numel()} bytes do not hold {n_values} values of type {qtype}")
     if out is None:
         out = torch.empty(max(n_values, 1), dtype=torch.float32, device=blocks_u8.device)
-    _check(lib().rl_moe_dequant(int(qtype), _ptr(blocks_u8), int(n_values), _ptr(out), _stream()), "rl_moe_dequant")
+    _need("out", out, (torch.float32,), (None,), blocks_u8.device)
+    if out.numel() < n_values:
+        raise RlError("dequant: out is too small")
+    _check(lib().rl_moe_dequant(int(qtype), int(decoder), _ptr(blocks_u8), int(n_values), _ptr(out), _stream()),
+           "rl_moe_dequant")
     return out[:n_values]
 
 
 def route(logits, k: int, ids=None, w=None):
     """Router on the GPU: (topk_ids int32 [T, k], topk_w float32 [T, k]) from fp32 logits [T, E]."""
     torch = _torch()
+    _need("logits", logits, (torch.float32,), (None, None))
     T, E = logits.shape
     if ids is None:
         ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if w is None:
         w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _need("topk_ids", ids, (torch.int32,), (T, k), logits.device)
+    _need("topk_w", w, (torch.float32,), (T, k), logits.device)
     _check(lib().rl_moe_route(_ptr(logits), T, E, int(k), _ptr(ids), _ptr(w), _stream()), "rl_moe_route")
     return ids, w
 

@@ -1926,4 +1926,74 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blo
     }
 }
 
+// The MFMA operand decoders of the expert GEMMs (T1Dec8 on fp8 operands; Q2Dec16 on bf16 operands
+// for gate/up, F16 = false, or fp16 operands for down, F16 = true), run exactly as the matrix
+// kernels run them: the decoder tables built in LDS by GuTables, each block's window of dwords
+// (from the dword boundary at or below the block start) in LDS, strip_prep with the block's byte
+// misalignment, then every step's operands.  Lane (n, g) of a wave decodes lane group g's share of
+// block 16 * wave_index + n and writes d * operand to the k position the operand byte (T1) or
+// 16-bit half (Q2B) stands for (t1_kmap / q2_kmap).  d * operand is exact in fp32.
+template <int QT, bool F16>
+__global__ __launch_bounds__(256) void k_dequant_mfma(const uint8_t* __restrict__ base4, uint32_t mis,
+                                                      int64_t n_blocks, float* __restrict__ out) {
+    typedef GuTables<QT, F16> Tab;
+    typedef WinGeo<QT> G;
+    constexpr int WDW = G::WIN / 4;  // dwords per window
+    __shared__ __attribute__((aligned(32768))) uint64_t t64[Tab::N64];
+    __shared__ uint32_t tbl8[8];
+    __shared__ uint32_t win[4][16][WDW];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    Tab::build(t64, tbl8, tid, 256);
+    const GuShared sh = Tab::shared(nullptr, nullptr, nullptr, t64, tbl8, nullptr, nullptr);
+    const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 16;  // first block of this wave
+    // the range of dwords that hold bytes of the blocks (reads beyond it return 0, as the matrix
+    // kernels' windows past a matrix's last block do)
+    const uint64_t span = (uint64_t)mis + (uint64_t)n_blocks * Fmt<QT>::BYTES;
+    const BufSrc src(base4, (uint32_t)(span < 0xFFFFFFF0ull ? span : 0xFFFFFFF0ull));
+    for (int i = lane; i < 16 * WDW; i += 64) {
+        const int r = i / WDW, d = i % WDW;
+        const int64_t b = b0 + r;
+        uint32_t v = 0;
+        if (b < n_blocks) v = src.dw(((uint32_t)(mis + (uint64_t)b * Fmt<QT>::BYTES) & ~3u) + 4u * (uint32_t)d);
+        win[wave][r][d] = v;
+    }
+    __syncthreads();
+    const int64_t b = b0 + n;
+    if (b >= n_blocks) return;
+    const uint32_t m = (uint32_t)(mis + (uint64_t)b * Fmt<QT>::BYTES) & 3u;
+    T1Lane8 ln;
+    ln.init(g);
+    typename StripDec<QT>::type dec;
+    strip_prep<QT>(dec, win[wave][n], m, g, ln, sh);
+    float* o = out + b * 256;
+    if constexpr (QT == QT_T1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t op[8];
+            dec.step(h, ln, sh.tsel, op);
+#pragma unroll
+            for (int p = 0; p < 32; ++p)
+                o[t1_kmap(g, 32 * h + p)] = __builtin_amdgcn_cvt_f32_fp8((int)(op[p >> 2] >> (8 * (p & 3))), 0) * dec.d;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                uint32_t op[8];
+                dec.half(h, p, sh.qsel, op);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {  // dword q: operand 2p + q/4, values 2(q%4), 2(q%4)+1
+                    const int j = 2 * p + (q >> 2);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const uint32_t bits = (op[q] >> (16 * s)) & 0xFFFFu;
+                        const float v = F16 ? half_bits_to_float(bits) : __uint_as_float(bits << 16);
+                        o[q2_kmap(g, h, j, 2 * (q & 3) + s)] = v * dec.d;
+                    }
+                }
+            }
+    }
+}
+
 }  // namespace rl

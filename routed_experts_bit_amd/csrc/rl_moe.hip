@@ -28,14 +28,27 @@ struct Layout {
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
 
+// Largest byte extent of a buffer that the kernels address with 32-bit offsets (activation rows
+// of the gate/up and down GEMMs); their buffer resources span at most 0x7FFFFFF0 bytes.
+constexpr int64_t OFF32_LIMIT = (int64_t(1) << 31) - (int64_t(1) << 16);
+
 bool shape_ok(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     if (T < 0 || k < 1 || k > 16) return false;
     if (E < 1 || E > MAX_E) return false;
     if (H < 256 || H > 8192 || H % 256) return false;
     if (I < 64 || I > 4096 || I % 64) return false;
     if (!(I % 256 == 0 || I == 64 || I == 128)) return false;
-    if (T * (int64_t)k > (1 << 24)) return false;
+    const int64_t P = T * (int64_t)k;
+    if (P > (1 << 24)) return false;
+    // x rows (bf16, or split into hi/lo fp8: 2H bytes per token) and h rows (fp16, or split:
+    // 2I bytes per pair) are read through 32-bit buffer offsets
+    if (T * 2 * (int64_t)H > OFF32_LIMIT) return false;
+    if (P * 2 * (int64_t)I > OFF32_LIMIT) return false;
     return true;
+}
+
+inline uint64_t matrix_bytes(int qtype, int32_t H, int32_t I) {
+    return (uint64_t)H * (uint64_t)I / 256u * (uint64_t)(qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES);
 }
 
 Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
@@ -80,9 +93,16 @@ P* at(void* ws, size_t off) {
 }
 
 // Common validation of the layer entry points.  Fills `present[q]` with the number of
-// experts of type q (from the host copy of the descriptors).
-int check_layer(const void* x, const void* ids, const void* w, const rl_expert_blobs* ex, const void* out, int32_t T,
-                int32_t k, const void* ws, size_t ws_bytes, int present[3]) {
+// experts of type q (from the host copy of the descriptors).  The workspace is checked last
+// (check_ws), so that callers can check buffers of their own in between.
+int check_ws(const rl_expert_blobs* ex, int32_t T, int32_t k, const void* ws, size_t ws_bytes) {
+    if (!ws || ((uintptr_t)ws % ALIGN)) return RL_EWORKSPACE;
+    if (ws_bytes < layout(T, k, ex->E, ex->H, ex->I).total) return RL_EWORKSPACE;
+    return RL_OK;
+}
+
+int check_args(const void* x, const void* ids, const void* w, const rl_expert_blobs* ex, const void* out, int32_t T,
+               int32_t k, int present[3]) {
     if (!ex) return RL_EINVAL;
     if (!shape_ok(T, k, ex->E, ex->H, ex->I)) return RL_ESHAPE;
     if (T == 0) return RL_OK;
@@ -91,8 +111,6 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
     if (((uintptr_t)x | (uintptr_t)out) & 15) return RL_EINVAL;
     if (((uintptr_t)ids | (uintptr_t)w) & 3) return RL_EINVAL;
     if ((uintptr_t)ex->desc & 7) return RL_EINVAL;
-    if (!ws || ((uintptr_t)ws % ALIGN)) return RL_EWORKSPACE;
-    if (ws_bytes < layout(T, k, ex->E, ex->H, ex->I).total) return RL_EWORKSPACE;
     if ((uintptr_t)ex->arena & 3) return RL_EINVAL;
     present[0] = present[1] = present[2] = 0;
     for (int e = 0; e < ex->E; ++e) {
@@ -100,9 +118,21 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
         int q = dd.qtype;
         if (q != QT_Q2B && q != QT_T1) return RL_EQTYPE;
         if ((dd.gate_off | dd.up_off | dd.down_off) & 3) return RL_EINVAL;
+        // every matrix inside the arena (the kernels' reads stay inside its matrix's dwords)
+        const uint64_t mb = matrix_bytes(q, ex->H, ex->I);
+        const uint64_t offs[3] = {dd.gate_off, dd.up_off, dd.down_off};
+        for (uint64_t o : offs)
+            if (o > ex->arena_bytes || ex->arena_bytes - o < mb) return RL_EINVAL;
         present[q] += 1;
     }
     return RL_OK;
+}
+
+int check_layer(const void* x, const void* ids, const void* w, const rl_expert_blobs* ex, const void* out, int32_t T,
+                int32_t k, const void* ws, size_t ws_bytes, int present[3]) {
+    const int rc = check_args(x, ids, w, ex, out, T, k, present);
+    if (rc != RL_OK || T == 0) return rc;
+    return check_ws(ex, T, k, ws, ws_bytes);
 }
 
 // Pair grouping; with split != NULL the split of x runs in the histogram launch.
@@ -338,6 +368,10 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
 #undef RL_GV2
 }
 
+// The T1 gate/up kernel writes h already split into hi/lo fp8 rows for the fp8 down kernel that
+// holds a chunk's activations in LDS (I a multiple of 256, at most DN_KMAX).
+bool t1_splits_h(const int present[3], int32_t I) { return present[QT_T1] > 0 && I % 256 == 0 && I <= DN_KMAX; }
+
 // grouping + gate/up for every present type; returns the layout used.  With h8 (T1, I <= 512)
 // the T1 gate/up writes its h rows split for the fp8 down kernel (h8, with k-group scales hsc)
 // instead of fp16 rows of hdst.
@@ -421,7 +455,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     mark(0);
     Layout L2;  // same layout as L
     // T1 with I <= 512: gate/up writes h already split for the down kernel (no split of h)
-    const bool t1_hsplit_fused = present[QT_T1] && experts->I % 256 == 0 && experts->I <= DN_KMAX;
+    const bool t1_hsplit_fused = t1_splits_h(present, experts->I);
     uint8_t* h8 = at<uint8_t>(workspace, L.h8);
     uint32_t* hsc = at<uint32_t>(workspace, L.hscale);
     run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events,
@@ -500,12 +534,21 @@ int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float
 }
 
 int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
-                   uint16_t* h_out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
+                   uint16_t* h16_out, uint8_t* h8_out, uint32_t* hsc_out, int32_t T, int32_t k, void* workspace,
+                   size_t ws_bytes, void* stream) {
     int present[3] = {0, 0, 0};
-    int rc = check_layer(x, topk_ids, topk_w, experts, h_out, T, k, workspace, ws_bytes, present);
+    // validated with a stand-in for `out` (the hook has no layer output); the h buffers below
+    int rc = check_args(x, topk_ids, topk_w, experts, x, T, k, present);
     if (rc != RL_OK || T == 0) return rc;
+    const bool split = t1_splits_h(present, experts->I);
+    const bool need16 = present[QT_Q2B] > 0 || (present[QT_T1] > 0 && !split);
+    if (need16 && (!h16_out || ((uintptr_t)h16_out & 1))) return RL_EINVAL;
+    if (split && (!h8_out || !hsc_out || ((uintptr_t)hsc_out & 3))) return RL_EINVAL;
+    rc = check_ws(experts, T, k, workspace, ws_bytes);
+    if (rc != RL_OK) return rc;
     Layout L;
-    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, h_out, static_cast<hipStream_t>(stream), L);
+    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, h16_out, static_cast<hipStream_t>(stream), L,
+                     nullptr, split ? h8_out : nullptr, split ? hsc_out : nullptr);
     return hip_status();
 }
 
@@ -578,19 +621,36 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
     return hip_status();
 }
 
-int rl_moe_dequant(int32_t qtype, const void* blocks, int64_t n_values, float* out, void* stream) {
+int rl_moe_dequant(int32_t qtype, int32_t decoder, const void* blocks, int64_t n_values, float* out, void* stream) {
     if (qtype != QT_Q2B && qtype != QT_T1) return RL_EINVAL;
+    if (decoder < RL_DEC_STRIP || decoder > RL_DEC_MFMA_DOWN) return RL_EINVAL;
     if (n_values < 0 || n_values % 256) return RL_ESHAPE;
     if (n_values == 0) return RL_OK;
     if (!blocks || !out) return RL_EINVAL;
     const int64_t n_blocks = n_values / 256;
-    dim3 grid((unsigned)((n_blocks * 4 + 255) / 256));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t* b = static_cast<const uint8_t*>(blocks);
-    if (qtype == QT_Q2B)
-        hipLaunchKernelGGL(k_dequant<QT_Q2B>, grid, dim3(256), 0, s, b, n_blocks, out);
+    if (decoder == RL_DEC_STRIP) {
+        dim3 grid((unsigned)((n_blocks * 4 + 255) / 256));
+        if (qtype == QT_Q2B)
+            hipLaunchKernelGGL(k_dequant<QT_Q2B>, grid, dim3(256), 0, s, b, n_blocks, out);
+        else
+            hipLaunchKernelGGL(k_dequant<QT_T1>, grid, dim3(256), 0, s, b, n_blocks, out);
+        return hip_status();
+    }
+    // the blocks' bytes must be addressable by 32-bit buffer offsets from their dword base
+    const uint32_t mis = (uint32_t)((uintptr_t)b & 3u);
+    if ((uint64_t)mis + (uint64_t)n_blocks * (qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES) >
+        0xFFFFFFF0ull)
+        return RL_ESHAPE;
+    const uint8_t* b4 = b - mis;
+    dim3 grid((unsigned)((n_blocks + 63) / 64));  // 4 waves x 16 blocks per work-group
+    if (qtype == QT_T1)
+        hipLaunchKernelGGL((k_dequant_mfma<QT_T1, false>), grid, dim3(256), 0, s, b4, mis, n_blocks, out);
+    else if (decoder == RL_DEC_MFMA_GATEUP)
+        hipLaunchKernelGGL((k_dequant_mfma<QT_Q2B, false>), grid, dim3(256), 0, s, b4, mis, n_blocks, out);
     else
-        hipLaunchKernelGGL(k_dequant<QT_T1>, grid, dim3(256), 0, s, b, n_blocks, out);
+        hipLaunchKernelGGL((k_dequant_mfma<QT_Q2B, true>), grid, dim3(256), 0, s, b4, mis, n_blocks, out);
     return hip_status();
 }
 
