@@ -21,8 +21,9 @@
  * `out` is then untouched.  An expert id outside [0, E) is only seen on the device: it sets
  * bit 0 of the workspace status flags (read with rl_moe_status after the stream is synced);
  * such a token's output is then unspecified, every other token's is still correct.  The
- * per-pair down outputs are kept in fp16 (as h is): one beyond the fp16 range (|y| >= 65520)
- * sets bit 2 of the status flags, and its token's output is then infinite.
+ * per-pair down outputs y wait for the ordered combine in fp16 under a power-of-two scale per
+ * (pair, 64 columns) chosen from their own largest value, so every finite y is kept with fp16's
+ * 11 significant bits relative to that maximum (none overflows).
  */
 #ifndef RL_MOE_H
 #define RL_MOE_H
@@ -95,7 +96,8 @@ size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, in
  * Alignment (RL_EINVAL otherwise): x and out 16-byte aligned, topk_ids and topk_w 4-byte
  * aligned, experts->desc 8-byte aligned (rows of any T-row slice of such buffers stay aligned).
  * Launches: pair grouping, one fused dequant + gate/up + SwiGLU kernel per block type
- * present, one dequant + down kernel per type, the ordered combine.  Asynchronous. */
+ * present, one fused dequant + down kernel per type, the ordered combine (in selection order,
+ * so out does not depend on the order in which experts finish).  Asynchronous. */
 int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                    const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                    void* workspace, size_t ws_bytes, void* stream);

@@ -10,9 +10,10 @@
 //   k_q2_mm          Q2B experts on the 16-bit MFMA (16x16x32), same structure: gate/up on bf16 x,
 //                    down for I > 512 on fp16 h
 //   k_split          split of fp16 h into hi/lo fp8 rows for the T1 down kernel when I > 512
-//   k_t1_dn          T1 down for I <= 512, a chunk's split h rows held in LDS -> y (fp16)
-//   k_q2_dn          Q2B down for I <= 512, a chunk's fp16 h rows held in LDS -> y (fp16)
-//   k_down           both types with I < 256: decode + down on fp16 MFMA -> y (fp16)
+//   k_t1_dn          T1 down for I <= 512, a chunk's split h rows held in LDS -> y slots
+//   k_q2_dn          Q2B down for I <= 512, a chunk's fp16 h rows held in LDS -> y slots
+//   k_down           both types with I < 256: decode + down on fp16 MFMA -> y slots
+//                    (y: fp16 under a power-of-two scale per pair and 64 columns, y_store)
 //   k_combine        out_t = sum_j w[t][j] * y_{t,j}, j ascending (selection order)
 //   k_gv_gateup      1-2 row matrix-vector gate/up + SwiGLU (packed bf16 dot products)
 //   k_gv_down        1-2 row matrix-vector down + ordered combine in one dispatch
@@ -33,7 +34,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int FLAG_BAD_ID = 1;
 constexpr int FLAG_BAD_QTYPE = 2;
-constexpr int FLAG_Y_RANGE = 4;   // a per-pair down output beyond the fp16 range
 constexpr int FLAGS_WORDS = 64;   // flags[0] error bits; flags[8 + q] work-list length of type q
 constexpr int MAX_E = 1024;
 
@@ -51,16 +51,6 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// y (the per-pair down outputs, summed later by k_combine) is kept in fp16; a value that rounds
-// beyond the fp16 range marks the call's status flags.
-__device__ __forceinline__ uint16_t y_bits(float v, bool& ovf) {
-    ovf |= fabsf(v) >= 65520.0f;
-    return f32_to_f16_bits(v);
-}
-__device__ __forceinline__ void y_range_flag(bool ovf, int32_t* flags) {
-    if (__ballot(ovf) != 0ull && __lane_id() == 0) atomicOr(flags, FLAG_Y_RANGE);
-}
 
 // ---------------------------------------------------------------------------------------
 // Pair grouping: two kernels over tiles of GT consecutive flattened pairs p = t*k + j.
@@ -94,9 +84,17 @@ struct GroupArgs {
     int32_t* worklist;  // [2][E]
     ItemRec* items;     // [2][E], same order as worklist
     int32_t* tile_hist; // [ntiles][E]
+    u32x4* zero;        // the y scale bytes of the call, cleared by the first launch (may be NULL)
+    int nzero;          // 16-byte words
     int P, E, ntiles;
     int nflags;         // status words to clear
 };
+
+// cleared by every work-group of the grouping's first launch (which precedes the down kernels)
+__device__ __forceinline__ void clear_words(const GroupArgs& a) {
+    for (int i = blockIdx.x * GROUP_NTHR + threadIdx.x; i < a.nzero; i += gridDim.x * GROUP_NTHR)
+        a.zero[i] = u32x4{0u, 0u, 0u, 0u};
+}
 
 __device__ __forceinline__ void group_count_tile(const GroupArgs& a, int tile) {
     __shared__ int32_t h[MAX_E];
@@ -113,7 +111,10 @@ __device__ __forceinline__ void group_count_tile(const GroupArgs& a, int tile) {
     for (int e = tid; e < a.E; e += GROUP_NTHR) a.tile_hist[(size_t)tile * a.E + e] = h[e];
 }
 
-__global__ __launch_bounds__(GROUP_NTHR) void k_group_count(GroupArgs a) { group_count_tile(a, blockIdx.x); }
+__global__ __launch_bounds__(GROUP_NTHR) void k_group_count(GroupArgs a) {
+    clear_words(a);
+    group_count_tile(a, blockIdx.x);
+}
 
 __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     constexpr int NW = GROUP_NTHR / 64;
@@ -527,6 +528,8 @@ __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
 // work-groups [0, ntiles) count, the others split 256/LPR token rows each.
 template <int LPR, int NG>
 __global__ __launch_bounds__(256) void k_count_split(GroupArgs g, SplitArgs a) {
+    static_assert(GROUP_NTHR == 256, "one thread layout for both parts");
+    clear_words(g);
     if ((int)blockIdx.x < g.ntiles)
         group_count_tile(g, blockIdx.x);
     else
@@ -565,6 +568,22 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, const uint32_t* b, f32x4 c) {
 // the token pair_src[p] / k of each sorted pair p, weights gate and up [I][H], output h (fp16,
 // SwiGLU, sorted-pair rows).  Down: activations in sorted-pair rows, weights down [H][I], output
 // y (fp16, row = original pair index t*k + j).  K is the contracted length, N the output width.
+// Per-pair outputs y of the down GEMMs, kept for the ordered combine (k_combine): fp16 under a
+// power-of-two scale 2^sigma per (pair, 64-column tile).  sigma = 0 (fp16 as it is) unless a
+// value of the storing wave reaches 2^15; then every tile of that wave takes the sigma that puts
+// its own largest |y| in [2^14, 2^15), so no finite y overflows and each keeps fp16's 11
+// significant bits relative to its tile maximum.  The sigma bytes are zeroed by the grouping's
+// first launch and written only by the scaled stores.
+constexpr int CT = 64;          // columns per scale tile
+constexpr int Y_SPARE = 4096;   // waves of a down launch (each stores its padding rows apart)
+struct YSlots {
+    uint16_t* yslot;  // [P][H] fp16 bits, row t*k + j: y * 2^sigma
+    int8_t* yexp;     // [P][H/CT] sigma of each (pair, tile)
+    uint16_t* yspare; // [Y_SPARE][CT]: each wave's own target for its padding rows (never read)
+    int8_t* espare;   // [Y_SPARE]
+    int H, P;
+};
+
 enum { GU_GATEUP = 0, GU_DOWN = 1 };
 struct GuArgs {
     const uint8_t* act;       // [rows][2K bytes] activations (see above)
@@ -577,7 +596,7 @@ struct GuArgs {
     uint8_t* h8;              // T1 gate/up, I <= 512: h written here as hi/lo fp8 rows instead (null: hbuf)
     uint32_t* hsc;            // with h8, and read by the T1 down kernel: byte 2*kb + p of word r = E8M0
                               // scale of k-groups 2p, 2p+1 of block kb of h row r
-    uint16_t* yslot;          // down output [P+1][N] fp16
+    YSlots ys;                // down: the per-pair outputs
     int32_t* flags;           // status words (flags[0])
     int K, N, ns;
     int k;                    // pairs per token (gate/up: token of pair index q is q / k)
@@ -981,6 +1000,59 @@ __device__ __forceinline__ float row16_max(float x) {
     return x;
 }
 
+// ---------------------------------------------------------------------------------------
+// Down epilogue: a wave's tile of per-pair outputs y into the slots (YSlots).
+// yv[mt][t][i]: the wave's fp32 outputs, row r = 16*mt + 4*g + i of the chunk, column
+// col0 + 16*t + n (t < 4: one 64-column tile); dst(r) = the row's pair index t*k + j, or >= P
+// for a padding row, which is stored to the wave's own spare tile instead (never read; keeps
+// padding stores of different waves off each other's cache lines).  A wave issues at least
+// Y_STORE_OPS vector-memory stores per row tile (16 fp16 stores; the scaled case adds 4 sigma
+// stores), which callers count in their waits.
+constexpr int Y_STORE_OPS = 4 * 4;
+template <int MT, class Dst>
+__device__ __forceinline__ void y_store(const YSlots& c, float (&yv)[MT][4][4], Dst dst, int col0) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int ntile = c.H / CT, tile = col0 / CT;
+    const int wid = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // < Y_SPARE (host-checked)
+    float lm = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) lm = fmaxf(lm, fabsf(yv[mt][t][i]));
+    if (__ballot(lm >= 32768.0f) == 0ull) {  // every value fits fp16 as it is (sigma = 0)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = dst(16 * mt + 4 * g + i);
+                uint16_t* yr = d < c.P ? c.yslot + (size_t)d * c.H + col0 + n : c.yspare + (size_t)wid * CT + n;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) yr[16 * t] = f32_to_f16_bits(yv[mt][t][i]);
+            }
+        return;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = fmaxf(fmaxf(fabsf(yv[mt][0][i]), fabsf(yv[mt][1][i])), fmaxf(fabsf(yv[mt][2][i]), fabsf(yv[mt][3][i])));
+            m = row16_max(m);  // the 16 lanes of a DPP row hold the same rows
+            const int ex = m > 0.f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 : 14;  // floor(log2 m)
+            int sigma = 14 - ex;
+            sigma = sigma < -120 ? -120 : (sigma > 120 ? 120 : sigma);
+            const float sc = __uint_as_float((uint32_t)(127 + sigma) << 23);
+            const int d = dst(16 * mt + 4 * g + i);
+            const bool real = d < c.P;
+            uint16_t* yr = real ? c.yslot + (size_t)d * c.H + col0 + n : c.yspare + (size_t)wid * CT + n;
+            int8_t* ye = real ? c.yexp + (size_t)d * ntile + tile : c.espare + wid;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) yr[16 * t] = f32_to_f16_bits(yv[mt][t][i] * sc);
+            *ye = (int8_t)sigma;  // (the 16 lanes of a DPP row store the same byte)
+        }
+}
+
 template <int MT, int NTI, class Ch>
 __device__ __forceinline__ void t1_h_split_out(const GuArgs& a, const GuShared& sh, const Ch& ch, int pc, int rows,
                                                int colw, int wave, int n, int g) {
@@ -1066,7 +1138,7 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
     constexpr int NMAT = MODE == GU_GATEUP ? 2 : 1;
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
     float ps = 0.f;
-    int pdst = 0;
+    int pdst = a.P;  // padding rows: the spare tile
     auto hook = [&]() {
         if (has_next) {
 #pragma unroll
@@ -1101,16 +1173,27 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
             return;
         }
     }
-    bool ovf = false;
-    // lane holds rows 4g..4g+3 of each 16-row tile, column n
+    if constexpr (MODE == GU_DOWN) {
+        static_assert(MODE != GU_DOWN || NTI == 4, "a down wave covers one 64-column scale tile");
+        float yv[MT][4][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + 4 * g + i;
-            if (r < rows) {
-                const float xs = sh.rscale[r];
-                if constexpr (MODE == GU_GATEUP) {
+            for (int i = 0; i < 4; ++i) {
+                const float xs = sh.rscale[mt * 16 + 4 * g + i];  // 0 for padding rows
+#pragma unroll
+                for (int t = 0; t < 4; ++t) yv[mt][t][i] = ch.acc[mt][t][i] * ch.rs[t].dprev * xs;
+            }
+        y_store<MT>(a.ys, yv, [&](int r) { return sh.rdst[r]; }, colw);
+    } else {
+        // lane holds rows 4g..4g+3 of each 16-row tile, column n
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mt * 16 + 4 * g + i;
+                if (r < rows) {
+                    const float xs = sh.rscale[r];
 #pragma unroll
                     for (int ti = 0; ti < NTI; ++ti) {
                         const float gv = ch.acc[mt][ti][i] * ch.rs[ti].dprev * xs;
@@ -1118,14 +1201,9 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
                         const int hc = QT == QT_T1 ? t1_hcol(colw + 16 * ti + n, a.N) : colw + 16 * ti + n;
                         a.hbuf[(size_t)(pc + r) * a.N + hc] = f32_to_f16_bits(silu_fast(gv) * uv);
                     }
-                } else {
-                    uint16_t* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + colw + n;
-#pragma unroll
-                    for (int t = 0; t < NTI; ++t) yrow[16 * t] = y_bits(ch.acc[mt][t][i] * ch.rs[t].dprev * xs, ovf);
                 }
             }
-        }
-    if constexpr (MODE == GU_DOWN) y_range_flag(ovf, a.flags);
+    }
     // rscale and rdst are rewritten only after the next chunk's step barriers
 }
 
@@ -1296,12 +1374,13 @@ struct DnSweep {
         }
     }
     // windows of block kb: the wave's own loads, so a wait on its own counter suffices.  At the
-    // first block of a sweep the previous sweep's epilogue has issued exactly 16*MT y stores (and
-    // at most one flag atomic) after this sweep's windows: waiting down to 16*MT outstanding
-    // operations completes the windows without waiting for those stores.
+    // first block of a sweep the previous sweep's epilogue (y_store) has issued exactly
+    // Y_STORE_OPS * MT stores after this sweep's windows: waiting down to that many outstanding
+    // operations completes the windows without waiting for those stores.  (The first sweep of a
+    // chunk follows a full wait.)
     __device__ __forceinline__ void block_top(int kb) {
         if (kb == 0)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(16 * MT) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Y_STORE_OPS * MT) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const uint32_t blk = (uint32_t)kb * BB;
@@ -1371,18 +1450,16 @@ __device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, co
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sw.rw[mt] = rw[mt];
         sw.run();
-        // y rows of the tile (padding rows to the spare row)
-        bool ovf = false;
+        // y tile of the wave (padding rows: rdst = P)
+        static_assert(DN_NT == 4, "a down wave covers one 64-column scale tile");
+        float yv[MT][4][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = mt * 16 + 4 * g + i;
-                uint16_t* yrow = a.yslot + (size_t)sh.rdst[r] * a.N + col0 + n;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int t = 0; t < DN_NT; ++t) yrow[16 * t] = y_bits(sw.acc[mt][t][i] * sw.rs[t].dprev, ovf);
-            }
-        y_range_flag(ovf, a.flags);
+                for (int t = 0; t < DN_NT; ++t) yv[mt][t][i] = sw.acc[mt][t][i] * sw.rs[t].dprev;
+        y_store<MT>(a.ys, yv, [&](int r) { return sh.rdst[r]; }, col0);
         pf_have = true;
     }
 }
@@ -1497,7 +1574,7 @@ struct DownArgs {
     const int32_t* worklist;
     const int32_t* wl_len;
     int32_t* counters;
-    uint16_t* yslot;  // [T*k + 1][H] fp16, row t*k + j
+    YSlots ys;        // the per-pair outputs
     int32_t* flags;
     int H, I, ns;
 };
@@ -1581,7 +1658,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * CH::LDA];
     __shared__ DecodeTables<QT, true> tab;
     __shared__ int item_sh;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, wave = tid >> 6;
     tab.build(tid, NTHR);
     __syncthreads();
     const int n_ranks = uni(*a.wl_len);
@@ -1617,46 +1694,57 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
                 case 3: down_chunk<QT, LCH, NW, NTW, 3>(a, tab, As, srch, src, sx, col0, acc, rs); break;
                 default: down_chunk<QT, LCH, NW, NTW, 4>(a, tab, As, srch, src, sx, col0, acc, rs); break;
             }
-            bool ovf = false;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (mt < mtiles) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = mt * 16 + 4 * g + i;
-                        if (r < rows) {
-                            uint16_t* yrow = a.yslot + (size_t)a.pair_src[p0 + mc + r] * a.H + col0 + n;
-#pragma unroll
-                            for (int t = 0; t < NTW; ++t) yrow[16 * t] = y_bits(acc[mt][t][i] * rs[t].dprev, ovf);
-                        }
-                    }
-                }
+            // y tile of the wave
+            static_assert(NTW == 4, "a down wave covers one 64-column scale tile");
+            const int32_t* psrc = a.pair_src + p0 + mc;
+            auto dst = [&](int r) { return r < rows ? psrc[r] : a.ys.P; };
+#define RL_KD_EPI(MT_)                                                                  \
+    {                                                                                   \
+        float yv[MT_][4][4];                                                            \
+        for (int mt = 0; mt < MT_; ++mt)                                                \
+            for (int i = 0; i < 4; ++i)                                                 \
+                for (int t = 0; t < 4; ++t) yv[mt][t][i] = acc[mt][t][i] * rs[t].dprev; \
+        y_store<MT_>(a.ys, yv, dst, col0);                                              \
+    }
+            switch (mtiles) {
+                case 1: RL_KD_EPI(1); break;
+                case 2: RL_KD_EPI(2); break;
+                case 3: RL_KD_EPI(3); break;
+                default: RL_KD_EPI(4); break;
             }
-            y_range_flag(ovf, a.flags);
+#undef RL_KD_EPI
         }
     }
 }
 
-// out[t][c] = sum over j = 0..K-1 (ascending) of w[t][j] * y[t*K + j][c]; one work-group per
-// token, eight columns per thread (16-byte loads of fp16 y), one instance per K (1..16).
+// The ordered weighted combine (the MoE tail): out[t][c] = sum over j = 0..K-1, in selection
+// order, of w[t][j] * y_{t,j}[c], with y read from the slots (fp16 * 2^-sigma per 64-column
+// tile, exact in fp32).  One work-group per token, eight columns per thread (16-byte loads),
+// one instance per K (1..16).  A separate pass: the k outputs of a token come from k experts on
+// different XCDs, and making them visible to a last-arriving wave inside the down kernels costs
+// more than this pass (L2 writebacks or device-coherent stores per tile).
 template <int K>
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ yslot, const float* __restrict__ w,
-                                                 float* __restrict__ out, int H) {
-    const int t = blockIdx.x;
+__global__ __launch_bounds__(256) void k_combine(YSlots ys, const float* __restrict__ w, float* __restrict__ out) {
+    const int t = blockIdx.x, H = ys.H, ntile = H / CT;
     const float* wt = w + (size_t)t * K;
     for (int c = 8 * threadIdx.x; c < H; c += 8 * 256) {
         // the K rows' loads are all in flight before the first product
         u32x4 y[K];
+        int e[K];
 #pragma unroll
-        for (int j = 0; j < K; ++j) y[j] = *(const u32x4*)(yslot + ((size_t)t * K + j) * H + c);
+        for (int j = 0; j < K; ++j) {
+            y[j] = *(const u32x4*)(ys.yslot + ((size_t)t * K + j) * H + c);
+            e[j] = ys.yexp[((size_t)t * K + j) * ntile + c / CT];
+        }
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const float wj = wt[j];
+            const float s = __uint_as_float((uint32_t)(127 - e[j]) << 23);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __fmaf_rn(wj, half_bits_to_float(y[j][i] & 0xFFFFu), acc[2 * i]);
-                acc[2 * i + 1] = __fmaf_rn(wj, half_bits_to_float(y[j][i] >> 16), acc[2 * i + 1]);
+                acc[2 * i] = __fmaf_rn(wj, half_bits_to_float(y[j][i] & 0xFFFFu) * s, acc[2 * i]);
+                acc[2 * i + 1] = __fmaf_rn(wj, half_bits_to_float(y[j][i] >> 16) * s, acc[2 * i + 1]);
             }
         }
         f32x4* o = (f32x4*)(out + (size_t)t * H + c);

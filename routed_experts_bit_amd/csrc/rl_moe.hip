@@ -23,7 +23,8 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, total;
+    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, yexp, yspare,
+        total;
 };
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
@@ -79,8 +80,12 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + P * sizeof(float));
     L.hbuf = off;  // fp16 h of the prefill path, or fp32 h of the 1-2 row path
     off = align_up(off + P * (size_t)I * sizeof(float));
-    L.yslot = off;  // row t*k + j of each pair, plus a spare row for the padding rows of tiles
-    off = align_up(off + (P + 1) * (size_t)H * sizeof(uint16_t));
+    L.yslot = off;  // fp16 y * 2^sigma, row t*k + j of each pair
+    off = align_up(off + P * (size_t)H * sizeof(uint16_t));
+    L.yexp = off;  // sigma of each (pair, 64-column tile)
+    off = align_up(off + P * (size_t)(H / CT));
+    L.yspare = off;  // each down wave's target for its padding rows
+    off = align_up(off + (size_t)Y_SPARE * CT * sizeof(uint16_t) + Y_SPARE);
     L.total = off;
     return L;
 }
@@ -138,8 +143,11 @@ int check_layer(const void* x, const void* ids, const void* w, const rl_expert_b
 // Pair grouping; with split != NULL the split of x runs in the histogram launch.
 void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
                   int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, int32_t* tile_hist,
-                  ItemRec* items, hipStream_t s, const SplitArgs* split = nullptr) {
+                  ItemRec* items, hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr,
+                  size_t zero_bytes = 0) {
     GroupArgs g;
+    g.zero = static_cast<u32x4*>(zero);
+    g.nzero = zero != nullptr ? (int)(zero_bytes / 16) : 0;
     g.ids = ids;
     g.desc = desc;
     g.offsets = offsets;
@@ -205,6 +213,10 @@ int grid_cap(int grid, int n_experts, int ns) {
     const int items = ((n_experts + 7) / 8) * 8 * ns;
     return grid < items ? grid : items;
 }
+
+// Down launches (4 waves per work-group) give every wave its own spare y tile: at most
+// Y_SPARE / 4 work-groups (a multiple of 8; MI355X holds 512 of them at once).
+int down_grid(int grid) { return grid < Y_SPARE / 4 ? grid : Y_SPARE / 4; }
 
 // The LDS-window kernels of a block type (T1 on the fp8 MFMA, Q2B on the 16-bit MFMA).
 template <int QT, int MODE, int NTI>
@@ -278,48 +290,54 @@ void launch_hsplit(const GuArgs& a, int P, hipStream_t s) {
     sa.scale = const_cast<float*>(a.ascale);
     launch_split<SPLIT_H>(sa, s);
 }
+// Columns of H per work item of the LDS-held down kernel (I a multiple of 256, at most 512).
+int down_item_cols(int32_t H) { return H % 1024 == 0 ? 1024 : (H % 512 == 0 ? 512 : 256); }
+
 // Down on the LDS-window kernels (I a multiple of 256): for I <= 512 the activations are held in
 // LDS, items of up to 1024 columns; else 4 waves x 4 tiles = 256 output columns per item.
 template <int QT>
 void launch_down_mm(const GuArgs& a, int n_experts, hipStream_t s) {
     GuArgs b = a;
     if (a.K <= DN_KMAX) {
-        const int cw = a.N % 1024 == 0 ? 1024 : (a.N % 512 == 0 ? 512 : 256);
+        const int cw = down_item_cols(a.N);
         b.ns = a.N / cw;
         constexpr auto K = dn_kernel_of<QT>();
-        const int grid = grid_cap(resident_grid<K>(64 * GU_NW), n_experts, b.ns);
+        const int grid = down_grid(grid_cap(resident_grid<K>(64 * GU_NW), n_experts, b.ns));
         hipLaunchKernelGGL(K, dim3(grid), dim3(64 * GU_NW), 0, s, b);
         return;
     }
     b.ns = a.N / 256;
-    launch_mm<QT, GU_DOWN, 4>(b, n_experts, s);
+    constexpr auto K = mm_kernel<QT, GU_DOWN, 4>();
+    const int grid = down_grid(grid_cap(resident_grid<K>(64 * GU_NW), n_experts, b.ns));
+    hipLaunchKernelGGL(K, dim3(grid), dim3(64 * GU_NW), 0, s, b);
 }
 
 template <int QT>
 void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
+    // 4 waves x 4 strips of 16 columns: one 64-column combine tile per wave, 256 columns per item
     DownArgs b = a;
     b.ns = a.H / 256;
     if (a.I % 256 == 0) {
-        const int grid = grid_cap(resident_grid<k_down<QT, 256, 8, 2>>(512), n_experts, b.ns);
-        hipLaunchKernelGGL((k_down<QT, 256, 8, 2>), dim3(grid), dim3(512), 0, s, b);
+        const int grid = down_grid(grid_cap(resident_grid<k_down<QT, 256, 4, 4>>(256), n_experts, b.ns));
+        hipLaunchKernelGGL((k_down<QT, 256, 4, 4>), dim3(grid), dim3(256), 0, s, b);
     } else if (a.I == 128) {
-        const int grid = grid_cap(resident_grid<k_down<QT, 128, 8, 2>>(512), n_experts, b.ns);
-        hipLaunchKernelGGL((k_down<QT, 128, 8, 2>), dim3(grid), dim3(512), 0, s, b);
+        const int grid = down_grid(grid_cap(resident_grid<k_down<QT, 128, 4, 4>>(256), n_experts, b.ns));
+        hipLaunchKernelGGL((k_down<QT, 128, 4, 4>), dim3(grid), dim3(256), 0, s, b);
     } else {
-        const int grid = grid_cap(resident_grid<k_down<QT, 64, 8, 2>>(512), n_experts, b.ns);
-        hipLaunchKernelGGL((k_down<QT, 64, 8, 2>), dim3(grid), dim3(512), 0, s, b);
+        const int grid = down_grid(grid_cap(resident_grid<k_down<QT, 64, 4, 4>>(256), n_experts, b.ns));
+        hipLaunchKernelGGL((k_down<QT, 64, 4, 4>), dim3(grid), dim3(256), 0, s, b);
     }
 }
 
 // ordered combine, one kernel instance per k (1..16)
 template <int K>
-void launch_combine_k(const uint16_t* y, const float* w, float* out, int T, int H, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine<K>, dim3(T), dim3(256), 0, s, y, w, out, H);
+void launch_combine_k(const YSlots& ys, const float* w, float* out, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine<K>, dim3(T), dim3(256), 0, s, ys, w, out);
 }
-void launch_combine(const uint16_t* y, const float* w, float* out, int T, int k, int H, hipStream_t s) {
+void launch_combine(const YSlots& ys, const float* w, float* out, int T, int k, hipStream_t s) {
     switch (k) {
 #define RL_CB(K) \
-    case K: launch_combine_k<K>(y, w, out, T, H, s); break;
+    case K: launch_combine_k<K>(ys, w, out, T, s); break;
         RL_CB(1) RL_CB(2) RL_CB(3) RL_CB(4) RL_CB(5) RL_CB(6) RL_CB(7) RL_CB(8)
         RL_CB(9) RL_CB(10) RL_CB(11) RL_CB(12) RL_CB(13) RL_CB(14) RL_CB(15) RL_CB(16)
 #undef RL_CB
@@ -396,7 +414,8 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     sa.rows = T;
     sa.K = ex->H;
     launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
-                 at<int32_t>(ws, L.tile_hist), items, s, present[QT_T1] ? &sa : nullptr);
+                 at<int32_t>(ws, L.tile_hist), items, s, present[QT_T1] ? &sa : nullptr, at<void>(ws, L.yexp),
+                 L.yspare - L.yexp);
     mark(1);
     GuArgs b = {};
     b.pair_src = pair_src;
@@ -451,7 +470,13 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     int32_t* offsets = at<int32_t>(workspace, L.offsets);
     int32_t* pair_src = at<int32_t>(workspace, L.pair_src);
     int32_t* worklist = at<int32_t>(workspace, L.worklist);
-    uint16_t* yslot = at<uint16_t>(workspace, L.yslot);
+    YSlots ys;
+    ys.yslot = at<uint16_t>(workspace, L.yslot);
+    ys.yexp = at<int8_t>(workspace, L.yexp);
+    ys.yspare = at<uint16_t>(workspace, L.yspare);
+    ys.espare = at<int8_t>(workspace, L.yspare + (size_t)Y_SPARE * CT * sizeof(uint16_t));
+    ys.H = experts->H;
+    ys.P = T * k;
     mark(0);
     Layout L2;  // same layout as L
     // T1 with I <= 512: gate/up writes h already split for the down kernel (no split of h)
@@ -466,7 +491,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     d.desc = experts->desc;
     d.offsets = offsets;
     d.pair_src = pair_src;
-    d.yslot = yslot;
+    d.ys = ys;
     d.flags = flags;
     d.H = experts->H;
     d.I = experts->I;
@@ -478,7 +503,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     b.pair_src = pair_src;
     b.arena = d.arena;
     b.hbuf = hbuf;
-    b.yslot = yslot;
+    b.ys = ys;
     b.flags = flags;
     b.K = experts->I;
     b.N = experts->H;
@@ -514,7 +539,7 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
             launch_down_t<QT_T1>(d, present[q], s);
     }
     mark(4);
-    launch_combine(yslot, topk_w, out, T, k, experts->H, s);
+    launch_combine(ys, topk_w, out, T, k, s);
     mark(5);
     return hip_status();
 }
