@@ -41,6 +41,7 @@ extern "C" {
 #define RL_EWORKSPACE (-3) /* workspace NULL, too small, or not 256-byte aligned */
 #define RL_EHIP (-4)       /* the HIP runtime reported an error at launch */
 #define RL_EQTYPE (-5)     /* the host descriptor copy names an unknown block type */
+#define RL_ETOOBIG (-6)    /* the call needs more scratch than the library's static buffer holds */
 
 /* Block types.  Both use 256-value blocks that tile a matrix flattened row-major; rows are
  * output features, the input dimension is contiguous.
@@ -113,6 +114,26 @@ int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk
 int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                          const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                          void* workspace, size_t ws_bytes, void* stream, void* const* events);
+
+/* rl_moe_prefill for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): no workspace argument; the library
+ * uses a static device buffer of RL_NOALLOC_SCRATCH_BYTES (40 MiB) that each GPU it runs on holds
+ * until the process ends, in place of the workspace.  The call itself allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine); its first call on a device looks up that
+ * device's copy of the buffer (hipGetSymbolAddress, once per device).  Sizes whose workspace
+ * (rl_moe_workspace_bytes) exceeds the buffer are RL_ETOOBIG before any launch: 40 MiB holds a
+ * 512-token call of a 512-expert, top-10, H 2048, I 512 layer.  Every call on one GPU shares its
+ * buffer: calls that may overlap on one GPU (other streams, other threads) race and must not be
+ * made; a call sets up everything it reads from the buffer, so consecutive calls are
+ * independent.  The status flags (rl_moe_status) live in the buffer: read them with
+ * rl_moe_noalloc_status.  Other arguments, results and errors as rl_moe_prefill. */
+#define RL_NOALLOC_SCRATCH_BYTES (40u << 20)
+int rl_moe_prefill_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                           const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* stream);
+
+/* Status flags of the last rl_moe_prefill_noalloc on the current device (after the stream is
+ * synced), as rl_moe_status; RL_EHIP if the buffer was never used on this device. */
+int rl_moe_noalloc_status(int32_t* flags_out);
 
 /* The same layer for 1 or 2 rows (decode and 2-row verify; dev75 "Decode", dev72 "2-row
  * verify"): matrix-vector kernels, gate/up + SwiGLU then down + the ordered combine in one

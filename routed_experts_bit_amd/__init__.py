@@ -22,6 +22,9 @@ from ._binding import (  # noqa: F401
     alloc_workspace,
     prefill,
     prefill_timed,
+    prefill_noalloc,
+    noalloc_status,
+    NOALLOC_SCRATCH_BYTES,
     TIMED_EVENTS,
     decode,
     gate_up,

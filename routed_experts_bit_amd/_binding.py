@@ -29,7 +29,10 @@ EXPORTS = (
     "rl_moe_route",
     "rl_moe_status",
     "rl_moe_strerror",
+    "rl_moe_prefill_noalloc",
+    "rl_moe_noalloc_status",
 )
+NOALLOC_SCRATCH_BYTES = 40 << 20  # RL_NOALLOC_SCRATCH_BYTES
 
 
 class RlError(RuntimeError):
@@ -72,6 +75,10 @@ def lib():
         getattr(L, name).restype = C.c_int
     L.rl_moe_gate_up.argtypes = [P, P, P, C.POINTER(_Blobs), P, P, P, I32, I32, P, SZ, P]
     L.rl_moe_gate_up.restype = C.c_int
+    L.rl_moe_prefill_noalloc.argtypes = [P, P, P, C.POINTER(_Blobs), P, I32, I32, P]
+    L.rl_moe_prefill_noalloc.restype = C.c_int
+    L.rl_moe_noalloc_status.argtypes = [P]
+    L.rl_moe_noalloc_status.restype = C.c_int
     L.rl_moe_prefill_timed.argtypes = layer + [C.POINTER(C.c_void_p)]
     L.rl_moe_prefill_timed.restype = C.c_int
     L.rl_moe_group_pairs.argtypes = [P, I32, I32, I32, P, P, P, P, SZ, P]
@@ -263,6 +270,31 @@ def prefill(x, ids, w, ex: DeviceExperts, out=None, ws=None):
     _check_layer_args(x, ids, w, ex, out, ws)
     _check(_layer(lib().rl_moe_prefill, x, ids, w, ex, out, ws), "rl_moe_prefill")
     return out
+
+
+def prefill_noalloc(x, ids, w, ex: DeviceExperts, out):
+    """rl_moe_prefill_noalloc: the layer into `out` (float32 [T, H], caller-allocated) with the
+    library's static scratch in place of a workspace; nothing is allocated."""
+    torch = _torch()
+    _need("topk_ids", ids, (torch.int32,), (None, None))
+    T, k = ids.shape
+    d = _dt()
+    dev = ids.device
+    _need("x", x, d["x"], (T, ex.H), dev)
+    _need("topk_w", w, d["w"], (T, k), dev)
+    _need("out", out, d["out"], (T, ex.H), dev)
+    rc = lib().rl_moe_prefill_noalloc(_ptr(x), _ptr(ids), _ptr(w), ex.blobs, _ptr(out), T, k, _stream())
+    _check(rc, "rl_moe_prefill_noalloc")
+    return out
+
+
+def noalloc_status():
+    """Status flags of the last rl_moe_prefill_noalloc on the current device (synchronises)."""
+    torch = _torch()
+    torch.cuda.current_stream().synchronize()
+    buf = (C.c_int32 * 4)()
+    _check(lib().rl_moe_noalloc_status(C.cast(buf, C.c_void_p)), "rl_moe_noalloc_status")
+    return list(buf)
 
 
 TIMED_EVENTS = 6  # RL_TIMED_EVENTS

@@ -10,14 +10,40 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "rl_kernels.h"
 #include "rl_route.h"
 #include "rl_moe.h"
 
+// Workspace of rl_moe_prefill_noalloc: one copy per device, held for the life of the process.
+// Host code never uses this name as an address: each device's address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[RL_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace rl;
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current) and kept; nullptr if the runtime reports an error.
+constexpr int NOALLOC_MAXDEV = 64;
+std::atomic<void*> g_scratch[NOALLOC_MAXDEV];
+std::mutex g_scratch_mu;
+
+void* noalloc_scratch(bool lookup) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAXDEV) return nullptr;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p != nullptr || !lookup) return p;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
@@ -549,6 +575,24 @@ int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk
     return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, stream, nullptr);
 }
 
+int rl_moe_prefill_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                           const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* stream) {
+    int present[3] = {0, 0, 0};
+    int rc = check_args(x, topk_ids, topk_w, experts, out, T, k, present);
+    if (rc != RL_OK || T == 0) return rc;
+    if (layout(T, k, experts->E, experts->H, experts->I).total > RL_NOALLOC_SCRATCH_BYTES) return RL_ETOOBIG;
+    void* ws = noalloc_scratch(true);
+    if (ws == nullptr) return RL_EHIP;
+    return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, ws, RL_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
+
+int rl_moe_noalloc_status(int32_t* flags_out) {
+    if (!flags_out) return RL_EINVAL;
+    void* ws = noalloc_scratch(false);
+    if (ws == nullptr) return RL_EHIP;
+    return rl_moe_status(ws, flags_out);
+}
+
 int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                          const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* workspace,
                          size_t ws_bytes, void* stream, void* const* events) {
@@ -693,6 +737,7 @@ const char* rl_moe_strerror(int status) {
         case RL_EWORKSPACE: return "workspace missing, misaligned or too small";
         case RL_EHIP: return "HIP runtime error at launch";
         case RL_EQTYPE: return "unknown block type in the expert descriptors";
+        case RL_ETOOBIG: return "the call needs more scratch than the no-allocation buffer holds";
         default: return "unknown status";
     }
 }

@@ -270,3 +270,24 @@ def test_binding_checks_descriptors_against_arena():
         _check_descriptors(d, ex.E, ex.H, ex.I, ex.arena.size)
     with pytest.raises(rl.RlError, match="records"):
         _check_descriptors(ex.desc[:2], ex.E, ex.H, ex.I, ex.arena.size)
+
+
+def test_noalloc_codes(L):
+    """rl_moe_prefill_noalloc validates like rl_moe_prefill and refuses, before any launch, a call
+    whose workspace exceeds its static buffer (RL_ETOOBIG)."""
+    import routed_experts_bit_amd as rl
+
+    RL_ESHAPE, RL_EINVAL, RL_ETOOBIG = -2, -1, -6
+    v = C.c_void_p
+    b, _ = _blobs(E=512, H=2048, I=512, qtype=2)
+
+    def call(T, k, x=0x100, out=0x400):
+        return L.rl_moe_prefill_noalloc(v(x), v(0x200), v(0x300), C.byref(b), v(out), T, k, None)
+
+    assert L.rl_moe_workspace_bytes(1024, 10, 512, 2048, 512) > rl.NOALLOC_SCRATCH_BYTES
+    assert L.rl_moe_workspace_bytes(512, 10, 512, 2048, 512) <= rl.NOALLOC_SCRATCH_BYTES
+    assert call(1024, 10) == RL_ETOOBIG
+    assert call(4, 17) == RL_ESHAPE
+    assert call(4, 10, x=0) == RL_EINVAL
+    assert call(0, 10, x=0, out=0) == 0
+    assert "scratch" in rl.strerror(RL_ETOOBIG)
