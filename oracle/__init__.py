@@ -13,5 +13,7 @@ from .oracle import (  # noqa: F401
     group_pairs,
     moe_prefill,
     moe_workload,
+    moe_block,
+    default_threads,
     route,
 )

@@ -64,6 +64,9 @@ def load():
     lib.orc_moe_prefill.argtypes = [P, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P,
                                     C.c_int]
     lib.orc_moe_prefill.restype = C.c_int
+    lib.orc_moe_block.argtypes = [P, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P,
+                                  C.c_int, P, C.c_int]
+    lib.orc_moe_block.restype = C.c_int
     lib.orc_route.argtypes = [P, C.c_int, C.c_int, C.c_int, P, P]
     lib.orc_route.restype = C.c_int
     _lib = lib
@@ -134,6 +137,29 @@ def moe_prefill(x, ids, w, arena, desc, E, H, I, tokens=None, want_h=False, thre
     if rc:
         raise ValueError(f"orc_moe_prefill failed ({rc})")
     return (out[:n], h[:n] if h is not None else None) if want_h else out[:n]
+
+
+def moe_block(x, ids, w, arena, desc, E, H, I, shared, shared_gate, residual=None, tokens=None, threads=None):
+    """The MoE block (orc_moe_block): routed sum in selection order, then the shared expert
+    `shared` weighted by shared_gate[t], then the residual [T, H] (None: none); float64 [n, H].
+    ids / w may have k = 0 columns."""
+    lib = load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    arena = np.ascontiguousarray(arena, dtype=np.uint8)
+    desc = np.ascontiguousarray(desc)
+    g = np.ascontiguousarray(shared_gate, dtype=np.float32)
+    res = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32)
+    T, k = ids.shape
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    out = np.empty((max(tok.size, 1), H), np.float64)
+    rc = lib.orc_moe_block(_ptr(x), _ptr(ids) if ids.size else None, _ptr(w) if w.size else None, _ptr(arena),
+                           _ptr(desc), E, H, I, T, k, int(shared), _ptr(g), _ptr(res) if res is not None else None,
+                           _ptr(tok), tok.size, _ptr(out), int(threads or default_threads()))
+    if rc:
+        raise ValueError(f"orc_moe_block failed ({rc})")
+    return out[: tok.size]
 
 
 def moe_workload(wl, tokens=None, want_h=False, threads=None):

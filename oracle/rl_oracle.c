@@ -331,6 +331,50 @@ int orc_moe_prefill(const uint16_t* x, const int32_t* ids, const float* w, const
     return 0;
 }
 
+/* ---------------------------------------------------------------- the MoE block: shared expert, residual */
+
+/* The MoE block around the routed experts (Red Lite dev75, "Prompt ingestion": the prefill
+ * profile lists the shared expert beside the routed experts; the block's output joins the
+ * residual stream):
+ *   out_t = ((sum over j = 0..k-1, in selection order, of w[t][j] * y_{t,j}) + g_t * s_t) + r_t
+ * where s_t = Wd_s (silu(Wg_s x_t) * (Wu_s x_t)) is the shared expert, a dense SwiGLU FFN of the
+ * same shapes stored like the routed ones (descriptor `shared` of desc[E]), g_t = shared_gate[t]
+ * (the caller's per-token gate of the shared expert), r_t = residual[t] (NULL: no residual).  The
+ * shared term is one more term of the same ordered sum, taken after the routed ones; k may be 0
+ * (the shared expert alone).  Arguments otherwise as orc_moe_prefill.  Returns as
+ * orc_moe_prefill, and -1 for a `shared` outside [0, E). */
+int orc_moe_block(const uint16_t* x, const int32_t* ids, const float* w, const uint8_t* arena, const orc_desc* desc,
+                  int E, int H, int I, int T, int k, int shared, const float* shared_gate, const float* residual,
+                  const int32_t* tokens, int n_tokens, double* out, int nthreads) {
+    if (T < 0 || k < 0 || shared < 0 || shared >= E || !shared_gate) return -1;
+    const int k1 = k + 1;
+    int32_t* ids1 = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * k1);
+    float* w1 = (float*)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * k1);
+    if (!ids1 || !w1) {
+        free(ids1);
+        free(w1);
+        return -3;
+    }
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            ids1[(int64_t)t * k1 + j] = ids[(int64_t)t * k + j];
+            w1[(int64_t)t * k1 + j] = w[(int64_t)t * k + j];
+        }
+        ids1[(int64_t)t * k1 + k] = shared;
+        w1[(int64_t)t * k1 + k] = shared_gate[t];
+    }
+    int rc = orc_moe_prefill(x, ids1, w1, arena, desc, E, H, I, T, k1, tokens, n_tokens, out, NULL, nthreads);
+    free(ids1);
+    free(w1);
+    if (rc || !residual) return rc;
+    const int n = tokens ? n_tokens : T;
+    for (int ti = 0; ti < n; ++ti) {
+        const int t = tokens ? tokens[ti] : ti;
+        for (int c = 0; c < H; ++c) out[(int64_t)ti * H + c] += (double)residual[(int64_t)t * H + c];
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- router (the step before the path) */
 
 /* Router of one layer (reading of the MoE routing the pages take as given: softmax over the
