@@ -103,6 +103,25 @@ int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk
                    const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* The MoE block around the routed experts (dev75 "Prompt ingestion": the prefill profile lists
+ * the shared expert beside the routed ones; the block's output joins the residual stream):
+ *     out_t = ((sum_{j=0..k-1} topk_w[t][j] * y_{t,j}) + shared_gate[t] * s_t) + residual[t]
+ * in that order, where s_t = Wd_s (silu(Wg_s x_t) * (Wu_s x_t)) is the shared expert: descriptor
+ * `shared_expert` of experts (a dense SwiGLU FFN of the same shapes and block formats as the
+ * routed experts; topk_ids may name it too).  The shared expert runs as one more pair of every
+ * token, through the same grouping, GEMMs and ordered combine, summed after the routed pairs.
+ *   shared_expert  in [0, E) (RL_EINVAL otherwise)
+ *   shared_gate    [dev] float [T]: the per-token weight of the shared expert (the caller's gate,
+ *                  e.g. a sigmoid of a projection of x), 4-byte aligned
+ *   residual       [dev] float [T][H] or NULL (no residual), 16-byte aligned
+ *   k in [0, 15] (k = 0: the shared expert alone; topk_ids / topk_w may then be NULL)
+ *   workspace      at least rl_moe_workspace_bytes(T, k + 1, E, H, I) bytes
+ * Other arguments, errors and launches as rl_moe_prefill. */
+int rl_moe_prefill_block(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                         const rl_expert_blobs* experts, int32_t shared_expert, const float* shared_gate,
+                         const float* residual, float* out, int32_t T, int32_t k, void* workspace,
+                         size_t ws_bytes, void* stream);
+
 /* Measurement hook: rl_moe_prefill with RL_TIMED_EVENTS events (events [host] array of
  * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels (whose
  * first launch also splits x for the T1 path), 1 after them, 2 after the gate/up kernel(s), 3

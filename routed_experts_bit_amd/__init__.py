@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     prefill,
     prefill_timed,
     prefill_noalloc,
+    prefill_block,
     noalloc_status,
     NOALLOC_SCRATCH_BYTES,
     TIMED_EVENTS,

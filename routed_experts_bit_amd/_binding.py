@@ -31,6 +31,7 @@ EXPORTS = (
     "rl_moe_strerror",
     "rl_moe_prefill_noalloc",
     "rl_moe_noalloc_status",
+    "rl_moe_prefill_block",
 )
 NOALLOC_SCRATCH_BYTES = 40 << 20  # RL_NOALLOC_SCRATCH_BYTES
 
@@ -75,6 +76,8 @@ def lib():
         getattr(L, name).restype = C.c_int
     L.rl_moe_gate_up.argtypes = [P, P, P, C.POINTER(_Blobs), P, P, P, I32, I32, P, SZ, P]
     L.rl_moe_gate_up.restype = C.c_int
+    L.rl_moe_prefill_block.argtypes = [P, P, P, C.POINTER(_Blobs), I32, P, P, P, I32, I32, P, SZ, P]
+    L.rl_moe_prefill_block.restype = C.c_int
     L.rl_moe_prefill_noalloc.argtypes = [P, P, P, C.POINTER(_Blobs), P, I32, I32, P]
     L.rl_moe_prefill_noalloc.restype = C.c_int
     L.rl_moe_noalloc_status.argtypes = [P]
@@ -269,6 +272,32 @@ def prefill(x, ids, w, ex: DeviceExperts, out=None, ws=None):
         ws = alloc_workspace(T, ids.shape[1], ex, device=ids.device)
     _check_layer_args(x, ids, w, ex, out, ws)
     _check(_layer(lib().rl_moe_prefill, x, ids, w, ex, out, ws), "rl_moe_prefill")
+    return out
+
+
+def prefill_block(x, ids, w, ex: DeviceExperts, shared: int, gate, residual=None, out=None, ws=None):
+    """The MoE block (rl_moe_prefill_block): routed experts in selection order, then the shared
+    expert `shared` (a descriptor index) weighted by gate float32 [T], then residual float32 [T, H]
+    (None: none).  ids int32 [T, k] / w float32 [T, k] may have k = 0 columns."""
+    torch = _torch()
+    _need("topk_ids", ids, (torch.int32,), (None, None))
+    T, k = ids.shape
+    dev = ids.device
+    d = _dt()
+    _need("x", x, d["x"], (T, ex.H), dev)
+    _need("topk_w", w, d["w"], (T, k), dev)
+    _need("shared_gate", gate, (torch.float32,), (T,), dev)
+    if residual is not None:
+        _need("residual", residual, (torch.float32,), (T, ex.H), dev)
+    if out is None:
+        out = torch.empty((T, ex.H), dtype=torch.float32, device=dev)
+    _need("out", out, d["out"], (T, ex.H), dev)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(max(T, 1), k + 1, ex.E, ex.H, ex.I), dtype=torch.uint8, device=dev)
+    _need("workspace", ws, d["ws"], (None,), dev)
+    rc = lib().rl_moe_prefill_block(_ptr(x), _ptr(ids) if k else None, _ptr(w) if k else None, ex.blobs, int(shared),
+                                    _ptr(gate), _ptr(residual), _ptr(out), T, k, _ptr(ws), ws.numel(), _stream())
+    _check(rc, "rl_moe_prefill_block")
     return out
 
 

@@ -74,15 +74,34 @@ struct ItemRec {
     uint64_t off[3];
 };
 
+// Pairs of a call: token t, selection j < kk.  Selections j < kin are the caller's topk_ids
+// (row stride kin); with a shared expert (shared >= 0) the last selection of every token is that
+// expert, so the shared expert's pairs run through the same grouping, GEMMs and ordered combine.
+struct PairIds {
+    const int32_t* ids;  // [T][kin]
+    int kin, kk, shared;
+    __device__ __forceinline__ int expert(int p) const {
+        if (shared < 0) return ids[p];
+        const int t = p / kk, j = p - t * kk;
+        return j < kin ? ids[t * kin + j] : shared;
+    }
+};
+
+// Work records: an expert's pairs are cut into records of at most REC_PAIRS sorted pairs (one
+// gate/up chunk), so that a hot expert (the shared expert has a pair for every token) is spread
+// over many work items.
+constexpr int REC_PAIRS = 64;
+__host__ __device__ constexpr int max_records(int E, int P) { return E + (P + REC_PAIRS - 1) / REC_PAIRS; }
+
 struct GroupArgs {
-    const int32_t* ids;
+    PairIds pid;
     const rl_expert_desc* desc;  // may be NULL: no work lists
     int32_t* offsets;
     int32_t* pair_src;
     int32_t* inv;
     int32_t* flags;
-    int32_t* worklist;  // [2][E]
-    ItemRec* items;     // [2][E], same order as worklist
+    ItemRec* items;     // [2][maxrec]: per block type, records longest first
+    int maxrec;
     int32_t* tile_hist; // [ntiles][E]
     u32x4* zero;        // the y scale bytes of the call, cleared by the first launch (may be NULL)
     int nzero;          // 16-byte words
@@ -104,7 +123,7 @@ __device__ __forceinline__ void group_count_tile(const GroupArgs& a, int tile) {
     __syncthreads();
     const int p0 = tile * GT, p1 = min(a.P, p0 + GT);
     for (int p = p0 + tid; p < p1; p += GROUP_NTHR) {
-        const int e = a.ids[p];
+        const int e = a.pid.expert(p);
         if (e >= 0 && e < a.E) atomicAdd(&h[e], 1);
     }
     __syncthreads();
@@ -143,7 +162,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
         }
     }
     if (tid == 0) bad_sh = 0;
-    for (int i = tid; i < GT; i += GROUP_NTHR) ids_sh[i] = i < n ? a.ids[p0 + i] : -1;
+    for (int i = tid; i < GT; i += GROUP_NTHR) ids_sh[i] = i < n ? a.pid.expert(p0 + i) : -1;
     {
         // pairs of each expert in earlier tiles and in all tiles; the histogram loads are issued
         // HB tiles at a time so that their latencies overlap
@@ -252,8 +271,10 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     __syncthreads();
     if (tid == 0 && bad_sh) atomicOr(&a.flags[0], FLAG_BAD_ID);
 
-    // per-type work lists, binned by pair count
+    // per-type work lists of records (at most REC_PAIRS pairs each), binned by record size,
+    // larger records first
     if (lister && a.desc != nullptr) {
+        static_assert(REC_PAIRS < NBIN, "record sizes are bins");
         for (int i = tid; i < 2 * NBIN; i += GROUP_NTHR) (&bins[0][0])[i] = 0;
         __syncthreads();
 #pragma unroll
@@ -261,15 +282,13 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             const int e = tid + GROUP_NTHR * i;
             if (e >= E) continue;
             const int q = dl[i].qtype, c = tot[e];
-            before[e] = -1;  // reused: list bin of e
             if (c == 0) continue;
             if (q != QT_Q2B && q != QT_T1) {
                 atomicOr(&bad_sh, 2);
                 continue;
             }
-            const int b = c < NBIN - 1 ? c : NBIN - 1;
-            before[e] = (q - 1) * NBIN + b;
-            atomicAdd(&bins[q - 1][b], 1);
+            if (c >= REC_PAIRS) atomicAdd(&bins[q - 1][REC_PAIRS], c / REC_PAIRS);
+            if (c % REC_PAIRS) atomicAdd(&bins[q - 1][c % REC_PAIRS], 1);
         }
         __syncthreads();
         if (tid < 128) {  // start of each bin in the type's list, high counts first: wave q scans type q
@@ -300,18 +319,19 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
         for (int i = 0; i < EPL; ++i) {
             const int e = tid + GROUP_NTHR * i;
             if (e >= E) continue;
-            const int key = before[e];
-            if (key < 0) continue;
-            const int q0 = key / NBIN, b = key % NBIN;
-            const int pos = q0 * E + atomicAdd(&bins[q0][b], 1);
-            a.worklist[pos] = e;
+            const int q = dl[i].qtype, c = tot[e];
+            if (c == 0 || (q != QT_Q2B && q != QT_T1)) continue;
             ItemRec r;
-            r.p0 = scan[e] - tot[e];
-            r.ne = tot[e];
             r.off[0] = dl[i].gate_off;
             r.off[1] = dl[i].up_off;
             r.off[2] = dl[i].down_off;
-            a.items[pos] = r;
+            const int first = scan[e] - c;
+            for (int p = 0; p < c; p += REC_PAIRS) {
+                const int sz = min(REC_PAIRS, c - p);
+                r.p0 = first + p;
+                r.ne = sz;
+                a.items[(size_t)(q - 1) * a.maxrec + atomicAdd(&bins[q - 1][sz], 1)] = r;
+            }
         }
         __syncthreads();
         if (tid == 0 && (bad_sh & 2)) atomicOr(&a.flags[0], FLAG_BAD_QTYPE);
@@ -1568,10 +1588,8 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_q2_dn(GuArgs a) { dn_kernel<Q
 struct DownArgs {
     const uint16_t* hbuf;  // [P][I] fp16, sorted-pair order
     const uint8_t* arena;
-    const rl_expert_desc* desc;
-    const int32_t* offsets;
     const int32_t* pair_src;
-    const int32_t* worklist;
+    const ItemRec* items;  // this type's work records
     const int32_t* wl_len;
     int32_t* counters;
     YSlots ys;        // the per-pair outputs
@@ -1666,9 +1684,9 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
     const BufSrc srch(a.hbuf, 0x7FFFFFF0u);
     int rank, slice;
     while (next_item(a.counters, a.ns, n_ranks, &item_sh, rank, slice)) {
-        const int e = uni(a.worklist[rank]);
-        const int p0 = uni(a.offsets[e]), ne = uni(a.offsets[e + 1]) - p0;
-        const BufSrc src(a.arena + uni64(a.desc[e].down_off), mat_bytes);
+        const ItemRec rec = load_item(a.items, rank);
+        const int p0 = rec.p0, ne = rec.ne;
+        const BufSrc src(a.arena + rec.off[2], mat_bytes);
         const int col0 = slice * (16 * NTW * NW) + wave * (16 * NTW);
 
         for (int mc = 0; mc < ne; mc += 64) {
@@ -1717,16 +1735,30 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void k_down(DownArgs a) {
     }
 }
 
+// Weights of the ordered combine: selection j < kin of token t weighs w[t*kin + j]; with a shared
+// expert (gate != NULL) the last selection (j = kin) weighs gate[t]; res (may be NULL) is added
+// after the whole sum.
+struct CombineW {
+    const float* w;     // [T][kin]
+    const float* gate;  // [T] or NULL
+    const float* res;   // [T][H] or NULL
+    int kin;
+};
+
 // The ordered weighted combine (the MoE tail): out[t][c] = sum over j = 0..K-1, in selection
-// order, of w[t][j] * y_{t,j}[c], with y read from the slots (fp16 * 2^-sigma per 64-column
-// tile, exact in fp32).  One work-group per token, eight columns per thread (16-byte loads),
-// one instance per K (1..16).  A separate pass: the k outputs of a token come from k experts on
-// different XCDs, and making them visible to a last-arriving wave inside the down kernels costs
-// more than this pass (L2 writebacks or device-coherent stores per tile).
+// order, of weight(t, j) * y_{t,j}[c] (then + res[t][c]), with y read from the slots (fp16 *
+// 2^-sigma per 64-column tile, exact in fp32).  One work-group per token, eight columns per thread
+// (16-byte loads), one instance per K (1..16 pairs per token).  A separate pass: the K outputs of
+// a token come from K experts on different XCDs, and making them visible to a last-arriving wave
+// inside the down kernels costs more than this pass (L2 writebacks or device-coherent stores per
+// tile).
 template <int K>
-__global__ __launch_bounds__(256) void k_combine(YSlots ys, const float* __restrict__ w, float* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_combine(YSlots ys, CombineW cw, float* __restrict__ out) {
     const int t = blockIdx.x, H = ys.H, ntile = H / CT;
-    const float* wt = w + (size_t)t * K;
+    float wt[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        wt[j] = (cw.gate != nullptr && j == K - 1) ? cw.gate[t] : cw.w[(size_t)t * cw.kin + j];
     for (int c = 8 * threadIdx.x; c < H; c += 8 * 256) {
         // the K rows' loads are all in flight before the first product
         u32x4 y[K];
@@ -1739,12 +1771,20 @@ __global__ __launch_bounds__(256) void k_combine(YSlots ys, const float* __restr
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            const float wj = wt[j];
             const float s = __uint_as_float((uint32_t)(127 - e[j]) << 23);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __fmaf_rn(wj, half_bits_to_float(y[j][i] & 0xFFFFu) * s, acc[2 * i]);
-                acc[2 * i + 1] = __fmaf_rn(wj, half_bits_to_float(y[j][i] >> 16) * s, acc[2 * i + 1]);
+                acc[2 * i] = __fmaf_rn(wt[j], half_bits_to_float(y[j][i] & 0xFFFFu) * s, acc[2 * i]);
+                acc[2 * i + 1] = __fmaf_rn(wt[j], half_bits_to_float(y[j][i] >> 16) * s, acc[2 * i + 1]);
+            }
+        }
+        if (cw.res != nullptr) {
+            const f32x4* r = (const f32x4*)(cw.res + (size_t)t * H + c);
+            const f32x4 r0 = r[0], r1 = r[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] += r0[i];
+                acc[4 + i] += r1[i];
             }
         }
         f32x4* o = (f32x4*)(out + (size_t)t * H + c);

@@ -49,8 +49,8 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, worklist, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, yexp, yspare,
-        total;
+    size_t flags, offsets, pair_src, inv, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, yexp, yspare, total;
+    int maxrec;  // work records per block type
 };
 
 int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
@@ -90,12 +90,11 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     off = align_up(off + P * sizeof(int32_t));
     L.inv = off;
     off = align_up(off + P * sizeof(int32_t));
-    L.worklist = off;
-    off = align_up(off + 2 * (size_t)E * sizeof(int32_t));
     L.tile_hist = off;
     off = align_up(off + (size_t)(group_tiles((int64_t)P) > 0 ? group_tiles((int64_t)P) : 1) * E * sizeof(int32_t));
-    L.items = off;  // work-list records, [2][E]
-    off = align_up(off + 2 * (size_t)E * sizeof(ItemRec));
+    L.items = off;  // work records, [2][maxrec]
+    L.maxrec = max_records(E, (int)P);
+    off = align_up(off + 2 * (size_t)L.maxrec * sizeof(ItemRec));
     L.xq = off;  // fp8 hi/lo activations of the T1 path
     off = align_up(off + (size_t)T * 2 * H);
     L.xscale = off;  // scale of each row of xq
@@ -132,15 +131,33 @@ int check_ws(const rl_expert_blobs* ex, int32_t T, int32_t k, const void* ws, si
     return RL_OK;
 }
 
-int check_args(const void* x, const void* ids, const void* w, const rl_expert_blobs* ex, const void* out, int32_t T,
-               int32_t k, int present[3]) {
+// The pairs of a call: kin selections per token from topk_ids / topk_w, plus (shared >= 0) one
+// pair of the shared expert per token weighted by gate[t]; res (may be NULL) is added to out
+// after the ordered sum.
+struct Route {
+    const int32_t* ids;
+    const float* w;
+    int32_t kin;
+    int32_t shared;
+    const float* gate;
+    const float* res;
+    int32_t kk() const { return kin + (shared >= 0 ? 1 : 0); }
+    PairIds pid() const { return PairIds{ids, kin, kk(), shared}; }
+};
+inline Route routed_only(const int32_t* ids, const float* w, int32_t k) { return Route{ids, w, k, -1, nullptr, nullptr}; }
+
+int check_args(const void* x, const Route& r, const rl_expert_blobs* ex, const void* out, int32_t T, int present[3]) {
     if (!ex) return RL_EINVAL;
-    if (!shape_ok(T, k, ex->E, ex->H, ex->I)) return RL_ESHAPE;
+    if (r.kin < 0 || !shape_ok(T, r.kk(), ex->E, ex->H, ex->I)) return RL_ESHAPE;
+    if (r.shared >= ex->E) return RL_EINVAL;
     if (T == 0) return RL_OK;
-    if (!x || !ids || !w || !out || !ex->arena || !ex->desc || !ex->desc_host) return RL_EINVAL;
-    // the kernels move x and out in 16-byte pieces and ids, w and descriptors in 4- and 8-byte words
-    if (((uintptr_t)x | (uintptr_t)out) & 15) return RL_EINVAL;
-    if (((uintptr_t)ids | (uintptr_t)w) & 3) return RL_EINVAL;
+    if (!x || !out || !ex->arena || !ex->desc || !ex->desc_host) return RL_EINVAL;
+    if (r.kin > 0 && (!r.ids || !r.w)) return RL_EINVAL;
+    if (r.shared >= 0 && !r.gate) return RL_EINVAL;
+    // the kernels move x, out and the residual in 16-byte pieces and ids, w, gates and
+    // descriptors in 4- and 8-byte words
+    if (((uintptr_t)x | (uintptr_t)out | (uintptr_t)r.res) & 15) return RL_EINVAL;
+    if (((uintptr_t)r.ids | (uintptr_t)r.w | (uintptr_t)r.gate) & 3) return RL_EINVAL;
     if ((uintptr_t)ex->desc & 7) return RL_EINVAL;
     if ((uintptr_t)ex->arena & 3) return RL_EINVAL;
     present[0] = present[1] = present[2] = 0;
@@ -159,31 +176,30 @@ int check_args(const void* x, const void* ids, const void* w, const rl_expert_bl
     return RL_OK;
 }
 
-int check_layer(const void* x, const void* ids, const void* w, const rl_expert_blobs* ex, const void* out, int32_t T,
-                int32_t k, const void* ws, size_t ws_bytes, int present[3]) {
-    const int rc = check_args(x, ids, w, ex, out, T, k, present);
+int check_layer(const void* x, const Route& r, const rl_expert_blobs* ex, const void* out, int32_t T, const void* ws,
+                size_t ws_bytes, int present[3]) {
+    const int rc = check_args(x, r, ex, out, T, present);
     if (rc != RL_OK || T == 0) return rc;
-    return check_ws(ex, T, k, ws, ws_bytes);
+    return check_ws(ex, T, r.kk(), ws, ws_bytes);
 }
 
 // Pair grouping; with split != NULL the split of x runs in the histogram launch.
-void launch_group(const int32_t* ids, int32_t T, int32_t k, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
-                  int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* worklist, int32_t* tile_hist,
-                  ItemRec* items, hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr,
-                  size_t zero_bytes = 0) {
+void launch_group(const PairIds& pid, int32_t T, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
+                  int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* tile_hist, ItemRec* items, int maxrec,
+                  hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr, size_t zero_bytes = 0) {
     GroupArgs g;
     g.zero = static_cast<u32x4*>(zero);
     g.nzero = zero != nullptr ? (int)(zero_bytes / 16) : 0;
-    g.ids = ids;
+    g.pid = pid;
     g.desc = desc;
     g.offsets = offsets;
     g.pair_src = pair_src;
     g.inv = inv;
     g.flags = flags;
-    g.worklist = worklist;
     g.items = items;
+    g.maxrec = maxrec;
     g.tile_hist = tile_hist;
-    g.P = T * k;
+    g.P = T * pid.kk;
     g.E = E;
     g.ntiles = group_tiles(g.P) > 0 ? group_tiles(g.P) : 1;
     g.nflags = FLAGS_WORDS;
@@ -355,19 +371,19 @@ void launch_down_t(const DownArgs& a, int n_experts, hipStream_t s) {
     }
 }
 
-// ordered combine, one kernel instance per k (1..16)
+// ordered combine, one kernel instance per number of pairs per token (1..16)
 template <int K>
-void launch_combine_k(const YSlots& ys, const float* w, float* out, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine<K>, dim3(T), dim3(256), 0, s, ys, w, out);
+void launch_combine_k(const YSlots& ys, const CombineW& cw, float* out, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine<K>, dim3(T), dim3(256), 0, s, ys, cw, out);
 }
-void launch_combine(const YSlots& ys, const float* w, float* out, int T, int k, hipStream_t s) {
-    switch (k) {
+void launch_combine(const YSlots& ys, const CombineW& cw, float* out, int T, int kk, hipStream_t s) {
+    switch (kk) {
 #define RL_CB(K) \
-    case K: launch_combine_k<K>(ys, w, out, T, s); break;
+    case K: launch_combine_k<K>(ys, cw, out, T, s); break;
         RL_CB(1) RL_CB(2) RL_CB(3) RL_CB(4) RL_CB(5) RL_CB(6) RL_CB(7) RL_CB(8)
         RL_CB(9) RL_CB(10) RL_CB(11) RL_CB(12) RL_CB(13) RL_CB(14) RL_CB(15) RL_CB(16)
 #undef RL_CB
-        default: break;  // k is checked to be in [1, 16] before any launch
+        default: break;  // checked to be in [1, 16] before any launch
     }
 }
 
@@ -416,20 +432,22 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
 // holds a chunk's activations in LDS (I a multiple of 256, at most DN_KMAX).
 bool t1_splits_h(const int present[3], int32_t I) { return present[QT_T1] > 0 && I % 256 == 0 && I <= DN_KMAX; }
 
+// Upper bound of the work records of one block type (its experts, plus one per REC_PAIRS pairs).
+int records_bound(int n_experts, int64_t P) { return n_experts + (int)((P + REC_PAIRS - 1) / REC_PAIRS); }
+
 // grouping + gate/up for every present type; returns the layout used.  With h8 (T1, I <= 512)
 // the T1 gate/up writes its h rows split for the fp8 down kernel (h8, with k-group scales hsc)
 // instead of fp16 rows of hdst.
-void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blobs* ex, int32_t T, int32_t k,
-                      void* ws, const int present[3], uint16_t* hdst, hipStream_t s, Layout& L,
-                      void* const* events = nullptr, uint8_t* h8 = nullptr, uint32_t* hsc = nullptr) {
+void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* ex, int32_t T, void* ws,
+                      const int present[3], uint16_t* hdst, hipStream_t s, Layout& L, void* const* events = nullptr,
+                      uint8_t* h8 = nullptr, uint32_t* hsc = nullptr) {
     auto mark = [&](int i) {
         if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
     };
-    L = layout(T, k, ex->E, ex->H, ex->I);
+    const int kk = r.kk();
+    L = layout(T, kk, ex->E, ex->H, ex->I);
     int32_t* flags = at<int32_t>(ws, L.flags);
-    int32_t* offsets = at<int32_t>(ws, L.offsets);
     int32_t* pair_src = at<int32_t>(ws, L.pair_src);
-    int32_t* worklist = at<int32_t>(ws, L.worklist);
     ItemRec* items = at<ItemRec>(ws, L.items);
     uint8_t* xq = at<uint8_t>(ws, L.xq);
     float* xscale = at<float>(ws, L.xscale);
@@ -439,13 +457,14 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     sa.scale = xscale;
     sa.rows = T;
     sa.K = ex->H;
-    launch_group(ids, T, k, ex->E, ex->desc, offsets, pair_src, at<int32_t>(ws, L.inv), flags, worklist,
-                 at<int32_t>(ws, L.tile_hist), items, s, present[QT_T1] ? &sa : nullptr, at<void>(ws, L.yexp),
-                 L.yspare - L.yexp);
+    launch_group(r.pid(), T, ex->E, ex->desc, at<int32_t>(ws, L.offsets), pair_src, at<int32_t>(ws, L.inv), flags,
+                 at<int32_t>(ws, L.tile_hist), items, L.maxrec, s, present[QT_T1] ? &sa : nullptr,
+                 at<void>(ws, L.yexp), L.yspare - L.yexp);
     mark(1);
+    const int64_t P = (int64_t)T * kk;
     GuArgs b = {};
     b.pair_src = pair_src;
-    b.k = k;
+    b.k = kk;
     b.arena = static_cast<const uint8_t*>(ex->arena);
     b.hbuf = hdst;
     b.K = ex->H;
@@ -454,9 +473,9 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
     if (present[QT_Q2B]) {  // x as it is (bf16)
         GuArgs q = b;
         q.act = reinterpret_cast<const uint8_t*>(x);
-        q.items = items + (QT_Q2B - 1) * ex->E;
+        q.items = items + (size_t)(QT_Q2B - 1) * L.maxrec;
         q.wl_len = flags + 8 + QT_Q2B;
-        launch_gateup_mm<QT_Q2B>(q, present[QT_Q2B], s);
+        launch_gateup_mm<QT_Q2B>(q, records_bound(present[QT_Q2B], P), s);
     }
     if (present[QT_T1]) {  // the split of x
         GuArgs q = b;
@@ -464,58 +483,47 @@ void run_group_gateup(const uint16_t* x, const int32_t* ids, const rl_expert_blo
         q.ascale = xscale;
         q.h8 = h8;
         q.hsc = hsc;
-        q.items = items + (QT_T1 - 1) * ex->E;
+        q.items = items + (size_t)(QT_T1 - 1) * L.maxrec;
         q.wl_len = flags + 8 + QT_T1;
-        launch_gateup_mm<QT_T1>(q, present[QT_T1], s);
+        launch_gateup_mm<QT_T1>(q, records_bound(present[QT_T1], P), s);
     }
     mark(2);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, int32_t I) {
-    if (!shape_ok(T_max, k, E, H, I)) return 0;
-    return layout(T_max, k, E, H, I).total;
-}
-
-static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
-                        const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* workspace,
-                        size_t ws_bytes, void* stream, void* const* events) {
+int prefill_impl(const uint16_t* x, const Route& r, const rl_expert_blobs* experts, float* out, int32_t T,
+                 void* workspace, size_t ws_bytes, void* stream, void* const* events) {
     int present[3] = {0, 0, 0};
-    int rc = check_layer(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, present);
+    int rc = check_layer(x, r, experts, out, T, workspace, ws_bytes, present);
     if (rc != RL_OK || T == 0) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     auto mark = [&](int i) {
         if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
     };
-    const Layout L = layout(T, k, experts->E, experts->H, experts->I);
+    const int kk = r.kk();
+    const int64_t P = (int64_t)T * kk;
+    const Layout L = layout(T, kk, experts->E, experts->H, experts->I);
     uint16_t* hbuf = at<uint16_t>(workspace, L.hbuf);
     int32_t* flags = at<int32_t>(workspace, L.flags);
-    int32_t* offsets = at<int32_t>(workspace, L.offsets);
     int32_t* pair_src = at<int32_t>(workspace, L.pair_src);
-    int32_t* worklist = at<int32_t>(workspace, L.worklist);
+    ItemRec* items = at<ItemRec>(workspace, L.items);
     YSlots ys;
     ys.yslot = at<uint16_t>(workspace, L.yslot);
     ys.yexp = at<int8_t>(workspace, L.yexp);
     ys.yspare = at<uint16_t>(workspace, L.yspare);
     ys.espare = at<int8_t>(workspace, L.yspare + (size_t)Y_SPARE * CT * sizeof(uint16_t));
     ys.H = experts->H;
-    ys.P = T * k;
+    ys.P = (int)P;
     mark(0);
     Layout L2;  // same layout as L
     // T1 with I <= 512: gate/up writes h already split for the down kernel (no split of h)
     const bool t1_hsplit_fused = t1_splits_h(present, experts->I);
     uint8_t* h8 = at<uint8_t>(workspace, L.h8);
     uint32_t* hsc = at<uint32_t>(workspace, L.hscale);
-    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, hbuf, s, L2, events,
-                     t1_hsplit_fused ? h8 : nullptr, t1_hsplit_fused ? hsc : nullptr);
+    run_group_gateup(x, r, experts, T, workspace, present, hbuf, s, L2, events, t1_hsplit_fused ? h8 : nullptr,
+                     t1_hsplit_fused ? hsc : nullptr);
     DownArgs d;
     d.hbuf = hbuf;
     d.arena = static_cast<const uint8_t*>(experts->arena);
-    d.desc = experts->desc;
-    d.offsets = offsets;
     d.pair_src = pair_src;
     d.ys = ys;
     d.flags = flags;
@@ -533,57 +541,77 @@ static int prefill_impl(const uint16_t* x, const int32_t* topk_ids, const float*
     b.flags = flags;
     b.K = experts->I;
     b.N = experts->H;
-    b.P = T * k;
+    b.P = (int)P;
     if (mm_dn && present[QT_T1]) {
         b.act = h8;
         b.ascale = at<float>(workspace, L.hscale);  // I > 512: one scale per row, from the split of h
         b.hsc = hsc;                                // I <= 512: k-group scales from gate/up
-        if (!t1_hsplit_fused) launch_hsplit(b, T * k, s);
+        if (!t1_hsplit_fused) launch_hsplit(b, (int)P, s);
     }
     mark(3);
     for (int q = QT_Q2B; q <= QT_T1; ++q) {
         if (!present[q]) continue;
+        const int nrec = records_bound(present[q], P);
         if (mm_dn) {
             GuArgs bq = b;
-            bq.items = at<ItemRec>(workspace, L.items) + (q - 1) * experts->E;
+            bq.items = items + (size_t)(q - 1) * L.maxrec;
             bq.wl_len = flags + 8 + q;
             if (q == QT_Q2B) {
                 bq.act = reinterpret_cast<const uint8_t*>(hbuf);
                 bq.ascale = nullptr;
-                launch_down_mm<QT_Q2B>(bq, present[q], s);
+                launch_down_mm<QT_Q2B>(bq, nrec, s);
             } else {
-                launch_down_mm<QT_T1>(bq, present[q], s);
+                launch_down_mm<QT_T1>(bq, nrec, s);
             }
             continue;
         }
-        d.worklist = worklist + (q - 1) * experts->E;
+        d.items = items + (size_t)(q - 1) * L.maxrec;
         d.wl_len = flags + 8 + q;
         d.counters = flags + counter_set(1, q);
         if (q == QT_Q2B)
-            launch_down_t<QT_Q2B>(d, present[q], s);
+            launch_down_t<QT_Q2B>(d, nrec, s);
         else
-            launch_down_t<QT_T1>(d, present[q], s);
+            launch_down_t<QT_T1>(d, nrec, s);
     }
     mark(4);
-    launch_combine(ys, topk_w, out, T, k, s);
+    launch_combine(ys, CombineW{r.w, r.shared >= 0 ? r.gate : nullptr, r.res, r.kin}, out, T, kk, s);
     mark(5);
     return hip_status();
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t rl_moe_workspace_bytes(int32_t T_max, int32_t k, int32_t E, int32_t H, int32_t I) {
+    if (!shape_ok(T_max, k, E, H, I)) return 0;
+    return layout(T_max, k, E, H, I).total;
+}
+
 int rl_moe_prefill(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
                    float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
-    return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, stream, nullptr);
+    return prefill_impl(x, routed_only(topk_ids, topk_w, k), experts, out, T, workspace, ws_bytes, stream, nullptr);
+}
+
+int rl_moe_prefill_block(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                         const rl_expert_blobs* experts, int32_t shared_expert, const float* shared_gate,
+                         const float* residual, float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes,
+                         void* stream) {
+    if (shared_expert < 0) return RL_EINVAL;
+    const Route r{topk_ids, topk_w, k, shared_expert, shared_gate, residual};
+    return prefill_impl(x, r, experts, out, T, workspace, ws_bytes, stream, nullptr);
 }
 
 int rl_moe_prefill_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                            const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* stream) {
     int present[3] = {0, 0, 0};
-    int rc = check_args(x, topk_ids, topk_w, experts, out, T, k, present);
+    const Route r = routed_only(topk_ids, topk_w, k);
+    int rc = check_args(x, r, experts, out, T, present);
     if (rc != RL_OK || T == 0) return rc;
     if (layout(T, k, experts->E, experts->H, experts->I).total > RL_NOALLOC_SCRATCH_BYTES) return RL_ETOOBIG;
     void* ws = noalloc_scratch(true);
     if (ws == nullptr) return RL_EHIP;
-    return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, ws, RL_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+    return prefill_impl(x, r, experts, out, T, ws, RL_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int rl_moe_noalloc_status(int32_t* flags_out) {
@@ -599,15 +627,16 @@ int rl_moe_prefill_timed(const uint16_t* x, const int32_t* topk_ids, const float
     if (!events) return RL_EINVAL;
     for (int i = 0; i < RL_TIMED_EVENTS; ++i)
         if (!events[i]) return RL_EINVAL;
-    return prefill_impl(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, stream, events);
+    return prefill_impl(x, routed_only(topk_ids, topk_w, k), experts, out, T, workspace, ws_bytes, stream, events);
 }
 
 int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
                    uint16_t* h16_out, uint8_t* h8_out, uint32_t* hsc_out, int32_t T, int32_t k, void* workspace,
                    size_t ws_bytes, void* stream) {
     int present[3] = {0, 0, 0};
+    const Route r = routed_only(topk_ids, topk_w, k);
     // validated with a stand-in for `out` (the hook has no layer output); the h buffers below
-    int rc = check_args(x, topk_ids, topk_w, experts, x, T, k, present);
+    int rc = check_args(x, r, experts, x, T, present);
     if (rc != RL_OK || T == 0) return rc;
     const bool split = t1_splits_h(present, experts->I);
     const bool need16 = present[QT_Q2B] > 0 || (present[QT_T1] > 0 && !split);
@@ -616,8 +645,8 @@ int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk
     rc = check_ws(experts, T, k, workspace, ws_bytes);
     if (rc != RL_OK) return rc;
     Layout L;
-    run_group_gateup(x, topk_ids, experts, T, k, workspace, present, h16_out, static_cast<hipStream_t>(stream), L,
-                     nullptr, split ? h8_out : nullptr, split ? hsc_out : nullptr);
+    run_group_gateup(x, r, experts, T, workspace, present, h16_out, static_cast<hipStream_t>(stream), L, nullptr,
+                     split ? h8_out : nullptr, split ? hsc_out : nullptr);
     return hip_status();
 }
 
@@ -625,7 +654,7 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
                   float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
     int present[3] = {0, 0, 0};
     if (experts && (T < 1 || T > 2 || !gv_dim_ok(experts->H) || !gv_dim_ok(experts->I))) return RL_ESHAPE;
-    int rc = check_layer(x, topk_ids, topk_w, experts, out, T, k, workspace, ws_bytes, present);
+    int rc = check_layer(x, routed_only(topk_ids, topk_w, k), experts, out, T, workspace, ws_bytes, present);
     if (rc != RL_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Layout L = layout(T, k, experts->E, experts->H, experts->I);
@@ -684,9 +713,8 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
     const Layout L = layout(T, k, E, 256, 64);
     if (ws_bytes < L.tile_hist + (size_t)(group_tiles((int64_t)T * k) > 0 ? group_tiles((int64_t)T * k) : 1) * E * 4)
         return RL_EWORKSPACE;
-    launch_group(topk_ids, T, k, E, nullptr, offsets, pair_src, inv, at<int32_t>(workspace, L.flags),
-                 at<int32_t>(workspace, L.worklist), at<int32_t>(workspace, L.tile_hist), nullptr,
-                 static_cast<hipStream_t>(stream));
+    launch_group(PairIds{topk_ids, k, k, -1}, T, E, nullptr, offsets, pair_src, inv, at<int32_t>(workspace, L.flags),
+                 at<int32_t>(workspace, L.tile_hist), nullptr, 0, static_cast<hipStream_t>(stream));
     return hip_status();
 }
 

@@ -28,5 +28,7 @@ from .gen import (  # noqa: F401
     make_experts,
     Workload,
     make_workload,
+    BlockWorkload,
+    make_block_workload,
     CONFIGS,
 )

@@ -306,3 +306,35 @@ def make_workload(name: str, seed: int = 1234, T: int | None = None, experts: Ex
     bias = zipf_bias(E, seed + 3) if cfg.get("bias") == "zipf" else None
     ids, w = _routing(T, E, k, seed + 2, bias)
     return Workload(name=name, x=x, ids=ids, w=w, experts=experts, seed=seed, meta=cfg)
+
+
+@dataclass
+class BlockWorkload:
+    """A layer workload plus the rest of the MoE block: the shared expert (descriptor `shared` of
+    wl.experts, after the routed experts 0..shared-1 that wl.ids route to), its per-token gate and
+    the residual stream."""
+
+    wl: Workload
+    shared: int
+    gate: np.ndarray      # float32 [T], the shared expert's weight per token
+    residual: np.ndarray  # float32 [T, H]
+
+
+def make_block_workload(name: str, seed: int = 1234, T: int | None = None, **over) -> BlockWorkload:
+    """Workload `name` with one more expert, the shared one, of the block type of the last routed
+    expert (weights from the same per-(seed, expert, matrix) streams, so the routed experts equal
+    make_workload's), a gate sigmoid(N(0,1)) per token (seed+4) and a residual N(0,1) fp32
+    (seed+5)."""
+    cfg = dict(CONFIGS[name])
+    cfg.update(over)
+    if T is not None:
+        cfg["T"] = T
+    E, H, I = cfg["E"], cfg["H"], cfg["I"]
+    qt = _qtypes(cfg["types"], E)
+    experts = make_experts(E + 1, H, I, np.concatenate([qt, qt[-1:]]), seed)
+    routed = make_workload(name, seed=seed, experts=experts, **{k_: v for k_, v in cfg.items() if k_ in ("T", "H", "E", "I", "k", "types")})
+    Tn = routed.T
+    rng = np.random.Generator(np.random.PCG64(seed + 4))
+    gate = (1.0 / (1.0 + np.exp(-rng.standard_normal(Tn)))).astype(np.float32)
+    residual = np.random.Generator(np.random.PCG64(seed + 5)).standard_normal((Tn, H), dtype=np.float32)
+    return BlockWorkload(wl=routed, shared=E, gate=gate, residual=residual)
