@@ -163,6 +163,15 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
                   const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                   void* workspace, size_t ws_bytes, void* stream);
 
+/* rl_moe_prefill_block for 1 or 2 rows on the matrix-vector kernels (decode and 2-row verify):
+ * the shared expert's pair follows each row's routed pairs in its ordered sum, then the residual.
+ * Arguments as rl_moe_prefill_block; T and the dimensions as rl_moe_decode.  Each row's result
+ * is bit-identical to a call with that row alone. */
+int rl_moe_decode_block(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                        const rl_expert_blobs* experts, int32_t shared_expert, const float* shared_gate,
+                        const float* residual, float* out, int32_t T, int32_t k, void* workspace,
+                        size_t ws_bytes, void* stream);
+
 /* Pair grouping alone (parity hook for the first step of rl_moe_prefill).  Pairs (t, j) are
  * ordered by (expert, token, slot):
  *   offsets  [dev] int32 [E+1], exclusive prefix sum of the per-expert pair counts

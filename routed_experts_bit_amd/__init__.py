@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     prefill_timed,
     prefill_noalloc,
     prefill_block,
+    decode_block,
     noalloc_status,
     NOALLOC_SCRATCH_BYTES,
     TIMED_EVENTS,

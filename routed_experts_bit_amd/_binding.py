@@ -32,6 +32,7 @@ EXPORTS = (
     "rl_moe_prefill_noalloc",
     "rl_moe_noalloc_status",
     "rl_moe_prefill_block",
+    "rl_moe_decode_block",
 )
 NOALLOC_SCRATCH_BYTES = 40 << 20  # RL_NOALLOC_SCRATCH_BYTES
 
@@ -76,8 +77,9 @@ def lib():
         getattr(L, name).restype = C.c_int
     L.rl_moe_gate_up.argtypes = [P, P, P, C.POINTER(_Blobs), P, P, P, I32, I32, P, SZ, P]
     L.rl_moe_gate_up.restype = C.c_int
-    L.rl_moe_prefill_block.argtypes = [P, P, P, C.POINTER(_Blobs), I32, P, P, P, I32, I32, P, SZ, P]
-    L.rl_moe_prefill_block.restype = C.c_int
+    for name in ("rl_moe_prefill_block", "rl_moe_decode_block"):
+        getattr(L, name).argtypes = [P, P, P, C.POINTER(_Blobs), I32, P, P, P, I32, I32, P, SZ, P]
+        getattr(L, name).restype = C.c_int
     L.rl_moe_prefill_noalloc.argtypes = [P, P, P, C.POINTER(_Blobs), P, I32, I32, P]
     L.rl_moe_prefill_noalloc.restype = C.c_int
     L.rl_moe_noalloc_status.argtypes = [P]
@@ -279,6 +281,17 @@ def prefill_block(x, ids, w, ex: DeviceExperts, shared: int, gate, residual=None
     """The MoE block (rl_moe_prefill_block): routed experts in selection order, then the shared
     expert `shared` (a descriptor index) weighted by gate float32 [T], then residual float32 [T, H]
     (None: none).  ids int32 [T, k] / w float32 [T, k] may have k = 0 columns."""
+    return _block(lib().rl_moe_prefill_block, "rl_moe_prefill_block", x, ids, w, ex, shared, gate, residual, out, ws)
+
+
+def decode_block(x, ids, w, ex: DeviceExperts, shared: int, gate, residual=None, out=None, ws=None):
+    """rl_moe_decode_block: the MoE block for 1 or 2 rows on the matrix-vector kernels."""
+    if ids.shape[0] not in (1, 2):
+        raise RlError(f"decode_block: {ids.shape[0]} rows, expected 1 or 2")
+    return _block(lib().rl_moe_decode_block, "rl_moe_decode_block", x, ids, w, ex, shared, gate, residual, out, ws)
+
+
+def _block(fn, name, x, ids, w, ex, shared, gate, residual, out, ws):
     torch = _torch()
     _need("topk_ids", ids, (torch.int32,), (None, None))
     T, k = ids.shape
@@ -295,9 +308,9 @@ def prefill_block(x, ids, w, ex: DeviceExperts, shared: int, gate, residual=None
     if ws is None:
         ws = torch.empty(workspace_bytes(max(T, 1), k + 1, ex.E, ex.H, ex.I), dtype=torch.uint8, device=dev)
     _need("workspace", ws, d["ws"], (None,), dev)
-    rc = lib().rl_moe_prefill_block(_ptr(x), _ptr(ids) if k else None, _ptr(w) if k else None, ex.blobs, int(shared),
-                                    _ptr(gate), _ptr(residual), _ptr(out), T, k, _ptr(ws), ws.numel(), _stream())
-    _check(rc, "rl_moe_prefill_block")
+    rc = fn(_ptr(x), _ptr(ids) if k else None, _ptr(w) if k else None, ex.blobs, int(shared), _ptr(gate),
+            _ptr(residual), _ptr(out), T, k, _ptr(ws), ws.numel(), _stream())
+    _check(rc, name)
     return out
 
 

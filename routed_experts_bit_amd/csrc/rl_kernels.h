@@ -1874,14 +1874,21 @@ __device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, uint32_t m
 
 struct GvArgs {
     const uint16_t* x;
-    const int32_t* ids;
-    const float* w;
+    PairIds pid;      // the call's pairs (k = pid.kk per row, the last one the shared expert if any)
+    const float* w;   // [R][pid.kin]
+    const float* gate;  // [R]: weight of the shared expert's pair (with pid.shared >= 0)
+    const float* res;   // [R][H] or NULL: added after the ordered sum
     const uint8_t* arena;
     const rl_expert_desc* desc;
     uint16_t* hgv;  // [R*k][I] fp16
     float* out;  // [R][H]
     int32_t* flags;
     int R, k, E, H, I;
+    __device__ __forceinline__ float weight(int p) const {  // weight of pair p = r*k + j
+        if (pid.shared < 0) return w[p];
+        const int r = p / k, j = p - r * k;
+        return j < pid.kin ? w[r * pid.kin + j] : gate[r];
+    }
 };
 
 // The call's pairs (R*k <= 32) read once per work-group: expert (-1 for an id outside [0, E)),
@@ -1896,7 +1903,7 @@ constexpr int GV_MAX_PAIRS = 32;
 __device__ __forceinline__ void gv_load_pairs(const GvArgs& a, GvPair* sp) {
     const int tid = threadIdx.x;
     if (tid < a.R * a.k) {
-        const int e = a.ids[tid];
+        const int e = a.pid.expert(tid);
         GvPair p{-1, 0, 0, 0, 0};
         if (e >= 0 && e < a.E) {
             const rl_expert_desc d = a.desc[e];
@@ -1923,7 +1930,7 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
         const int pr = wv / half_i;
         const int i0 = 2 * (wv % half_i);
         const int r = pr / a.k;
-        const int e = a.ids[pr];
+        const int e = a.pid.expert(pr);
         const int row = i0 + (rs & 1);
         float part = 0.f;
         if (e >= 0 && e < a.E) {
@@ -1952,8 +1959,8 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
     tb.build(threadIdx.x, 256);
     gv_load_pairs(a, sp);
     if (threadIdx.x < a.R * a.k) {
-        wsh[threadIdx.x] = a.w[threadIdx.x];
-        const int e = a.ids[threadIdx.x];
+        wsh[threadIdx.x] = a.weight(threadIdx.x);
+        const int e = a.pid.expert(threadIdx.x);
         if (blockIdx.x == 0 && (e < 0 || e >= a.E)) atomicOr(&a.flags[0], FLAG_BAD_ID);
     }
     __syncthreads();
@@ -2018,7 +2025,7 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
                 if (j0 + s2 < a.k) acc = __fmaf_rn(wsh[r * a.k + j0 + s2], y, acc);
             }
         }
-        if (lane == 0) a.out[(size_t)r * a.H + c] = acc;
+        if (lane == 0) a.out[(size_t)r * a.H + c] = a.res != nullptr ? acc + a.res[(size_t)r * a.H + c] : acc;
     }
 }
 

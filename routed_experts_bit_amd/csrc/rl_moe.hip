@@ -650,25 +650,28 @@ int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk
     return hip_status();
 }
 
-int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
-                  float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
+static int decode_impl(const uint16_t* x, const Route& r, const rl_expert_blobs* experts, float* out, int32_t T,
+                       void* workspace, size_t ws_bytes, void* stream) {
     int present[3] = {0, 0, 0};
     if (experts && (T < 1 || T > 2 || !gv_dim_ok(experts->H) || !gv_dim_ok(experts->I))) return RL_ESHAPE;
-    int rc = check_layer(x, routed_only(topk_ids, topk_w, k), experts, out, T, workspace, ws_bytes, present);
+    int rc = check_layer(x, r, experts, out, T, workspace, ws_bytes, present);
     if (rc != RL_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Layout L = layout(T, k, experts->E, experts->H, experts->I);
+    const int kk = r.kk();
+    Layout L = layout(T, kk, experts->E, experts->H, experts->I);
     GvArgs a;
     a.x = x;
-    a.ids = topk_ids;
-    a.w = topk_w;
+    a.pid = r.pid();
+    a.w = r.w;
+    a.gate = r.gate;
+    a.res = r.res;
     a.arena = static_cast<const uint8_t*>(experts->arena);
     a.desc = experts->desc;
     a.hgv = at<uint16_t>(workspace, L.hbuf);  // [R*k][I] fp16
     a.out = out;
     a.flags = at<int32_t>(workspace, L.flags);
     a.R = T;
-    a.k = k;
+    a.k = kk;
     a.E = experts->E;
     a.H = experts->H;
     a.I = experts->I;
@@ -680,6 +683,20 @@ int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_
     else
         launch_gv<3>(a, s);
     return hip_status();
+}
+
+int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, const rl_expert_blobs* experts,
+                  float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes, void* stream) {
+    return decode_impl(x, routed_only(topk_ids, topk_w, k), experts, out, T, workspace, ws_bytes, stream);
+}
+
+int rl_moe_decode_block(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                        const rl_expert_blobs* experts, int32_t shared_expert, const float* shared_gate,
+                        const float* residual, float* out, int32_t T, int32_t k, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    if (shared_expert < 0) return RL_EINVAL;
+    const Route r{topk_ids, topk_w, k, shared_expert, shared_gate, residual};
+    return decode_impl(x, r, experts, out, T, workspace, ws_bytes, stream);
 }
 
 int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,

@@ -122,3 +122,30 @@ def test_block_full_size(orc, rl, name):
     err = rel_l2(out - res, ref - res)
     log(f"block full {name}: T={wl.T} rel_l2 {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("types", ["t1", "mixed"])
+def test_decode_block(orc, rl, types):
+    """The 1-2 row path with the shared expert and the residual: against the oracle, each row of a
+    2-row call bit-identical to a 1-row call, and within the bar of the prefill block."""
+    import torch
+
+    name = {"t1": "t1_2048", "mixed": "mixed_2048"}[types]
+    bw = make_block_workload(name, seed=88, T=2, E=64)
+    wl = bw.wl
+    wl.ids[1, :3] = wl.ids[0, :3]  # the rows share some experts
+    x, ids, w, g, r, ex = _dev(bw)
+    two = rl.decode_block(x, ids, w, ex, bw.shared, g, r)
+    one0 = rl.decode_block(x[:1].contiguous(), ids[:1].contiguous(), w[:1].contiguous(), ex, bw.shared,
+                           g[:1].contiguous(), r[:1].contiguous())
+    one1 = rl.decode_block(x[1:].contiguous(), ids[1:].contiguous(), w[1:].contiguous(), ex, bw.shared,
+                           g[1:].contiguous(), r[1:].contiguous())
+    assert torch.equal(two[0], one0[0]) and torch.equal(two[1], one1[0])
+    got = two.cpu().numpy().astype(np.float64)
+    ref = _oracle(orc, bw)
+    res = bw.residual.astype(np.float64)
+    err = rel_l2(got - res, ref - res)
+    log(f"decode block {types}: rel_l2 {err:.3e}")
+    assert err <= TOL
+    pre = rl.prefill_block(x, ids, w, ex, bw.shared, g, r).cpu().numpy().astype(np.float64)
+    assert rel_l2(got - res, pre - res) <= TOL
