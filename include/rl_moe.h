@@ -122,6 +122,22 @@ int rl_moe_prefill_block(const uint16_t* x, const int32_t* topk_ids, const float
                          const float* residual, float* out, int32_t T, int32_t k, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* The router and the layer in one call: every token's k experts are chosen among experts
+ * [0, n_route) from its fp32 logits exactly as rl_moe_route chooses them, inside the first launch
+ * of the pair grouping (the router's work-groups also count their pairs per expert), and written
+ * to topk_ids / topk_w; then the layer (with shared_expert >= 0 the MoE block, as
+ * rl_moe_prefill_block; shared_expert < 0: the routed experts only, shared_gate and residual
+ * ignored) runs on them.
+ *   logits    [dev] float [T][n_route], 4-byte aligned, finite
+ *   topk_ids  [dev] int32 [T][k], topk_w [dev] float [T][k]: outputs (the routing), 4-byte aligned
+ *   n_route in [1, E]; k in [1, min(16, n_route)], at most 15 with a shared expert
+ *   workspace at least rl_moe_workspace_bytes(T, k (+1 with a shared expert), E, H, I) bytes
+ * Other arguments and errors as rl_moe_prefill / rl_moe_prefill_block. */
+int rl_moe_prefill_from_logits(const uint16_t* x, const float* logits, int32_t n_route,
+                               const rl_expert_blobs* experts, int32_t shared_expert, const float* shared_gate,
+                               const float* residual, float* out, int32_t* topk_ids, float* topk_w, int32_t T,
+                               int32_t k, void* workspace, size_t ws_bytes, void* stream);
+
 /* Measurement hook: rl_moe_prefill with RL_TIMED_EVENTS events (events [host] array of
  * hipEvent_t, created by the caller) recorded on `stream`: 0 before the grouping kernels (whose
  * first launch also splits x for the T1 path), 1 after them, 2 after the gate/up kernel(s), 3

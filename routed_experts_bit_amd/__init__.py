@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     prefill_noalloc,
     prefill_block,
     decode_block,
+    prefill_from_logits,
     noalloc_status,
     NOALLOC_SCRATCH_BYTES,
     TIMED_EVENTS,

@@ -33,6 +33,7 @@ EXPORTS = (
     "rl_moe_noalloc_status",
     "rl_moe_prefill_block",
     "rl_moe_decode_block",
+    "rl_moe_prefill_from_logits",
 )
 NOALLOC_SCRATCH_BYTES = 40 << 20  # RL_NOALLOC_SCRATCH_BYTES
 
@@ -80,6 +81,8 @@ def lib():
     for name in ("rl_moe_prefill_block", "rl_moe_decode_block"):
         getattr(L, name).argtypes = [P, P, P, C.POINTER(_Blobs), I32, P, P, P, I32, I32, P, SZ, P]
         getattr(L, name).restype = C.c_int
+    L.rl_moe_prefill_from_logits.argtypes = [P, P, I32, C.POINTER(_Blobs), I32, P, P, P, P, P, I32, I32, P, SZ, P]
+    L.rl_moe_prefill_from_logits.restype = C.c_int
     L.rl_moe_prefill_noalloc.argtypes = [P, P, P, C.POINTER(_Blobs), P, I32, I32, P]
     L.rl_moe_prefill_noalloc.restype = C.c_int
     L.rl_moe_noalloc_status.argtypes = [P]
@@ -312,6 +315,43 @@ def _block(fn, name, x, ids, w, ex, shared, gate, residual, out, ws):
             _ptr(residual), _ptr(out), T, k, _ptr(ws), ws.numel(), _stream())
     _check(rc, name)
     return out
+
+
+def prefill_from_logits(x, logits, k: int, ex: DeviceExperts, shared: int = -1, gate=None, residual=None, out=None,
+                        ids=None, w=None, ws=None):
+    """rl_moe_prefill_from_logits: route every token among the first logits.shape[1] experts (fp32
+    logits [T, n_route]) in the grouping's first launch, then the layer (with shared >= 0 the MoE
+    block).  Returns (out float32 [T, H], topk_ids int32 [T, k], topk_w float32 [T, k])."""
+    torch = _torch()
+    _need("logits", logits, (torch.float32,), (None, None))
+    T, n_route = logits.shape
+    dev = logits.device
+    d = _dt()
+    _need("x", x, d["x"], (T, ex.H), dev)
+    kk = k + (1 if shared >= 0 else 0)
+    if shared >= 0:
+        _need("shared_gate", gate, (torch.float32,), (T,), dev)
+        if residual is not None:
+            _need("residual", residual, (torch.float32,), (T, ex.H), dev)
+    else:
+        gate, residual = None, None
+    if out is None:
+        out = torch.empty((T, ex.H), dtype=torch.float32, device=dev)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need("out", out, d["out"], (T, ex.H), dev)
+    _need("topk_ids", ids, (torch.int32,), (T, k), dev)
+    _need("topk_w", w, (torch.float32,), (T, k), dev)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(max(T, 1), kk, ex.E, ex.H, ex.I), dtype=torch.uint8, device=dev)
+    _need("workspace", ws, d["ws"], (None,), dev)
+    rc = lib().rl_moe_prefill_from_logits(_ptr(x), _ptr(logits), n_route, ex.blobs, int(shared), _ptr(gate),
+                                          _ptr(residual), _ptr(out), _ptr(ids), _ptr(w), T, int(k), _ptr(ws),
+                                          ws.numel(), _stream())
+    _check(rc, "rl_moe_prefill_from_logits")
+    return out, ids, w
 
 
 def prefill_noalloc(x, ids, w, ex: DeviceExperts, out):

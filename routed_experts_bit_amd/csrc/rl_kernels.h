@@ -103,6 +103,7 @@ struct GroupArgs {
     ItemRec* items;     // [2][maxrec]: per block type, records longest first
     int maxrec;
     int32_t* tile_hist; // [ntiles][E]
+    int tp;             // pairs per tile (at most GT)
     u32x4* zero;        // the y scale bytes of the call, cleared by the first launch (may be NULL)
     int nzero;          // 16-byte words
     int P, E, ntiles;
@@ -121,7 +122,7 @@ __device__ __forceinline__ void group_count_tile(const GroupArgs& a, int tile) {
     if (tile == 0 && tid < a.nflags) a.flags[tid] = 0;
     for (int e = tid; e < a.E; e += GROUP_NTHR) h[e] = 0;
     __syncthreads();
-    const int p0 = tile * GT, p1 = min(a.P, p0 + GT);
+    const int p0 = tile * a.tp, p1 = min(a.P, p0 + a.tp);
     for (int p = p0 + tid; p < p1; p += GROUP_NTHR) {
         const int e = a.pid.expert(p);
         if (e >= 0 && e < a.E) atomicAdd(&h[e], 1);
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tile = blockIdx.x;
     const bool lister = tile == a.ntiles;  // the offsets and work lists; no pairs (n <= 0)
     const int E = a.E;
-    const int p0 = tile * GT, n = min(a.P - p0, GT);
+    const int p0 = tile * a.tp, n = min(a.P - p0, a.tp);
     // the work-list builder's expert descriptors (e = tid + GROUP_NTHR * i), loaded before the
     // scans so that their latency overlaps them
     constexpr int EPL = MAX_E / GROUP_NTHR;

@@ -53,7 +53,10 @@ struct Layout {
     int maxrec;  // work records per block type
 };
 
-int group_tiles(int64_t P) { return (int)((P + GT - 1) / GT); }
+// Grouping tiles of tp pairs (tp = GT, or the largest multiple of the pairs per token that fits
+// GT when the router runs in the grouping's first launch: always more than GT / 2).
+int group_tiles(int64_t P, int tp = GT) { return (int)((P + tp - 1) / tp); }
+int tile_hist_rows(int64_t P) { return P > 0 ? group_tiles(P, GT / 2) : 1; }
 
 // Largest byte extent of a buffer that the kernels address with 32-bit offsets (activation rows
 // of the gate/up and down GEMMs); their buffer resources span at most 0x7FFFFFF0 bytes.
@@ -91,7 +94,7 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     L.inv = off;
     off = align_up(off + P * sizeof(int32_t));
     L.tile_hist = off;
-    off = align_up(off + (size_t)(group_tiles((int64_t)P) > 0 ? group_tiles((int64_t)P) : 1) * E * sizeof(int32_t));
+    off = align_up(off + (size_t)tile_hist_rows((int64_t)P) * E * sizeof(int32_t));
     L.items = off;  // work records, [2][maxrec]
     L.maxrec = max_records(E, (int)P);
     off = align_up(off + 2 * (size_t)L.maxrec * sizeof(ItemRec));
@@ -134,6 +137,9 @@ int check_ws(const rl_expert_blobs* ex, int32_t T, int32_t k, const void* ws, si
 // The pairs of a call: kin selections per token from topk_ids / topk_w, plus (shared >= 0) one
 // pair of the shared expert per token weighted by gate[t]; res (may be NULL) is added to out
 // after the ordered sum.
+// With logits != NULL the call routes first: the router picks the kin selections of every token
+// among experts [0, n_route) from logits [T][n_route] and writes them to ids / w (the caller's
+// output buffers), in the grouping's first launch.
 struct Route {
     const int32_t* ids;
     const float* w;
@@ -141,6 +147,8 @@ struct Route {
     int32_t shared;
     const float* gate;
     const float* res;
+    const float* logits = nullptr;
+    int32_t n_route = 0;
     int32_t kk() const { return kin + (shared >= 0 ? 1 : 0); }
     PairIds pid() const { return PairIds{ids, kin, kk(), shared}; }
 };
@@ -150,7 +158,9 @@ int check_args(const void* x, const Route& r, const rl_expert_blobs* ex, const v
     if (!ex) return RL_EINVAL;
     if (r.kin < 0 || !shape_ok(T, r.kk(), ex->E, ex->H, ex->I)) return RL_ESHAPE;
     if (r.shared >= ex->E) return RL_EINVAL;
+    if (r.logits != nullptr && (r.n_route < 1 || r.n_route > ex->E || r.kin < 1 || r.kin > r.n_route)) return RL_ESHAPE;
     if (T == 0) return RL_OK;
+    if ((uintptr_t)r.logits & 3) return RL_EINVAL;
     if (!x || !out || !ex->arena || !ex->desc || !ex->desc_host) return RL_EINVAL;
     if (r.kin > 0 && (!r.ids || !r.w)) return RL_EINVAL;
     if (r.shared >= 0 && !r.gate) return RL_EINVAL;
@@ -184,9 +194,34 @@ int check_layer(const void* x, const Route& r, const rl_expert_blobs* ex, const 
 }
 
 // Pair grouping; with split != NULL the split of x runs in the histogram launch.
+template <int NR>
+void launch_route_count_split(const RouteArgs& ra, const GroupArgs& g, const SplitArgs& a, hipStream_t s) {
+    const int G = a.K / 32;  // K <= 8192: G <= 256
+    const int nsplit = a.rows > 0 ? a.rows : 0;
+#define RL_RCS(LPR, NG)                                                                                              \
+    hipLaunchKernelGGL((k_route_count_split<NR, LPR, NG>), dim3(g.ntiles + (nsplit + 256 / LPR - 1) / (256 / LPR)), \
+                       dim3(256), 0, s, ra, g, a)
+    if (G <= 8)
+        RL_RCS(8, 1);
+    else if (G <= 16)
+        RL_RCS(16, 1);
+    else if (G <= 32)
+        RL_RCS(32, 1);
+    else if (G <= 64)
+        RL_RCS(64, 1);
+    else if (G <= 128)
+        RL_RCS(64, 2);
+    else if (G <= 192)
+        RL_RCS(64, 3);
+    else
+        RL_RCS(64, 4);
+#undef RL_RCS
+}
+
 void launch_group(const PairIds& pid, int32_t T, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
                   int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* tile_hist, ItemRec* items, int maxrec,
-                  hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr, size_t zero_bytes = 0) {
+                  hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr, size_t zero_bytes = 0,
+                  const RouteArgs* route = nullptr) {
     GroupArgs g;
     g.zero = static_cast<u32x4*>(zero);
     g.nzero = zero != nullptr ? (int)(zero_bytes / 16) : 0;
@@ -201,9 +236,25 @@ void launch_group(const PairIds& pid, int32_t T, int32_t E, const rl_expert_desc
     g.tile_hist = tile_hist;
     g.P = T * pid.kk;
     g.E = E;
-    g.ntiles = group_tiles(g.P) > 0 ? group_tiles(g.P) : 1;
+    g.tp = route != nullptr ? (GT / pid.kk) * pid.kk : GT;  // token-aligned tiles when routing here
+    g.ntiles = group_tiles(g.P, g.tp) > 0 ? group_tiles(g.P, g.tp) : 1;
     g.nflags = FLAGS_WORDS;
-    if (split != nullptr && split->rows > 0) {
+    if (route != nullptr) {
+        SplitArgs a = {};
+        if (split != nullptr) a = *split;
+        a.K = split != nullptr ? split->K : 256;
+        const int E_r = route->n_route;
+        if (E_r <= 64)
+            launch_route_count_split<1>(*route, g, a, s);
+        else if (E_r <= 128)
+            launch_route_count_split<2>(*route, g, a, s);
+        else if (E_r <= 256)
+            launch_route_count_split<4>(*route, g, a, s);
+        else if (E_r <= 512)
+            launch_route_count_split<8>(*route, g, a, s);
+        else
+            launch_route_count_split<16>(*route, g, a, s);
+    } else if (split != nullptr && split->rows > 0) {
         const SplitArgs& a = *split;
         const int G = a.K / 32;  // K <= 8192: G <= 256
 #define RL_CSPLIT(LPR, NG)                                                                                      \
@@ -457,9 +508,10 @@ void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* 
     sa.scale = xscale;
     sa.rows = T;
     sa.K = ex->H;
+    RouteArgs ra{r.logits, const_cast<int32_t*>(r.ids), const_cast<float*>(r.w), T, r.n_route, r.kin};
     launch_group(r.pid(), T, ex->E, ex->desc, at<int32_t>(ws, L.offsets), pair_src, at<int32_t>(ws, L.inv), flags,
                  at<int32_t>(ws, L.tile_hist), items, L.maxrec, s, present[QT_T1] ? &sa : nullptr,
-                 at<void>(ws, L.yexp), L.yspare - L.yexp);
+                 at<void>(ws, L.yexp), L.yspare - L.yexp, r.logits != nullptr ? &ra : nullptr);
     mark(1);
     const int64_t P = (int64_t)T * kk;
     GuArgs b = {};
@@ -602,6 +654,18 @@ int rl_moe_prefill_block(const uint16_t* x, const int32_t* topk_ids, const float
     return prefill_impl(x, r, experts, out, T, workspace, ws_bytes, stream, nullptr);
 }
 
+int rl_moe_prefill_from_logits(const uint16_t* x, const float* logits, int32_t n_route, const rl_expert_blobs* experts,
+                               int32_t shared_expert, const float* shared_gate, const float* residual, float* out,
+                               int32_t* topk_ids, float* topk_w, int32_t T, int32_t k, void* workspace,
+                               size_t ws_bytes, void* stream) {
+    if (k < 1) return RL_ESHAPE;
+    if (T > 0 && !logits) return RL_EINVAL;
+    Route r{topk_ids, topk_w, k, shared_expert < 0 ? -1 : shared_expert, shared_gate, residual};
+    r.logits = logits;
+    r.n_route = n_route;
+    return prefill_impl(x, r, experts, out, T, workspace, ws_bytes, stream, nullptr);
+}
+
 int rl_moe_prefill_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                            const rl_expert_blobs* experts, float* out, int32_t T, int32_t k, void* stream) {
     int present[3] = {0, 0, 0};
@@ -728,8 +792,7 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
     if (!offsets || (T > 0 && (!topk_ids || !pair_src || !inv))) return RL_EINVAL;
     if (!workspace || ((uintptr_t)workspace % ALIGN)) return RL_EWORKSPACE;
     const Layout L = layout(T, k, E, 256, 64);
-    if (ws_bytes < L.tile_hist + (size_t)(group_tiles((int64_t)T * k) > 0 ? group_tiles((int64_t)T * k) : 1) * E * 4)
-        return RL_EWORKSPACE;
+    if (ws_bytes < L.tile_hist + (size_t)tile_hist_rows((int64_t)T * k) * E * 4) return RL_EWORKSPACE;
     launch_group(PairIds{topk_ids, k, k, -1}, T, E, nullptr, offsets, pair_src, inv, at<int32_t>(workspace, L.flags),
                  at<int32_t>(workspace, L.tile_hist), nullptr, 0, static_cast<hipStream_t>(stream));
     return hip_status();

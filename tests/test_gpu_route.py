@@ -118,3 +118,45 @@ def test_routed_layer_other_k(orc, rl, k):
     err = rel_l2(out, ref)
     log(f"  k={k} routed layer rel_l2 {err:.3e}")
     assert err <= 2e-3 and rl.status(ws)[0] == 0
+
+
+# ----------------------------------------------------------------------------- router fused with the grouping
+@pytest.mark.parametrize(
+    "name,T,E,k,shared,ties",
+    [("tiny", 64, 8, 2, False, False), ("t1_2048", 300, 64, 10, False, False), ("mixed_2048", 257, 48, 7, True, False),
+     ("t1_2048", 2048, 512, 10, False, False), ("q2b_1090", 1090, 512, 10, True, False),
+     ("mixed_2048", 199, 32, 16, False, True)],
+)
+def test_prefill_from_logits(orc, rl, name, T, E, k, shared, ties):
+    """rl_moe_prefill_from_logits routes in the grouping's first launch: its topk_ids equal the
+    oracle router's bit for bit (weights within 4e-6, and bit-identical to rl_moe_route's), and its
+    layer output is bit-identical to rl_moe_prefill (or rl_moe_prefill_block) on that routing --
+    the pairs' sorted order is unique, so the token-aligned grouping tiles change nothing."""
+    import torch
+
+    from workload import make_block_workload
+
+    bw = make_block_workload(name, seed=300 + k, T=T, E=E, k=k)
+    wl = bw.wl
+    ex = rl.DeviceExperts.from_workload(wl.experts)
+    if ties:
+        lg = np.random.default_rng(301).integers(-2, 3, size=(T, E)).astype(np.float32)
+    else:
+        lg = gen_logits(T, E, seed=302 + E, bias=zipf_bias(E, 303) if name == "q2b_1090" else None)
+    x = torch.from_numpy(wl.x.view(np.int16).copy()).cuda()
+    lgd = torch.from_numpy(lg).cuda()
+    g = torch.from_numpy(bw.gate).cuda()
+    r = torch.from_numpy(bw.residual).cuda()
+    sh = bw.shared if shared else -1
+    log(f"from logits {name} T={T} E={E}(+shared) k={k} shared={shared} ties={ties}")
+    out, ids, w = rl.prefill_from_logits(x, lgd, k, ex, shared=sh, gate=g, residual=r)
+    rids, rw = orc.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert (np.abs(w.cpu().numpy().astype(np.float64) - rw) / rw).max() <= WTOL
+    ids2, w2 = rl.route(lgd, k)
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    if shared:
+        ref = rl.prefill_block(x, ids, w, ex, bw.shared, g, r)
+    else:
+        ref = rl.prefill(x, ids, w, ex)
+    assert torch.equal(out, ref)
