@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 # half the fp8 peak, which equals the dense bf16/fp16 MFMA peak (256 CU x 4 SIMD x 1024 FLOP/clk
 # x 2.4 GHz).
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # the fp8 MFMA rate the T1 kernels issue at (AMD: 5.0 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0
 STAGES = ("group", "gate_up", "hsplit", "down", "combine")  # group includes the split of x
 KERNEL_SOURCES = ("routed_experts_bit_amd/csrc/rl_kernels.h", "routed_experts_bit_amd/csrc/rl_decode.h")
@@ -67,7 +68,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps first (the GPU takes some tens of ms of load to reach its steady clocks)")
+                    help="untimed layer steps before the timed ones (the 1-2 row and router measurements run "
+                         "first, so the GPU is already under load)")
     ap.add_argument("--config", default="t1_2048")
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--rotate", type=int, default=3, help="distinct arena copies cycled through")
@@ -129,66 +131,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # warm-up
-    for i in range(args.warmup):
-        layer(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    assert rl.status(ws)[0] == 0
-
-    # timed region: K steps, rotating weight sets
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        layer(sets[i % len(sets)])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # per-step times (one event pair around each step's calls; each interval also holds one
-    # event's overhead) for the median and the minimum
-    ev_steps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ev_steps[i][0].record(stream)
-        layer(sets[i % len(sets)])
-        ev_steps[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([a_.elapsed_time(b_) for a_, b_ in ev_steps])
-
-    # same number of steps with events between the kernels (on the stream the kernels run on)
-    # (per chunk; a step's stage time is the sum over its chunks)
-    ne = rl.TIMED_EVENTS
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in spans] for _ in range(args.steps)]
-    for step_evs in evs:  # torch creates the HIP event on its first record
-        for row in step_evs:
-            for e in row:
-                e.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        for (c0, c1), row in zip(spans, evs[i]):
-            rl.prefill_timed(x[c0:c1], ids[c0:c1], w[c0:c1], sets[i % len(sets)], out[c0:c1], ws, row)
-    torch.cuda.synchronize()
-    stage = np.array([[sum(row[j].elapsed_time(row[j + 1]) for row in evs[i]) for j in range(ne - 1)]
-                      for i in range(args.steps)])
-    st_ms = dict(zip(STAGES, stage.mean(axis=0)))
-
-    # warm (same weights every step) for context
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        layer(dev)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_warm = e0.elapsed_time(e1) / args.steps
-
-    gpu_out = out.cpu().numpy().astype(np.float64)
-
     # the 1-2 row path (decode and 2-row verify) on the same experts: each step its own seeded
     # routing and x, weight sets rotating as above; weight bytes = the distinct experts' 3 matrices
     from workload.gen import _routing, gen_x, matrix_bytes
+
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
 
     qt = ex0.qtypes
 
@@ -256,6 +205,110 @@ def main():
               "GB_s_graph": round(r_bytes / r_us_g / 1e3, 1),
               "pct_hbm_peak_graph": round(100 * r_bytes / r_us_g / 1e3 / PEAK_HBM_GBS, 2)}
     log(f"[bench] router: {r_us:.2f} us per call, {r_us_g:.2f} us per call from a graph ({router['GB_s_graph']} GB/s)")
+    # the MoE block (shared expert + residual, rl_moe_prefill_block) and the router fused with the
+    # grouping (rl_moe_prefill_from_logits) against the router and the layer as two calls, on the
+    # same workload with one more (shared) expert of the same block type (run before the layer's
+    # warm-up and timed steps, which then start on a GPU under load)
+    from workload import make_block_workload
+
+    bw = make_block_workload(args.config, seed=args.seed)
+    bdev = rl.DeviceExperts.from_workload(bw.wl.experts)
+    bsets = [bdev] + [bdev.with_arena(bdev.arena.clone()) for _ in range(max(args.rotate, 1) - 1)]
+    gate = torch.from_numpy(bw.gate).cuda()
+    resid = torch.from_numpy(bw.residual).cuda()
+    lg_b = torch.from_numpy(gen_logits(T, E, args.seed + 2, zipf_bias(E, args.seed + 3) if wl.meta.get("bias") == "zipf"
+                                       else None)).cuda()
+    ws_b = torch.empty(rl.workspace_bytes(min(T, chunk), k + 1, E + 1, H, I), dtype=torch.uint8, device="cuda")
+    ids_r = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_r = torch.empty((T, k), dtype=torch.float32, device="cuda")
+
+    def block_layer(exps):
+        for c0, c1 in spans:
+            rl.prefill_block(x[c0:c1], ids[c0:c1], w[c0:c1], exps, bw.shared, gate[c0:c1], resid[c0:c1],
+                             out=out[c0:c1], ws=ws_b)
+
+    def fused_route_layer(exps):
+        for c0, c1 in spans:
+            rl.prefill_from_logits(x[c0:c1], lg_b[c0:c1], k, exps, out=out[c0:c1], ids=ids_r[c0:c1],
+                                   w=w_r[c0:c1], ws=ws)
+
+    def split_route_layer(exps):
+        for c0, c1 in spans:
+            rl.route(lg_b[c0:c1], k, ids_r[c0:c1], w_r[c0:c1])
+            rl.prefill(x[c0:c1], ids_r[c0:c1], w_r[c0:c1], exps, out=out[c0:c1], ws=ws)
+
+    def time_layer(fn, sets_):
+        for i in range(5):
+            fn(sets_[i % len(sets_)])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(sets_[i % len(sets_)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_block = time_layer(block_layer, bsets)
+    ms_fused = time_layer(fused_route_layer, sets)
+    ms_split = time_layer(split_route_layer, sets)
+    del bsets, bdev
+    log(f"[bench] MoE block (shared expert + residual): {ms_block * 1e3:.1f} us/layer; router + layer: fused "
+        f"{ms_fused * 1e3:.1f} us, two calls {ms_split * 1e3:.1f} us")
+    # warm-up
+    for i in range(args.warmup):
+        layer(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    assert rl.status(ws)[0] == 0
+
+    # timed region: K steps, rotating weight sets
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        layer(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-step times (one event pair around each step's calls; each interval also holds one
+    # event's overhead) for the median and the minimum
+    ev_steps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev_steps[i][0].record(stream)
+        layer(sets[i % len(sets)])
+        ev_steps[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a_.elapsed_time(b_) for a_, b_ in ev_steps])
+
+    # same number of steps with events between the kernels (on the stream the kernels run on)
+    # (per chunk; a step's stage time is the sum over its chunks)
+    ne = rl.TIMED_EVENTS
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in spans] for _ in range(args.steps)]
+    for step_evs in evs:  # torch creates the HIP event on its first record
+        for row in step_evs:
+            for e in row:
+                e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for (c0, c1), row in zip(spans, evs[i]):
+            rl.prefill_timed(x[c0:c1], ids[c0:c1], w[c0:c1], sets[i % len(sets)], out[c0:c1], ws, row)
+    torch.cuda.synchronize()
+    stage = np.array([[sum(row[j].elapsed_time(row[j + 1]) for row in evs[i]) for j in range(ne - 1)]
+                      for i in range(args.steps)])
+    st_ms = dict(zip(STAGES, stage.mean(axis=0)))
+
+    # warm (same weights every step) for context
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        layer(dev)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / args.steps
+
+    gpu_out = out.cpu().numpy().astype(np.float64)
+
+
     tflops = flops / (ms_step * 1e-3) / 1e12
     gu_tflops = flops_gateup / (st_ms["gate_up"] * 1e-3) / 1e12
     log(f"[bench] {ms_step * 1e3:.1f} us/layer = {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.2f}% of bf16 "
@@ -273,7 +326,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",  # T1 experts: e4m3 operands (x and h as exact hi + lo pairs), fp32 accumulation
+        # T1 experts on the fp8 MFMA: weights s*t exact in e4m3, bf16 x carried exactly as hi + lo e4m3
+        # pairs (h with 8 significant bits), fp32 accumulation: bf16-class arithmetic
+        "dtype": "bf16-equivalent (fp8 e4m3 hi+lo operands, fp32 accumulation)",
         "data": "synthetic",
         "config": {
             "workload": f"{args.config}: {T} tokens x {E} experts x top-{k}, hidden {H}, intermediate {I}, "
@@ -301,25 +356,37 @@ def main():
                                 "type)"}[wl.meta["types"]],
             "bound": "mfma",
             "achieved": round(gu_tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
+            # the kernel issues fp8 MFMAs (T1; Q2B: bf16 at the same time per product), two per useful
+            # product (activation hi and lo): frac against the fp8 peak, and against half of it
+            "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 5),
+            "frac": round(gu_tflops / PEAK_FP8_TFLOPS, 5),
+            "frac_of_hi_lo_ceiling": round(gu_tflops / PEAK_BF16_TFLOPS, 5),
             "traffic": measured_traffic(args.config),
         },
+        "moe_block_ms_per_layer": round(ms_block, 5),
+        "router_fused_ms_per_layer": round(ms_fused, 5),
+        "router_then_layer_ms": round(ms_split, 5),
     }
 
     if not args.no_oracle:
         import oracle
 
-        nthr = args.oracle_threads or min(16, os.cpu_count() or 1)
+        nthr = args.oracle_threads or oracle.default_threads()
         t1 = time.time()
         ref = oracle.moe_workload(wl, threads=nthr)
         cpu_s = time.time() - t1
         err = float(np.linalg.norm(gpu_out - ref) / np.linalg.norm(ref))
+        try:
+            affinity = len(os.sched_getaffinity(0))
+        except (AttributeError, OSError):
+            affinity = None
         result["cpu_baseline"] = {"value": round(flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": nthr,
                                   "kind": "oracle", "ms_per_layer": round(cpu_s * 1e3, 1),
+                                  "host_cpus": os.cpu_count(), "cpus_available": affinity,
                                   "sample": f"the whole {args.config} layer once (all {T * k} pairs; same inputs), "
-                                            f"C, float64, {nthr} threads"}
+                                            f"C, float64, {nthr} threads (the cores this process may use, capped "
+                                            f"by OMP_NUM_THREADS)"}
         result["parity_rel_l2_vs_oracle"] = err
         log(f"[bench] oracle {cpu_s:.1f}s on {nthr} threads; GPU vs oracle rel_l2 {err:.3e}")
     print(json.dumps(result), flush=True)
