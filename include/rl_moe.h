@@ -123,9 +123,9 @@ int rl_moe_prefill_block(const uint16_t* x, const int32_t* topk_ids, const float
                          size_t ws_bytes, void* stream);
 
 /* The router and the layer in one call: every token's k experts are chosen among experts
- * [0, n_route) from its fp32 logits exactly as rl_moe_route chooses them, inside the first launch
- * of the pair grouping (the router's work-groups also count their pairs per expert), and written
- * to topk_ids / topk_w; then the layer (with shared_expert >= 0 the MoE block, as
+ * [0, n_route) from its fp32 logits exactly as rl_moe_route chooses them (its kernel, launched
+ * first on the stream) and written to topk_ids / topk_w; then the layer (with shared_expert >= 0
+ * the MoE block, as
  * rl_moe_prefill_block; shared_expert < 0: the routed experts only, shared_gate and residual
  * ignored) runs on them.
  *   logits    [dev] float [T][n_route], 4-byte aligned, finite

@@ -194,34 +194,9 @@ int check_layer(const void* x, const Route& r, const rl_expert_blobs* ex, const 
 }
 
 // Pair grouping; with split != NULL the split of x runs in the histogram launch.
-template <int NR>
-void launch_route_count_split(const RouteArgs& ra, const GroupArgs& g, const SplitArgs& a, hipStream_t s) {
-    const int G = a.K / 32;  // K <= 8192: G <= 256
-    const int nsplit = a.rows > 0 ? a.rows : 0;
-#define RL_RCS(LPR, NG)                                                                                              \
-    hipLaunchKernelGGL((k_route_count_split<NR, LPR, NG>), dim3(g.ntiles + (nsplit + 256 / LPR - 1) / (256 / LPR)), \
-                       dim3(256), 0, s, ra, g, a)
-    if (G <= 8)
-        RL_RCS(8, 1);
-    else if (G <= 16)
-        RL_RCS(16, 1);
-    else if (G <= 32)
-        RL_RCS(32, 1);
-    else if (G <= 64)
-        RL_RCS(64, 1);
-    else if (G <= 128)
-        RL_RCS(64, 2);
-    else if (G <= 192)
-        RL_RCS(64, 3);
-    else
-        RL_RCS(64, 4);
-#undef RL_RCS
-}
-
 void launch_group(const PairIds& pid, int32_t T, int32_t E, const rl_expert_desc* desc, int32_t* offsets,
                   int32_t* pair_src, int32_t* inv, int32_t* flags, int32_t* tile_hist, ItemRec* items, int maxrec,
-                  hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr, size_t zero_bytes = 0,
-                  const RouteArgs* route = nullptr) {
+                  hipStream_t s, const SplitArgs* split = nullptr, void* zero = nullptr, size_t zero_bytes = 0) {
     GroupArgs g;
     g.zero = static_cast<u32x4*>(zero);
     g.nzero = zero != nullptr ? (int)(zero_bytes / 16) : 0;
@@ -236,27 +211,13 @@ void launch_group(const PairIds& pid, int32_t T, int32_t E, const rl_expert_desc
     g.tile_hist = tile_hist;
     g.P = T * pid.kk;
     g.E = E;
-    g.tp = route != nullptr ? (GT / pid.kk) * pid.kk : GT;  // token-aligned tiles when routing here
-    g.ntiles = group_tiles(g.P, g.tp) > 0 ? group_tiles(g.P, g.tp) : 1;
+    g.tp = GT;
+    g.ntiles = group_tiles(g.P) > 0 ? group_tiles(g.P) : 1;
     g.nflags = FLAGS_WORDS;
-    if (route != nullptr) {
-        SplitArgs a = {};
-        if (split != nullptr) a = *split;
-        a.K = split != nullptr ? split->K : 256;
-        const int E_r = route->n_route;
-        if (E_r <= 64)
-            launch_route_count_split<1>(*route, g, a, s);
-        else if (E_r <= 128)
-            launch_route_count_split<2>(*route, g, a, s);
-        else if (E_r <= 256)
-            launch_route_count_split<4>(*route, g, a, s);
-        else if (E_r <= 512)
-            launch_route_count_split<8>(*route, g, a, s);
-        else
-            launch_route_count_split<16>(*route, g, a, s);
-    } else if (split != nullptr && split->rows > 0) {
+    const int nsplit = split != nullptr && split->rows > 0 ? split->rows : 0;
+    const int G = split != nullptr ? split->K / 32 : 8;  // K <= 8192: G <= 256
+    if (nsplit > 0) {
         const SplitArgs& a = *split;
-        const int G = a.K / 32;  // K <= 8192: G <= 256
 #define RL_CSPLIT(LPR, NG)                                                                                      \
     hipLaunchKernelGGL((k_count_split<LPR, NG>), dim3(g.ntiles + (a.rows + 256 / LPR - 1) / (256 / LPR)), \
                        dim3(256), 0, s, g, a)
@@ -483,6 +444,23 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
 // holds a chunk's activations in LDS (I a multiple of 256, at most DN_KMAX).
 bool t1_splits_h(const int present[3], int32_t I) { return present[QT_T1] > 0 && I % 256 == 0 && I <= DN_KMAX; }
 
+// The router: one wave per token, NR logits per lane.
+void launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* w, hipStream_t s) {
+    const dim3 grid((unsigned)((T + 3) / 4));
+#define RL_RT(NR) hipLaunchKernelGGL(k_route<NR>, grid, dim3(256), 0, s, logits, T, E, k, ids, w)
+    if (E <= 64)
+        RL_RT(1);
+    else if (E <= 128)
+        RL_RT(2);
+    else if (E <= 256)
+        RL_RT(4);
+    else if (E <= 512)
+        RL_RT(8);
+    else
+        RL_RT(16);
+#undef RL_RT
+}
+
 // Upper bound of the work records of one block type (its experts, plus one per REC_PAIRS pairs).
 int records_bound(int n_experts, int64_t P) { return n_experts + (int)((P + REC_PAIRS - 1) / REC_PAIRS); }
 
@@ -508,10 +486,11 @@ void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* 
     sa.scale = xscale;
     sa.rows = T;
     sa.K = ex->H;
-    RouteArgs ra{r.logits, const_cast<int32_t*>(r.ids), const_cast<float*>(r.w), T, r.n_route, r.kin};
+    if (r.logits != nullptr)  // the router writes the call's selections first
+        launch_route(r.logits, T, r.n_route, r.kin, const_cast<int32_t*>(r.ids), const_cast<float*>(r.w), s);
     launch_group(r.pid(), T, ex->E, ex->desc, at<int32_t>(ws, L.offsets), pair_src, at<int32_t>(ws, L.inv), flags,
                  at<int32_t>(ws, L.tile_hist), items, L.maxrec, s, present[QT_T1] ? &sa : nullptr,
-                 at<void>(ws, L.yexp), L.yspare - L.yexp, r.logits != nullptr ? &ra : nullptr);
+                 at<void>(ws, L.yexp), L.yspare - L.yexp);
     mark(1);
     const int64_t P = (int64_t)T * kk;
     GuArgs b = {};
@@ -769,20 +748,7 @@ int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
     if (T == 0) return RL_OK;
     if (!logits || !topk_ids || !topk_w) return RL_EINVAL;
     if (((uintptr_t)logits | (uintptr_t)topk_ids | (uintptr_t)topk_w) & 3) return RL_EINVAL;
-    const dim3 grid((unsigned)((T + 3) / 4));
-    hipStream_t s = static_cast<hipStream_t>(stream);
-#define RL_RT(NR) hipLaunchKernelGGL(k_route<NR>, grid, dim3(256), 0, s, logits, T, E, k, topk_ids, topk_w)
-    if (E <= 64)
-        RL_RT(1);
-    else if (E <= 128)
-        RL_RT(2);
-    else if (E <= 256)
-        RL_RT(4);
-    else if (E <= 512)
-        RL_RT(8);
-    else
-        RL_RT(16);
-#undef RL_RT
+    launch_route(logits, T, E, k, topk_ids, topk_w, static_cast<hipStream_t>(stream));
     return hip_status();
 }
 

@@ -5,8 +5,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "rl_kernels.h"
-
 namespace rl {
 
 // Router: one wave per token.  Lane l holds logits l, l + 64, ..., l + 64 (NR - 1) (NR = the
@@ -77,47 +75,6 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
         ids[(size_t)t * k + lane] = id;
         w[(size_t)t * k + lane] = wt;
     }
-}
-
-// The router fused with the first launch of the pair grouping: work-groups [0, ntiles) each
-// route the tokens of one grouping tile (g.tp / kk tokens, one wave per token at a time), write
-// their topk_ids / topk_w and count the tile's pairs per expert in LDS (the shared expert's pair
-// of every token included); the other work-groups split x (as k_count_split).  The grouping's
-// scatter then reads the ids this launch wrote.
-struct RouteArgs {
-    const float* logits;  // [T][n_route]
-    int32_t* ids;         // [T][k], written
-    float* w;             // [T][k], written
-    int T, n_route, k;
-};
-
-template <int NR, int LPR, int NG>
-__global__ __launch_bounds__(256) void k_route_count_split(RouteArgs ra, GroupArgs g, SplitArgs a) {
-    clear_words(g);
-    if ((int)blockIdx.x >= g.ntiles) {
-        split_rows<SPLIT_X, LPR, NG>(a, blockIdx.x - g.ntiles);
-        return;
-    }
-    __shared__ int32_t h[MAX_E];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, tile = blockIdx.x;
-    if (tile == 0 && tid < g.nflags) g.flags[tid] = 0;
-    for (int e = tid; e < g.E; e += 256) h[e] = 0;
-    __syncthreads();
-    const int tpt = g.tp / g.pid.kk;  // tokens per tile
-    const int t0 = tile * tpt, t1 = min(ra.T, t0 + tpt);
-    for (int t = t0 + wave; t < t1; t += 4) {
-        int id;
-        float wt;
-        route_token<NR>(ra.logits + (size_t)t * ra.n_route, ra.n_route, ra.k, lane, id, wt);
-        if (lane < ra.k) {
-            ra.ids[(size_t)t * ra.k + lane] = id;
-            ra.w[(size_t)t * ra.k + lane] = wt;
-            atomicAdd(&h[id], 1);
-        }
-    }
-    if (g.pid.shared >= 0 && tid == 0 && t1 > t0) atomicAdd(&h[g.pid.shared], t1 - t0);
-    __syncthreads();
-    for (int e = tid; e < g.E; e += 256) g.tile_hist[(size_t)tile * g.E + e] = h[e];
 }
 
 }  // namespace rl
