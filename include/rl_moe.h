@@ -41,7 +41,8 @@ extern "C" {
 #define RL_EWORKSPACE (-3) /* workspace NULL, too small, or not 256-byte aligned */
 #define RL_EHIP (-4)       /* the HIP runtime reported an error at launch */
 #define RL_EQTYPE (-5)     /* the host descriptor copy names an unknown block type */
-#define RL_ETOOBIG (-6)    /* the call needs more scratch than the library's static buffer holds */
+#define RL_ETOOBIG (-6)    /* the call needs more than a fixed-size resource holds (the no-allocation
+                              * scratch buffer, or an expert cache's slots) */
 
 /* Block types.  Both use 256-value blocks that tile a matrix flattened row-major; rows are
  * output features, the input dimension is contiguous.
@@ -249,6 +250,53 @@ int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk
  * asynchronous. */
 int rl_moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
                  void* stream);
+
+/* Bounded expert cache (dev72 "The 2-row verify with a bounded expert cache"): the layer's experts
+ * stay in host memory and a fixed number of device slots hold the ones the next call needs.  A
+ * prepare makes every expert of a request resident at once -- for a 2-row verify, the union of
+ * both rows' selections, so that no row's experts are evicted while the other row is in flight --
+ * and evicts, for the request's missing experts, the least recently requested experts outside
+ * it (free slots first, lowest index first).  Each row then runs with its own selection order
+ * (rl_moe_decode / rl_moe_decode_block on the view the prepare returns), bit-identical to a run on
+ * the whole resident arena.  The cache object is host memory owned by the library (create /
+ * destroy); the slots and the device descriptor table are the caller's device memory.  A cache is
+ * used by one host thread at a time. */
+typedef struct rl_cache rl_cache;
+
+/* Bytes of one slot: the three matrices of an expert of either block type, each 256-byte
+ * aligned; 0 for unsupported H / I. */
+uint64_t rl_cache_slot_bytes(int32_t H, int32_t I);
+
+/* host_arena [host]: the layer's packed experts, host_arena_bytes long, laid out per host_desc
+ * [host] (E descriptors, offsets into host_arena; copied by the call).  Pinned host memory
+ * (hipHostMalloc) lets the copies of prepare run asynchronously; it must stay valid and unchanged
+ * for the cache's lifetime.  slots [dev]: n_slots * rl_cache_slot_bytes(H, I) bytes, 256-byte
+ * aligned, n_slots in [1, E]; dev_desc [dev]: E descriptors, 8-byte aligned, which the cache keeps
+ * naming each expert's slot (experts not resident name slot 0 and must not be routed to).  With
+ * slots = NULL (and dev_desc NULL) the cache only plans: residency, hits, misses and evictions are
+ * tracked, nothing is copied.  Synchronises the NULL stream once (the initial table).  *out
+ * receives the cache; RL_ESHAPE / RL_EINVAL / RL_EQTYPE as the layer calls define them. */
+int rl_cache_create(const void* host_arena, uint64_t host_arena_bytes, const rl_expert_desc* host_desc, int32_t E,
+                    int32_t H, int32_t I, void* slots, int32_t n_slots, rl_expert_desc* dev_desc, rl_cache** out);
+
+/* Make the experts ids [host] (n ids, duplicates allowed) resident together.  Missing experts are
+ * copied from the host arena into their slots and the changed descriptors written to dev_desc, all
+ * enqueued on `stream` (calls that use the view must follow on that stream); the descriptor
+ * entries travel in kernel arguments, so later prepares never change what an earlier enqueued
+ * call reads.  blobs [host] (may be NULL) receives the device view: arena = slots, desc = dev_desc,
+ * desc_host = the cache's host copy of the table (valid until the next prepare or destroy), E, H,
+ * I, arena_bytes.  RL_ETOOBIG if the request names more distinct experts than there are slots
+ * (nothing changes); RL_EINVAL for an id outside [0, E); RL_EHIP if a copy could not be enqueued
+ * (the cache must then be destroyed). */
+int rl_cache_prepare(rl_cache* cache, const int32_t* ids, int32_t n, rl_expert_blobs* blobs, void* stream);
+
+/* stats [host] int64 [4]: prepares, hits, misses (experts copied in), evictions. */
+int rl_cache_stats(const rl_cache* cache, int64_t* stats);
+
+/* Slot holding expert e, or -1 if it is not resident. */
+int32_t rl_cache_slot_of(const rl_cache* cache, int32_t e);
+
+void rl_cache_destroy(rl_cache* cache);
 
 /* Device status flags of the last call that used `workspace` [dev]; the caller must have
  * synchronised the stream.  flags_out [host] int32 [4].  Blocking copy. */

@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     prefill_block,
     decode_block,
     prefill_from_logits,
+    ExpertCache,
+    CachedExperts,
     noalloc_status,
     NOALLOC_SCRATCH_BYTES,
     TIMED_EVENTS,

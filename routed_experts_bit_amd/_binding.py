@@ -35,6 +35,15 @@ EXPORTS = (
     "rl_moe_decode_block",
     "rl_moe_prefill_from_logits",
 )
+# the bounded expert cache (include/rl_moe.h, rl_cache_*)
+CACHE_EXPORTS = (
+    "rl_cache_slot_bytes",
+    "rl_cache_create",
+    "rl_cache_prepare",
+    "rl_cache_stats",
+    "rl_cache_slot_of",
+    "rl_cache_destroy",
+)
 NOALLOC_SCRATCH_BYTES = 40 << 20  # RL_NOALLOC_SCRATCH_BYTES
 
 
@@ -95,6 +104,18 @@ def lib():
     L.rl_moe_dequant.restype = C.c_int
     L.rl_moe_route.argtypes = [P, I32, I32, I32, P, P, P]
     L.rl_moe_route.restype = C.c_int
+    L.rl_cache_slot_bytes.argtypes = [I32, I32]
+    L.rl_cache_slot_bytes.restype = C.c_uint64
+    L.rl_cache_create.argtypes = [P, C.c_uint64, P, I32, I32, I32, P, I32, P, C.POINTER(C.c_void_p)]
+    L.rl_cache_create.restype = C.c_int
+    L.rl_cache_prepare.argtypes = [P, P, I32, C.POINTER(_Blobs), P]
+    L.rl_cache_prepare.restype = C.c_int
+    L.rl_cache_stats.argtypes = [P, P]
+    L.rl_cache_stats.restype = C.c_int
+    L.rl_cache_slot_of.argtypes = [P, I32]
+    L.rl_cache_slot_of.restype = I32
+    L.rl_cache_destroy.argtypes = [P]
+    L.rl_cache_destroy.restype = None
     L.rl_moe_status.argtypes = [P, P]
     L.rl_moe_status.restype = C.c_int
     L.rl_moe_strerror.argtypes = [C.c_int]
@@ -105,7 +126,7 @@ def lib():
 
 def exported_symbols():
     L = lib()
-    return {name: hasattr(L, name) for name in EXPORTS}
+    return {name: hasattr(L, name) for name in EXPORTS + CACHE_EXPORTS}
 
 
 def strerror(code: int) -> str:
@@ -503,3 +524,85 @@ def status(ws):
     buf = (C.c_int32 * 4)()
     _check(lib().rl_moe_status(_ptr(ws), C.cast(buf, C.c_void_p)), "rl_moe_status")
     return list(buf)
+
+
+class ExpertCache:
+    """Bounded expert cache (rl_cache_*): the experts stay in host memory (`host_arena`: a uint8
+    tensor, pinned for asynchronous copies, or a numpy array in planning mode) and `n_slots`
+    device slots hold the ones a prepare requests.  With plan_only=True nothing touches the GPU:
+    the cache tracks residency, hits, misses and evictions only."""
+
+    def __init__(self, host_arena, desc_np: np.ndarray, E: int, H: int, I: int, n_slots: int, plan_only=False,
+                 device="cuda"):
+        self.E, self.H, self.I, self.n_slots = int(E), int(H), int(I), int(n_slots)
+        self.desc_host = np.ascontiguousarray(desc_np)
+        self.host_arena = host_arena
+        L = lib()
+        sb = int(L.rl_cache_slot_bytes(self.H, self.I))
+        if sb == 0:
+            raise RlError(f"unsupported H={H} I={I}")
+        if isinstance(host_arena, np.ndarray):
+            hptr, hbytes = host_arena.ctypes.data, host_arena.nbytes
+        else:
+            hptr, hbytes = host_arena.data_ptr(), host_arena.numel()
+        if plan_only:
+            self.slots, self.dev_desc = None, None
+        else:
+            torch = _torch()
+            self.slots = torch.empty(self.n_slots * sb, dtype=torch.uint8, device=device)
+            self.dev_desc = torch.empty(self.E * 32, dtype=torch.uint8, device=device)
+        h = C.c_void_p(0)
+        rc = L.rl_cache_create(C.c_void_p(hptr), hbytes, self.desc_host.ctypes.data, self.E, self.H, self.I,
+                               _ptr(self.slots), self.n_slots, _ptr(self.dev_desc), C.byref(h))
+        _check(rc, "rl_cache_create")
+        self._h = h
+        self._blobs = _Blobs()
+
+    def prepare(self, ids) -> "CachedExperts":
+        """Make the experts of ids (host array-like of ints) resident together; returns the view the
+        layer calls take in place of DeviceExperts."""
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+        rc = lib().rl_cache_prepare(self._h, a.ctypes.data if a.size else None, a.size, C.byref(self._blobs),
+                                    None if self.slots is None else _stream())
+        _check(rc, "rl_cache_prepare")
+        return CachedExperts(self)
+
+    def stats(self):
+        buf = (C.c_int64 * 4)()
+        _check(lib().rl_cache_stats(self._h, C.cast(buf, C.c_void_p)), "rl_cache_stats")
+        return dict(prepares=buf[0], hits=buf[1], misses=buf[2], evictions=buf[3])
+
+    def slot_of(self, e: int) -> int:
+        return int(lib().rl_cache_slot_of(self._h, int(e)))
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            lib().rl_cache_destroy(self._h)
+            self._h = C.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class CachedExperts:
+    """The device view of an ExpertCache after a prepare (arena = its slots): usable wherever a
+    DeviceExperts is, until the next prepare of the same cache."""
+
+    def __init__(self, cache: ExpertCache):
+        self.E, self.H, self.I = cache.E, cache.H, cache.I
+        self.arena, self.desc = cache.slots, cache.dev_desc
+        self._blobs = _Blobs(cache._blobs.arena, cache._blobs.desc, cache._blobs.desc_host, cache._blobs.E,
+                             cache._blobs.H, cache._blobs.I, cache._blobs.arena_bytes)
+        self.desc_host = cache.desc_host  # block types (the cache keeps each expert's type)
+        self._cache = cache
+
+    @property
+    def blobs(self):
+        return C.byref(self._blobs)
+
+    @property
+    def qtypes(self) -> np.ndarray:
+        return self.desc_host["qtype"]

@@ -811,7 +811,7 @@ const char* rl_moe_strerror(int status) {
         case RL_EWORKSPACE: return "workspace missing, misaligned or too small";
         case RL_EHIP: return "HIP runtime error at launch";
         case RL_EQTYPE: return "unknown block type in the expert descriptors";
-        case RL_ETOOBIG: return "the call needs more scratch than the no-allocation buffer holds";
+        case RL_ETOOBIG: return "the call needs more than a fixed-size resource holds (no-allocation scratch, cache slots)";
         default: return "unknown status";
     }
 }

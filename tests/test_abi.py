@@ -22,8 +22,8 @@ def test_exports_match_header(L):
     import routed_experts_bit_amd as rl
 
     hdr = open(os.path.join(ROOT, "include", "rl_moe.h")).read()
-    declared = set(re.findall(r"\b(rl_moe_\w+)\s*\(", hdr))
-    assert declared == set(rl._binding.EXPORTS)
+    declared = set(re.findall(r"\b(rl_(?:moe|cache)_\w+)\s*\(", hdr))
+    assert declared == set(rl._binding.EXPORTS + rl._binding.CACHE_EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
 
@@ -290,4 +290,4 @@ def test_noalloc_codes(L):
     assert call(4, 17) == RL_ESHAPE
     assert call(4, 10, x=0) == RL_EINVAL
     assert call(0, 10, x=0, out=0) == 0
-    assert "scratch" in rl.strerror(RL_ETOOBIG)
+    assert "scratch" in rl.strerror(RL_ETOOBIG) and "cache" in rl.strerror(RL_ETOOBIG)

@@ -58,6 +58,6 @@ def test_noalloc_refuses_beyond_buffer(rl):
     x, ids, w, ex = to_device(wl)
     assert rl.workspace_bytes(wl.T, wl.k, ex.E, ex.H, ex.I) > rl.NOALLOC_SCRATCH_BYTES
     out = torch.zeros((wl.T, ex.H), dtype=torch.float32, device="cuda")
-    with pytest.raises(rl.RlError, match="scratch"):
+    with pytest.raises(rl.RlError, match="no-allocation scratch"):
         rl.prefill_noalloc(x, ids, w, ex, out)
     assert torch.count_nonzero(out).item() == 0  # nothing was launched
