@@ -59,7 +59,7 @@ __host__ __device__ inline float half_bits_to_float(uint32_t h) {
 
 // 16-bit float pattern of a small integer (|v| <= 45): exact in both bf16 and fp16.
 template <bool F16>
-__host__ __device__ inline uint32_t int_to_op16(int v) {
+__host__ __device__ constexpr uint32_t int_to_op16(int v) {
     float f = (float)v;
     if constexpr (F16) {
         return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
@@ -96,7 +96,7 @@ __host__ __device__ inline uint32_t perm2(uint32_t hi, uint32_t lo, uint32_t sel
 }
 
 // ------------------------------------------------------------------ tables
-__host__ __device__ inline uint32_t tern_entry(uint32_t b) {
+__host__ __device__ constexpr uint32_t tern_entry(uint32_t b) {
     if (b > 242) return 0x155u;  // five 1-digits
     uint32_t r = 0;
     for (int i = 0; i < 5; ++i) {
@@ -109,7 +109,7 @@ __host__ __device__ inline uint32_t tern_entry(uint32_t b) {
 
 // Entry `idx` = s*256 + q of the value table.
 template <int QT, bool F16>
-__host__ __device__ inline uint64_t val_entry(int idx) {
+__host__ __device__ constexpr uint64_t val_entry(int idx) {
     const int s = idx >> 8, q = idx & 255;
     uint64_t r = 0;
     for (int i = 0; i < 4; ++i) {

@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rl_decode.h"
 #include "rl_moe.h"
 
@@ -368,15 +370,38 @@ __device__ __forceinline__ bool next_item(int32_t* counters, int ns, int n_ranks
 
 // Decode tables of one block type, built once per (persistent) work-group.
 template <int QT, bool F16>
-struct DecodeTables {
+struct alignas(16) DecodeTables {
     uint64_t val[val_entries<QT>()];
-    uint32_t tern[QT == QT_T1 ? 256 : 1];
+    uint32_t tern[QT == QT_T1 ? 256 : 4];  // (Q2B: padding to whole 16-byte units)
     __device__ inline void build(int tid, int nthr) {
         for (int i = tid; i < val_entries<QT>(); i += nthr) val[i] = val_entry<QT, F16>(i);
         if constexpr (QT == QT_T1)
             for (int i = tid; i < 256; i += nthr) tern[i] = tern_entry((uint32_t)i);
     }
 };
+
+// The same tables as initialised device data (evaluated by the compiler from the same entry
+// functions): short-lived work-groups copy them into LDS with 16-byte loads instead of computing
+// them.
+template <int QT, bool F16>
+constexpr DecodeTables<QT, F16> make_tables() {
+    DecodeTables<QT, F16> t{};
+    for (int i = 0; i < val_entries<QT>(); ++i) t.val[i] = val_entry<QT, F16>(i);
+    if constexpr (QT == QT_T1)
+        for (int i = 0; i < 256; ++i) t.tern[i] = tern_entry((uint32_t)i);
+    return t;
+}
+template <int QT, bool F16>
+__device__ constexpr DecodeTables<QT, F16> kDecodeTables = make_tables<QT, F16>();
+
+template <int QT, bool F16>
+__device__ __forceinline__ void copy_tables(DecodeTables<QT, F16>& dst, int tid, int nthr) {
+    static_assert(sizeof(DecodeTables<QT, F16>) % 16 == 0, "whole 16-byte units");
+    constexpr int N = (int)(sizeof(DecodeTables<QT, F16>) / 16);
+    const u32x4* s = reinterpret_cast<const u32x4*>(&kDecodeTables<QT, F16>);
+    u32x4* d = reinterpret_cast<u32x4*>(&dst);
+    for (int i = tid; i < N; i += nthr) d[i] = s[i];
+}
 
 __device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
@@ -1802,13 +1827,15 @@ __global__ __launch_bounds__(256) void k_combine(YSlots ys, CombineW cw, float* 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+struct NoTables {};
+// only the tables of the types present take LDS (T1 alone: 17 KB, Q2B alone: 32 KB)
 template <int QMASK, bool F16>
 struct GvTables {
-    DecodeTables<QT_Q2B, F16> q2b;
-    DecodeTables<QT_T1, F16> t1;
-    __device__ inline void build(int tid, int nthr) {
-        if constexpr (QMASK & 1) q2b.build(tid, nthr);
-        if constexpr (QMASK & 2) t1.build(tid, nthr);
+    std::conditional_t<(QMASK & 1) != 0, DecodeTables<QT_Q2B, F16>, NoTables> q2b;
+    std::conditional_t<(QMASK & 2) != 0, DecodeTables<QT_T1, F16>, NoTables> t1;
+    __device__ inline void load(int tid, int nthr) {
+        if constexpr (QMASK & 1) copy_tables(q2b, tid, nthr);
+        if constexpr (QMASK & 2) copy_tables(t1, tid, nthr);
     }
 };
 
@@ -1873,6 +1900,16 @@ __device__ __forceinline__ float row_dot(int qtype, const uint8_t* W, uint32_t m
     return 0.f;
 }
 
+// The call's pairs (R*k <= 32): expert (-1 for an id outside [0, E)), type and matrix offsets.
+// The gate/up kernel resolves them (ids, then descriptors) into LDS, so that a wave's weight
+// loads wait on LDS, and its first work-group stores the table for the down kernel, which then
+// reads it with one load instead of two dependent ones.
+struct GvPair {
+    int32_t e, qt;
+    uint64_t gate_off, up_off, down_off;
+};
+constexpr int GV_MAX_PAIRS = 32;
+
 struct GvArgs {
     const uint16_t* x;
     PairIds pid;      // the call's pairs (k = pid.kk per row, the last one the shared expert if any)
@@ -1882,6 +1919,7 @@ struct GvArgs {
     const uint8_t* arena;
     const rl_expert_desc* desc;
     uint16_t* hgv;  // [R*k][I] fp16
+    GvPair* pairs;  // [R*k]: written by the gate/up kernel, read by the down kernel
     float* out;  // [R][H]
     int32_t* flags;
     int R, k, E, H, I;
@@ -1892,14 +1930,6 @@ struct GvArgs {
     }
 };
 
-// The call's pairs (R*k <= 32) read once per work-group: expert (-1 for an id outside [0, E)),
-// type and matrix offsets, so that a wave's weight loads wait on LDS rather than on two
-// dependent global loads.
-struct GvPair {
-    int32_t e, qt;
-    uint64_t gate_off, up_off, down_off;
-};
-constexpr int GV_MAX_PAIRS = 32;
 
 __device__ __forceinline__ void gv_load_pairs(const GvArgs& a, GvPair* sp) {
     const int tid = threadIdx.x;
@@ -1917,12 +1947,35 @@ __device__ __forceinline__ void gv_load_pairs(const GvArgs& a, GvPair* sp) {
 // A wave computes features i0, i0+1 of one (row, slot) pair: lanes 0-15 gate row i0, 16-31
 // gate i0+1, 32-47 up i0, 48-63 up i0+1; each lane covers H/16 consecutive values (two lanes
 // per 256-value block when H = 2048), then a fixed xor tree reduces the 16 partial sums.
+// x (R rows, 16-byte aligned) is staged in LDS once per work-group: each lane reads H/16 values
+// of it per row, which through the vector memory path cost more than the weight loads.  Every
+// run of H/16 values (one lane's share) is followed by 16 bytes of padding, so that the 16 lanes
+// of a row, reading at the same offset of their runs, fall on different LDS banks.  Dynamic LDS
+// of gv_xs_bytes(R, H) bytes.
+__host__ __device__ constexpr int gv_xs_row(int H) { return H + 16 * 8; }  // halfwords per staged row
+__host__ __device__ constexpr size_t gv_xs_bytes(int R, int H) { return (size_t)R * gv_xs_row(H) * 2; }
 template <int QMASK, int S1, int MAXS>
 __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
     __shared__ GvTables<QMASK, false> tb;
-    tb.build(threadIdx.x, 256);
-    if (blockIdx.x == 0 && threadIdx.x < FLAGS_WORDS) a.flags[threadIdx.x] = 0;  // k_gv_down sets them
+    __shared__ GvPair sp[GV_MAX_PAIRS];
+    extern __shared__ u32x4 gv_xs[];
+    const int tid = threadIdx.x;
+    gv_load_pairs(a, sp);  // the pair table first: its loads are in flight while the rest is staged
+    {
+        const int units = a.H / 8, run = a.H / 128;  // 16-byte units per row and per lane run
+        for (int i = tid; i < a.R * units; i += 256) {
+            const int r = i / units, u = i - r * units;
+            gv_xs[r * (gv_xs_row(a.H) / 8) + u + u / run] = reinterpret_cast<const u32x4*>(a.x)[i];
+        }
+    }
+    tb.load(tid, 256);
+    if (blockIdx.x == 0 && tid < FLAGS_WORDS) a.flags[tid] = 0;
     __syncthreads();
+    if (blockIdx.x == 0 && tid < a.R * a.k) {
+        a.pairs[tid] = sp[tid];
+        if (sp[tid].e < 0) atomicOr(&a.flags[0], FLAG_BAD_ID);
+    }
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(gv_xs);
     const int lane = threadIdx.x & 63, rs = lane >> 4, q = lane & 15;
     const int half_i = a.I >> 1;
     const int total = a.R * a.k * half_i;
@@ -1931,20 +1984,21 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
         const int pr = wv / half_i;
         const int i0 = 2 * (wv % half_i);
         const int r = pr / a.k;
-        const int e = a.pid.expert(pr);
+        const GvPair pp = sp[pr];
+        const int e = pp.e;
         const int row = i0 + (rs & 1);
         float part = 0.f;
-        if (e >= 0 && e < a.E) {
-            const rl_expert_desc dsc = a.desc[e];
-            const uint8_t* W = a.arena + (rs < 2 ? dsc.gate_off : dsc.up_off);
-            const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 * (dsc.qtype == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
-            part = row_dot<QMASK, S1, MAXS, true>(dsc.qtype, W, mb, a.H, row, q * span, span, a.x + (size_t)r * a.H + q * span, tb);
+        if (e >= 0) {
+            const uint8_t* W = a.arena + (rs < 2 ? pp.gate_off : pp.up_off);
+            const uint32_t mb = (uint32_t)((size_t)a.I * a.H / 256 * (pp.qt == QT_T1 ? Fmt<QT_T1>::BYTES : Fmt<QT_Q2B>::BYTES));
+            part = row_dot<QMASK, S1, MAXS, true>(pp.qt, W, mb, a.H, row, q * span, span,
+                                                  xs + r * gv_xs_row(a.H) + q * (span + 8), tb);
         }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
         const float other = __shfl_xor(part, 32, 64);  // gate lanes receive the up sum of their feature
         if (rs < 2 && q == 0)
-            a.hgv[(size_t)pr * a.I + row] = f32_to_f16_bits((e >= 0 && e < a.E) ? silu(part) * other : 0.f);
+            a.hgv[(size_t)pr * a.I + row] = f32_to_f16_bits(e >= 0 ? silu(part) * other : 0.f);
     }
 }
 
@@ -1957,13 +2011,11 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
     __shared__ GvTables<QMASK, true> tb;
     __shared__ GvPair sp[GV_MAX_PAIRS];
     __shared__ float wsh[GV_MAX_PAIRS];
-    tb.build(threadIdx.x, 256);
-    gv_load_pairs(a, sp);
     if (threadIdx.x < a.R * a.k) {
+        sp[threadIdx.x] = a.pairs[threadIdx.x];  // resolved by the gate/up kernel
         wsh[threadIdx.x] = a.weight(threadIdx.x);
-        const int e = a.pid.expert(threadIdx.x);
-        if (blockIdx.x == 0 && (e < 0 || e >= a.E)) atomicOr(&a.flags[0], FLAG_BAD_ID);
     }
+    tb.load(threadIdx.x, 256);
     __syncthreads();
     const int lane = threadIdx.x & 63, gq = lane >> 4, q = lane & 15;
     const int span = a.I >> 4;

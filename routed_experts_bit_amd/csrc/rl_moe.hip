@@ -49,7 +49,8 @@ constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t flags, offsets, pair_src, inv, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, yexp, yspare, total;
+    size_t flags, gvpairs, offsets, pair_src, inv, tile_hist, items, xq, xscale, h8, hscale, hbuf, yslot, yexp, yspare,
+        total;
     int maxrec;  // work records per block type
 };
 
@@ -87,6 +88,8 @@ Layout layout(int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
     size_t off = 0;
     L.flags = off;
     off = align_up(off + FLAGS_WORDS * sizeof(int32_t));
+    L.gvpairs = off;  // the resolved pair table of the 1-2 row path
+    off = align_up(off + GV_MAX_PAIRS * sizeof(GvPair));
     L.offsets = off;
     off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
     L.pair_src = off;
@@ -408,7 +411,8 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
     dim3 g1((waves1 + 3) / 4 < 1024 ? (waves1 + 3) / 4 : 1024);
     dim3 g2((waves2 + 3) / 4 < 1024 ? (waves2 + 3) / 4 : 1024);
     // strips of S values per lane: S = 64 for dimensions >= 1024 (then H/1024 or I/1024 strips)
-#define RL_GV1(S, M) hipLaunchKernelGGL((k_gv_gateup<QMASK, S, M>), g1, dim3(256), 0, s, a)
+    const size_t xs_bytes = gv_xs_bytes(a.R, a.H);  // x staged in LDS (at most 32.5 KB)
+#define RL_GV1(S, M) hipLaunchKernelGGL((k_gv_gateup<QMASK, S, M>), g1, dim3(256), xs_bytes, s, a)
     if (a.H >= 1024) {
         if (a.H <= 1024)
             RL_GV1(64, 1);
@@ -711,6 +715,7 @@ static int decode_impl(const uint16_t* x, const Route& r, const rl_expert_blobs*
     a.arena = static_cast<const uint8_t*>(experts->arena);
     a.desc = experts->desc;
     a.hgv = at<uint16_t>(workspace, L.hbuf);  // [R*k][I] fp16
+    a.pairs = at<GvPair>(workspace, L.gvpairs);
     a.out = out;
     a.flags = at<int32_t>(workspace, L.flags);
     a.R = T;

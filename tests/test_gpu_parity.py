@@ -575,6 +575,43 @@ def test_decode_full_size(orc, rl, R):
         assert err <= TOL
 
 
+def test_decode_graph_replay(rl):
+    """The 1-2 row path captured in a HIP graph (it records kernel launches only): several steps
+    in one graph, replayed three times with eager calls and synchronisations in between; every
+    replay gives the eager outputs bit for bit."""
+    import torch
+
+    from workload.gen import _routing, gen_x
+
+    ex_np = make_experts(64, 2048, 512, [QTYPE_Q2B] * 32 + [QTYPE_T1] * 32, seed=44)
+    ex = rl.DeviceExperts.from_workload(ex_np)
+    steps = []
+    for s in range(4):
+        R = 1 + s % 2
+        i_np, w_np = _routing(R, 64, 8, 700 + s)
+        steps.append((torch.from_numpy(gen_x(R, 2048, 750 + s).view(np.int16).copy()).cuda(),
+                      torch.from_numpy(i_np).cuda(), torch.from_numpy(w_np).cuda()))
+    wss = [rl.alloc_workspace(2, 8, ex) for _ in steps]
+    eager = [rl.decode(x, i, w, ex, ws=ws).clone() for (x, i, w), ws in zip(steps, wss)]
+    outs = [torch.full_like(e, float("nan")) for e in eager]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (x, i, w), ws, o in zip(steps, wss, outs):
+            rl.decode(x, i, w, ex, out=o, ws=ws)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for s, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), (rep, s)
+        x, i, w = steps[rep % len(steps)]
+        rl.decode(x, i, w, ex)  # eager work between replays
+        torch.cuda.synchronize()
+    log("decode graph replays bit-identical")
+
+
 def test_chunked_layer_bit_identical_to_one_call(orc, rl):
     """A layer taken as consecutive calls of at most 128 tokens (the 8,192-token workload runs as
     four 2,048-token calls) gives bit-identical outputs to one call over all its tokens: every
