@@ -71,7 +71,10 @@ typedef struct rl_expert_desc {
  * the host to decide which type-specialised kernels to launch and to check the offsets); the two
  * copies must agree.  E in [1, 1024].  H (hidden) a multiple of 256 in [256, 8192].  I (expert
  * intermediate) a multiple of 64 in [64, 4096] that is either a multiple of 256 or one of
- * 64 / 128.  Matrix bytes: H * I / 256 blocks of 74 (Q2B) or 57 (T1) bytes. */
+ * 64 / 128.  Matrix bytes: H * I / 256 blocks of 74 (Q2B) or 57 (T1) bytes.  A T1 digit byte
+ * holds five base-3 digits, so it is at most 242; the kernels do not check it (a larger byte
+ * decodes as five zero weights), so arenas are to be validated once when they are loaded (the
+ * Python binding does so for arenas it copies from host memory). */
 typedef struct rl_expert_blobs {
     const void* arena;
     const rl_expert_desc* desc;

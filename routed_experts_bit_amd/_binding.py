@@ -212,6 +212,8 @@ class DeviceExperts:
         torch = _torch()
         self.E, self.H, self.I = int(E), int(H), int(I)
         if isinstance(arena_u8, np.ndarray):
+            _check_descriptors(np.ascontiguousarray(desc_np), self.E, self.H, self.I, arena_u8.size)
+            _check_t1_digit_bytes(arena_u8, desc_np, self.H, self.I)
             n = arena_u8.size
             buf = torch.zeros((n + 3) // 4 * 4, dtype=torch.uint8, device=device)
             buf[:n].copy_(torch.from_numpy(np.ascontiguousarray(arena_u8)))
@@ -265,6 +267,24 @@ def _check_descriptors(desc: np.ndarray, E: int, H: int, I: int, arena_bytes: in
             if off % 4 or off + mb > arena_bytes:
                 raise RlError(f"expert {e}: {which} {off} (+{mb} bytes) is not a dword-aligned matrix inside the "
                               f"{arena_bytes}-byte arena")
+
+
+def _check_t1_digit_bytes(arena: np.ndarray, desc: np.ndarray, H: int, I: int):
+    """T1 digit bytes hold five base-3 digits, so a valid byte is at most 242.  The kernels do not
+    check (a larger byte decodes as five zero weights); an arena given as host memory is checked
+    here once, before it is copied to the device."""
+    bb = _BLOCK_BYTES[RL_QTYPE_T1]
+    nb = H * I // 256
+    flat = np.ascontiguousarray(arena).reshape(-1)
+    for e in np.nonzero(desc["qtype"] == RL_QTYPE_T1)[0]:
+        for which in ("gate_off", "up_off", "down_off"):
+            off = int(desc[which][e])
+            blocks = flat[off:off + nb * bb].reshape(nb, bb)
+            bad = np.nonzero((blocks[:, 5:] > 242).any(axis=1))[0]
+            if bad.size:
+                b = int(bad[0])
+                v = int(blocks[b, 5:].max())
+                raise RlError(f"expert {int(e)}: {which[:-4]} block {b} holds the T1 digit byte {v} (at most 242)")
 
 
 def workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:

@@ -291,3 +291,23 @@ def test_noalloc_codes(L):
     assert call(4, 10, x=0) == RL_EINVAL
     assert call(0, 10, x=0, out=0) == 0
     assert "scratch" in rl.strerror(RL_ETOOBIG) and "cache" in rl.strerror(RL_ETOOBIG)
+
+
+def test_t1_digit_bytes_checked_on_load():
+    """A T1 digit byte above 242 (more than five base-3 digits) is rejected when a host arena
+    is loaded (the kernels themselves decode such a byte as five zero weights, the oracle
+    rejects it); a valid arena loads."""
+    import routed_experts_bit_amd as rl
+    from workload import QTYPE_Q2B, QTYPE_T1, make_experts
+
+    ex = make_experts(4, 256, 64, [QTYPE_Q2B, QTYPE_T1, QTYPE_T1, QTYPE_Q2B], seed=5, threads=1)
+    rl.DeviceExperts(ex.arena, ex.desc, ex.E, ex.H, ex.I, device="cpu")
+    bad = ex.arena.copy()
+    off = int(ex.desc["up_off"][2]) + 3 * 57 + 5 + 17  # expert 2 (T1), up matrix, block 3, a digit byte
+    bad[off] = 243
+    with pytest.raises(rl.RlError, match="expert 2: up block 3"):
+        rl.DeviceExperts(bad, ex.desc, ex.E, ex.H, ex.I, device="cpu")
+    # Q2B code bytes take every value
+    ok = ex.arena.copy()
+    ok[int(ex.desc["gate_off"][0]) + 20] = 255
+    rl.DeviceExperts(ok, ex.desc, ex.E, ex.H, ex.I, device="cpu")
