@@ -89,10 +89,13 @@ struct PairIds {
     }
 };
 
-// Work records: an expert's pairs are cut into records of at most REC_PAIRS sorted pairs (one
-// gate/up chunk), so that a hot expert (the shared expert has a pair for every token) is spread
-// over many work items.
-constexpr int REC_PAIRS = 64;
+// Work records: an expert's pairs are cut into records of at most REC_PAIRS sorted pairs, so that
+// a hot expert (the shared expert has a pair for every token) is spread over many work items.  96
+// pairs = two down chunks of 48 (or a 64-row and a 32-row gate/up chunk): every expert up to 96
+// pairs stays one record, so no chunk of the down kernel is cut short by a record boundary
+// (records of 64 pairs made a 74-pair expert three down chunks, 48 + 16 + 10, and the Zipf-routed
+// Q2B layer's down 17 us slower).
+constexpr int REC_PAIRS = 96;
 __host__ __device__ constexpr int max_records(int E, int P) { return E + (P + REC_PAIRS - 1) / REC_PAIRS; }
 
 struct GroupArgs {
