@@ -612,6 +612,37 @@ def test_decode_graph_replay(rl):
     log("decode graph replays bit-identical")
 
 
+@pytest.mark.parametrize("name", ["med_mixed", "i1024_t1"])
+def test_prefill_graph_replay(rl, cases, name):
+    """rl_moe_prefill captured in a HIP graph (it records kernel launches only: no allocation, no
+    memset, no host synchronisation) with two calls on their own workspaces, replayed three times
+    with eager calls in between: every replay gives the eager outputs bit for bit."""
+    import torch
+
+    wl = _case(cases, name)
+    x, ids, w, ex = to_device(wl)
+    ids2 = torch.flip(ids, dims=[1]).contiguous()
+    w2 = torch.flip(w, dims=[1]).contiguous()
+    wss = [rl.alloc_workspace(wl.T, wl.k, ex) for _ in range(2)]
+    eager = [rl.prefill(x, i, ww, ex, ws=ws).clone() for (i, ww), ws in zip(((ids, w), (ids2, w2)), wss)]
+    outs = [torch.full_like(e, float("nan")) for e in eager]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (i, ww), ws, o in zip(((ids, w), (ids2, w2)), wss, outs):
+            rl.prefill(x, i, ww, ex, out=o, ws=ws)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for s, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), (rep, s)
+        rl.prefill(x, ids, w, ex)  # eager work between replays
+        torch.cuda.synchronize()
+    log(f"prefill graph replays bit-identical ({name})")
+
+
 def test_chunked_layer_bit_identical_to_one_call(orc, rl):
     """A layer taken as consecutive calls of at most 128 tokens (the 8,192-token workload runs as
     four 2,048-token calls) gives bit-identical outputs to one call over all its tokens: every
