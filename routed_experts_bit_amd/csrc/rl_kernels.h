@@ -705,6 +705,31 @@ __device__ __forceinline__ uint32_t win_lane_byte(int lane) {
     return QT == QT_T1 ? 16u * (uint32_t)(lane & 3) : 16u * (uint32_t)(lane % 5);
 }
 
+// LDS layout of one wave's windows of NT strips.  Narrow (the general case): per strip four
+// quarters of 4 rows, WQ bytes apart, each quarter loaded by its own buffer-to-LDS instruction of
+// 4*WL active lanes (4*NT instructions per block).  Wide (T1, 4 strips of one matrix: WL = 4, so
+// 64 lanes cover one quarter of all four strips): quarter q holds [strip][row][64 bytes] followed
+// by 16 bytes of padding, and lane L fetches 16 bytes (L & 3) of row 4q + ((L >> 2) & 3) of strip
+// L >> 4, so one 64-lane instruction per quarter loads it (4 per block instead of 16: the down
+// kernels 6.5 us faster).  Gate/up keeps the narrow layout: its strips come from two matrices (two
+// buffer resources), and two 32-lane instructions per quarter made it 10 us slower.  In both
+// layouts the 16 rows of a strip read by one lane group fall on distinct banks: wide row 4q + j of
+// strip t starts at 1040q + 256t + 64j bytes, bank 4q + 16j.
+template <int QT, int NT, int NMAT>
+struct WinLay {
+    typedef WinGeo<QT> G;
+    static constexpr bool WIDE = QT == QT_T1 && NT == 4 && NMAT == 1;
+    static constexpr int QS = NT * 256 + 16;  // wide: bytes per quarter
+    static constexpr int WAVE_BYTES = WIDE ? 4 * QS : NT * G::WS;
+    static constexpr int LOADS = WIDE ? 4 : 4 * NT;  // buffer-to-LDS instructions per block
+    __device__ static __forceinline__ const uint32_t* win(uint8_t* wave_base, int t, int r) {
+        if constexpr (WIDE)
+            return (const uint32_t*)(wave_base + QS * (r >> 2) + 256 * t + 64 * (r & 3));
+        else
+            return (const uint32_t*)(wave_base + t * G::WS + G::WQ * (r >> 2) + G::WIN * (r & 3));
+    }
+};
+
 // A staged step of an activation row is 256 bytes in 16 pieces of 16 bytes; piece 4g + j
 // (lane group g, operand quarter j) sits at slot (4g + j) ^ (row % 16) of the row (spreading the
 // rows that one LDS read serves over the banks), so the loading lane of slot s fetches piece
@@ -928,11 +953,10 @@ struct GuChunk {
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * G::WS; }
+    typedef WinLay<QT, NT, NMAT> WLay;
+    __device__ __forceinline__ uint8_t* wbase() const { return sh.wts + wave * WLay::WAVE_BYTES; }
     // window of row r (0..15) of strip t
-    __device__ __forceinline__ const uint32_t* win(int t, int r) const {
-        return (const uint32_t*)(wts(t) + G::WQ * (r >> 2) + G::WIN * (r & 3));
-    }
+    __device__ __forceinline__ const uint32_t* win(int t, int r) const { return WLay::win(wbase(), t, r); }
 
     // step c of the activations into ring slot `slot`; c = NS: step 0 of the next chunk
     __device__ __forceinline__ void act(int c, int slot) {
@@ -946,18 +970,24 @@ struct GuChunk {
         }
     }
     // the windows of block kb (clamped to the last block, so that the number of loads is
-    // fixed) of this wave's rows: in quarter q, lane L < 4*WL fetches its 16 bytes of the window
-    // of row 4q + win_lane_row(L) (woff[t] holds lane L's offset for q = 0; rows are row_bytes
-    // apart, except that quarter 3 of a strip may start wx[t] bytes further on)
+    // fixed) of this wave's rows.  Narrow: in quarter q, lane L < 4*WL fetches its 16 bytes of the
+    // window of row 4q + win_lane_row(L) (wo[t] holds lane L's offset for q = 0; rows are row_bytes
+    // apart, except that quarter 3 of a strip may start wxx[t] bytes further on).  Wide: wo[q] is
+    // lane L's offset in quarter q (see WinLay).
     __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo,
                                                const uint32_t* wxx, uint32_t blk) {
-        if ((threadIdx.x & 63) < 4 * G::WL) {
+        if constexpr (WLay::WIDE) {  // (one matrix: sg)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(sg.r, (lds_void*)(wbase() + WLay::QS * q), 16,
+                                                         (wo[q] + blk) & ~3u, 0, 0, 0);
+        } else if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        (t < NTI ? sg : su).r, (lds_void*)(wts(t) + G::WQ * q), 16,
+                        (t < NTI ? sg : su).r, (lds_void*)(wbase() + t * G::WS + G::WQ * q), 16,
                         (wo[t] + 4u * (uint32_t)q * rowb + (q == 3 ? wxx[t] : 0u) + blk) & ~3u, 0, 0, 0);
         }
     }
@@ -988,7 +1018,7 @@ struct GuChunk {
         if (H == 0)
             vm_barrier<0>();
         else
-            vm_barrier<4 * NT>();
+            vm_barrier<WLay::LOADS>();
         // the hook's loads complete before the next step's wait
         if (c == NS - 2) hook();
         act(c + 1, 1 - H);
@@ -1269,7 +1299,8 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
     __shared__ int32_t rdst[64];
-    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * NT * WinGeo<QT>::WS];
+    typedef WinLay<QT, NT, MODE == GU_GATEUP ? 2 : 1> WLay;
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * WLay::WAVE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
     constexpr bool HCOL = QT == QT_T1 && MODE == GU_GATEUP;  // output columns in t1_hcol order
@@ -1332,10 +1363,18 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
         for (int t = 0; t < NT; ++t) {
             const int c0 = colw + 16 * (t % NTI), c0n = colw_n + 16 * (t % NTI);
             roff[t] = (uint32_t)col(c0 + n) * row_bytes;
-            woff[t] = (uint32_t)col(c0 + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
-            woff_n[t] = (uint32_t)col(c0n + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
-            wx[t] = (uint32_t)(col(c0 + 12) - col(c0) - 12) * row_bytes;
-            wx_n[t] = (uint32_t)(col(c0n + 12) - col(c0n) - 12) * row_bytes;
+            if constexpr (WLay::WIDE) {  // entry t: quarter t of the lane's own strip (lane >> 4)
+                const int tl = lane >> 4, j = (lane >> 2) & 3;
+                const int l0 = colw + 16 * (tl % NTI), l0n = colw_n + 16 * (tl % NTI);
+                woff[t] = (uint32_t)col(l0 + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
+                woff_n[t] = (uint32_t)col(l0n + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
+                wx[t] = wx_n[t] = 0u;
+            } else {
+                woff[t] = (uint32_t)col(c0 + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
+                woff_n[t] = (uint32_t)col(c0n + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
+                wx[t] = (uint32_t)(col(c0 + 12) - col(c0) - 12) * row_bytes;
+                wx_n[t] = (uint32_t)(col(c0n + 12) - col(c0n) - 12) * row_bytes;
+            }
         }
         uint32_t xon[GU_DMA];
 #pragma unroll
@@ -1408,17 +1447,22 @@ struct DnSweep {
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    __device__ __forceinline__ uint8_t* wts(int t) const { return sh.wts + (wave * NT + t) * G::WS; }
-    __device__ __forceinline__ const uint32_t* win(int t, int r) const {
-        return (const uint32_t*)(wts(t) + G::WQ * (r >> 2) + G::WIN * (r & 3));
-    }
+    typedef WinLay<QT, NT, 1> WLay;
+    __device__ __forceinline__ uint8_t* wbase() const { return sh.wts + wave * WLay::WAVE_BYTES; }
+    __device__ __forceinline__ const uint32_t* win(int t, int r) const { return WLay::win(wbase(), t, r); }
+    // narrow: wo[t] is the lane's offset in quarter 0 of strip t; wide: wo[q] its offset in quarter q
     __device__ __forceinline__ void wload_from(const BufSrc& sw, const uint32_t* wo, uint32_t blk) {
-        if ((threadIdx.x & 63) < 4 * G::WL) {
+        if constexpr (WLay::WIDE) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wbase() + WLay::QS * q), 16,
+                                                         (wo[q] + blk) & ~3u, 0, 0, 0);
+        } else if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wts(t) + G::WQ * q), 16,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wbase() + t * G::WS + G::WQ * q), 16,
                                                              (wo[t] + 4u * (uint32_t)q * rowb + blk) & ~3u, 0, 0, 0);
         }
     }
@@ -1491,8 +1535,14 @@ __device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, co
 #pragma unroll
         for (int t = 0; t < DN_NT; ++t) {
             roff[t] = (uint32_t)(col0 + 16 * t + n) * rowb;
-            woff[t] = ((uint32_t)(col0 + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
-            woff_n[t] = ((uint32_t)(col0n + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
+            if constexpr (WinLay<QT, DN_NT, 1>::WIDE) {  // entry t: quarter t of the lane's strip
+                const uint32_t r = (uint32_t)(16 * (lane >> 4) + 4 * t + ((lane >> 2) & 3));
+                woff[t] = ((uint32_t)col0 + r) * rowb + 16u * (uint32_t)(lane & 3);
+                woff_n[t] = ((uint32_t)col0n + r) * rowb + 16u * (uint32_t)(lane & 3);
+            } else {
+                woff[t] = ((uint32_t)(col0 + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
+                woff_n[t] = ((uint32_t)(col0n + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
+            }
         }
         DnSweep<QT, MT> sw{sh,  srcw, last ? srcw_next_item : srcw, roff, woff, woff_n, ln, nkb, wave, n, g, rowb,
                            !last || next_item, pf_have};
@@ -1523,7 +1573,8 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
     __shared__ uint32_t tbl8[8];
     __shared__ uint32_t rsc[DN_ROWS];  // T1: the rows' scale words (hsc)
     __shared__ int32_t rdst[DN_ROWS];
-    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * DN_NT * G::WS];
+    typedef WinLay<QT, DN_NT, 1> WLay;
+    __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * WLay::WAVE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t actb[(DN_KMAX / 128) * DN_ACT];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, g = lane >> 4;
     const StaticSched sc(uni(*a.wl_len), a.ns);
@@ -1582,14 +1633,22 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
         stage(rec.p0 + mc, rows);
         if (first) {  // the first sweep's windows (later ones are loaded by the sweep before)
             const int col0 = cbase + wave * (16 * DN_NT);
-            if ((lane & 63) < 4 * G::WL) {
+            uint8_t* wb = wts + wave * WLay::WAVE_BYTES;
+            if constexpr (WLay::WIDE) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const uint32_t r = (uint32_t)(16 * (lane >> 4) + 4 * qq + ((lane >> 2) & 3));
+                    const uint32_t wo = ((uint32_t)col0 + r) * rowb + 16u * (uint32_t)(lane & 3);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wb + WLay::QS * qq), 16, wo & ~3u, 0, 0, 0);
+                }
+            } else if ((lane & 63) < 4 * G::WL) {
 #pragma unroll
                 for (int t = 0; t < DN_NT; ++t)
 #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {
                         const uint32_t wo = ((uint32_t)(col0 + 16 * t) + win_lane_row<QT>(lane)) * rowb +
                                             win_lane_byte<QT>(lane);
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wts + (wave * DN_NT + t) * G::WS + G::WQ * qq),
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wb + t * G::WS + G::WQ * qq),
                                                                  16, (wo + 4u * (uint32_t)qq * rowb) & ~3u, 0, 0, 0);
                     }
             }
