@@ -711,14 +711,15 @@ __device__ __forceinline__ uint32_t win_lane_byte(int lane) {
 // 64 lanes cover one quarter of all four strips): quarter q holds [strip][row][64 bytes] followed
 // by 16 bytes of padding, and lane L fetches 16 bytes (L & 3) of row 4q + ((L >> 2) & 3) of strip
 // L >> 4, so one 64-lane instruction per quarter loads it (4 per block instead of 16: the down
-// kernels 6.5 us faster).  Gate/up keeps the narrow layout: its strips come from two matrices (two
-// buffer resources), and two 32-lane instructions per quarter made it 10 us slower.  In both
-// layouts the 16 rows of a strip read by one lane group fall on distinct banks: wide row 4q + j of
-// strip t starts at 1040q + 256t + 64j bytes, bank 4q + 16j.
-template <int QT, int NT, int NMAT>
+// kernels 6.5 us faster).  Gate/up strips come from two matrices: the wide layout then needs one
+// buffer resource spanning both (SPAN, 9 us faster; two resources, i.e. two 32-lane instructions
+// per quarter, measured 10 us slower than the narrow layout).  In both layouts the 16 rows of a
+// strip read by one lane group fall on distinct banks: wide row 4q + j of strip t starts at
+// 1040q + 256t + 64j bytes, bank 4q + 16j.
+template <int QT, int NT, int NMAT, bool SPAN = true>
 struct WinLay {
     typedef WinGeo<QT> G;
-    static constexpr bool WIDE = QT == QT_T1 && NT == 4 && NMAT == 1;
+    static constexpr bool WIDE = QT == QT_T1 && NT == 4 && (NMAT == 1 || SPAN);
     static constexpr int QS = NT * 256 + 16;  // wide: bytes per quarter
     static constexpr int WAVE_BYTES = WIDE ? 4 * QS : NT * G::WS;
     static constexpr int LOADS = WIDE ? 4 : 4 * NT;  // buffer-to-LDS instructions per block
@@ -927,7 +928,7 @@ __device__ __forceinline__ int t1_hcol(int q, int I) {
     return 256 * (q >> 8) + t1_kmap((q >> 6) & 3, q & 63);
 }
 
-template <int QT, int NMAT, int NTI, int MT>
+template <int QT, int NMAT, int NTI, int MT, bool SPAN>
 struct GuChunk {
     static constexpr int NT = NMAT * NTI;
     static constexpr int BB = Fmt<QT>::BYTES;
@@ -953,7 +954,7 @@ struct GuChunk {
     RunScale rs[NT];
     f32x4 acc[MT][NT];
 
-    typedef WinLay<QT, NT, NMAT> WLay;
+    typedef WinLay<QT, NT, NMAT, SPAN> WLay;
     __device__ __forceinline__ uint8_t* wbase() const { return sh.wts + wave * WLay::WAVE_BYTES; }
     // window of row r (0..15) of strip t
     __device__ __forceinline__ const uint32_t* win(int t, int r) const { return WLay::win(wbase(), t, r); }
@@ -976,7 +977,7 @@ struct GuChunk {
     // lane L's offset in quarter q (see WinLay).
     __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo,
                                                const uint32_t* wxx, uint32_t blk) {
-        if constexpr (WLay::WIDE) {  // (one matrix: sg)
+        if constexpr (WLay::WIDE) {  // (one resource: sg; for gate/up it spans both matrices)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(sg.r, (lds_void*)(wbase() + WLay::QS * q), 16,
@@ -1207,7 +1208,7 @@ __device__ __forceinline__ void t1_h_split_out(const GuArgs& a, const GuShared& 
 // fp16 rows of y).  During the chunk's next-to-last step the hook gathers the next chunk's
 // activation row offsets (xon), this chunk's per-row activation scales (ps; 1 for Q2B) and, for
 // down, the rows' original pair indices (one row per thread of the first wave).
-template <int QT, int MODE, int NTI, int MT>
+template <int QT, int MODE, int NTI, int MT, bool SPAN>
 __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, const BufSrc& srcx,
                                          const BufSrc& srcg, const BufSrc& srcu, const BufSrc& srcg_n,
                                          const BufSrc& srcu_n, const uint32_t* xoff, const uint32_t* roff,
@@ -1237,7 +1238,7 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
             }
         }
     };
-    GuChunk<QT, NMAT, NTI, MT> ch{sh,   srcx,   srcg,   srcu, srcg_n, srcu_n, xoff, roff, woff,
+    GuChunk<QT, NMAT, NTI, MT, SPAN> ch{sh,   srcx,   srcg,   srcu, srcg_n, srcu_n, xoff, roff, woff,
                                   woff_n, wx,   wx_n,   xon,  ln,     nkb,    2 * nkb, wave, n,
                                   g,      (uint32_t)nkb * (uint32_t)Fmt<QT>::BYTES, has_next, pf_have};
     ch.run(hook);
@@ -1287,7 +1288,7 @@ __device__ __forceinline__ void gu_chunk(const GuArgs& a, const GuShared& sh, co
 }
 
 // Body of the gate/up kernels (and of the streamed down kernels for I > 512).
-template <int QT, int MODE, int NTI>
+template <int QT, int MODE, int NTI, bool SPAN>
 __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     constexpr int NTHR = 64 * GU_NW;
     constexpr int NT = (MODE == GU_GATEUP ? 2 : 1) * NTI;
@@ -1299,7 +1300,7 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     __shared__ uint32_t tbl8[8];
     __shared__ float rscale[64];
     __shared__ int32_t rdst[64];
-    typedef WinLay<QT, NT, MODE == GU_GATEUP ? 2 : 1> WLay;
+    typedef WinLay<QT, NT, MODE == GU_GATEUP ? 2 : 1, SPAN> WLay;
     __shared__ __attribute__((aligned(16))) uint8_t wts[GU_NW * WLay::WAVE_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ring0[GU_STEP];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[GU_STEP];
@@ -1349,9 +1350,16 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
         }
         const int rows = min(64, rec.ne - mc);
         const int rows_n = has_next ? min(64, recn.ne - mcn) : 1;
-        const BufSrc srcg(a.arena + rec.off[MODE == GU_GATEUP ? 0 : 2], mat_bytes);
+        // wide gate/up windows: one resource from the lower of the gate and up matrices to the end
+        // of the higher one, each lane's offsets relative to it
+        constexpr bool COMB = WLay::WIDE && MODE == GU_GATEUP;
+        const uint64_t lo = COMB ? min(rec.off[0], rec.off[1]) : rec.off[MODE == GU_GATEUP ? 0 : 2];
+        const uint64_t lo_n = COMB ? min(recn.off[0], recn.off[1]) : recn.off[MODE == GU_GATEUP ? 0 : 2];
+        const uint32_t span = COMB ? (uint32_t)(max(rec.off[0], rec.off[1]) - lo) + mat_bytes : mat_bytes;
+        const uint32_t span_n = COMB ? (uint32_t)(max(recn.off[0], recn.off[1]) - lo_n) + mat_bytes : mat_bytes;
+        const BufSrc srcg(a.arena + lo, span);
         const BufSrc srcu(a.arena + rec.off[1], mat_bytes);
-        const BufSrc srcg_n(a.arena + recn.off[MODE == GU_GATEUP ? 0 : 2], mat_bytes);
+        const BufSrc srcg_n(a.arena + lo_n, span_n);
         const BufSrc srcu_n(a.arena + recn.off[1], mat_bytes);
         const int colw = sc.slice(ix) * (16 * NTI * GU_NW) + wave * (16 * NTI);
         const int colw_n = sc.slice(ixn) * (16 * NTI * GU_NW) + wave * (16 * NTI);
@@ -1366,8 +1374,13 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
             if constexpr (WLay::WIDE) {  // entry t: quarter t of the lane's own strip (lane >> 4)
                 const int tl = lane >> 4, j = (lane >> 2) & 3;
                 const int l0 = colw + 16 * (tl % NTI), l0n = colw_n + 16 * (tl % NTI);
-                woff[t] = (uint32_t)col(l0 + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
-                woff_n[t] = (uint32_t)col(l0n + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
+                uint32_t mo = 0, mo_n = 0;  // the lane's matrix within the combined resource
+                if constexpr (COMB) {
+                    mo = (uint32_t)(rec.off[tl < NTI ? 0 : 1] - lo);
+                    mo_n = (uint32_t)(recn.off[tl < NTI ? 0 : 1] - lo_n);
+                }
+                woff[t] = mo + (uint32_t)col(l0 + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
+                woff_n[t] = mo_n + (uint32_t)col(l0n + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
                 wx[t] = wx_n[t] = 0u;
             } else {
                 woff[t] = (uint32_t)col(c0 + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
@@ -1381,7 +1394,7 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
         for (int i = 0; i < GU_DMA; ++i) xon[i] = xoff[i];
         const int pc = rec.p0 + mc, pn = recn.p0 + mcn;
 #define RL_GU_CHUNK(MT_)                                                                                               \
-    gu_chunk<QT, MODE, NTI, MT_>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, wx, wx_n, ln, nkb, \
+    gu_chunk<QT, MODE, NTI, MT_, SPAN>(a, sh, srcx, srcg, srcu, srcg_n, srcu_n, xoff, roff, woff, woff_n, wx, wx_n, ln, nkb, \
                                  pc, rows, colw, has_next, pf_have, pn, rows_n, xon)
         switch ((rows + 15) >> 4) {
             case 1: RL_GU_CHUNK(1); break;
@@ -1401,15 +1414,17 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     }
 }
 
-// T1 experts on the fp8 MFMA: gate/up + SwiGLU (MODE GU_GATEUP), or down for I > 512 (GU_DOWN)
-template <int MODE, int NTI>
+// T1 experts on the fp8 MFMA: gate/up + SwiGLU (MODE GU_GATEUP), or down for I > 512 (GU_DOWN).
+// SPAN: every expert's gate and up matrices lie within one buffer resource (the gate/up windows
+// then take the wide layout, see WinLay); the host checks the descriptors.
+template <int MODE, int NTI, bool SPAN>
 __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(GuArgs a) {
-    gu_kernel<QT_T1, MODE, NTI>(a);
+    gu_kernel<QT_T1, MODE, NTI, SPAN>(a);
 }
 // Q2B experts on the 16-bit MFMA: the same two uses
 template <int MODE, int NTI>
 __global__ __launch_bounds__(64 * GU_NW, 2) void k_q2_mm(GuArgs a) {
-    gu_kernel<QT_Q2B, MODE, NTI>(a);
+    gu_kernel<QT_Q2B, MODE, NTI, false>(a);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -276,10 +276,10 @@ int grid_cap(int grid, int n_experts, int ns) {
 int down_grid(int grid) { return grid < Y_SPARE / 4 ? grid : Y_SPARE / 4; }
 
 // The LDS-window kernels of a block type (T1 on the fp8 MFMA, Q2B on the 16-bit MFMA).
-template <int QT, int MODE, int NTI>
+template <int QT, int MODE, int NTI, bool SPAN = false>
 constexpr auto mm_kernel() {
     if constexpr (QT == QT_T1)
-        return &k_t1_f8<MODE, NTI>;
+        return &k_t1_f8<MODE, NTI, SPAN>;
     else
         return &k_q2_mm<MODE, NTI>;
 }
@@ -291,21 +291,39 @@ constexpr auto dn_kernel_of() {
         return &k_q2_dn;
 }
 
-template <int QT, int MODE, int NTI>
+template <int QT, int MODE, int NTI, bool SPAN = false>
 void launch_mm(const GuArgs& b, int n_experts, hipStream_t s) {
-    constexpr auto K = mm_kernel<QT, MODE, NTI>();
+    constexpr auto K = mm_kernel<QT, MODE, NTI, SPAN>();
     const int grid = grid_cap(resident_grid<K>(64 * GU_NW), n_experts, b.ns);
     hipLaunchKernelGGL(K, dim3(grid), dim3(64 * GU_NW), 0, s, b);
+}
+
+// Whether every expert of block type qt has its gate and up matrices within one buffer resource
+// (the span from the lower to the end of the higher below 2^31 bytes), so that the T1 gate/up
+// kernel can fetch the windows of both with one instruction.
+bool gateup_spans(const rl_expert_blobs* ex, int qt) {
+    const uint64_t mb = matrix_bytes(qt, ex->H, ex->I);
+    for (int e = 0; e < ex->E; ++e) {
+        const rl_expert_desc& d = ex->desc_host[e];
+        if (d.qtype != qt) continue;
+        const uint64_t lo = d.gate_off < d.up_off ? d.gate_off : d.up_off;
+        const uint64_t hi = d.gate_off < d.up_off ? d.up_off : d.gate_off;
+        if (hi - lo + mb > 0x7FFF0000ull) return false;
+    }
+    return true;
 }
 
 // Gate/up: 4 waves x (2 gate + 2 up tiles) = 128 intermediate columns per work item when
 // I % 128 == 0, else 64 columns (1 + 1 tiles per wave).
 template <int QT>
-void launch_gateup_mm(const GuArgs& a, int n_experts, hipStream_t s) {
+void launch_gateup_mm(const GuArgs& a, int n_experts, hipStream_t s, bool span) {
     GuArgs b = a;
     if (a.N % 128 == 0) {
         b.ns = a.N / 128;
-        launch_mm<QT, GU_GATEUP, 2>(b, n_experts, s);
+        if (QT == QT_T1 && span)
+            launch_mm<QT, GU_GATEUP, 2, true>(b, n_experts, s);
+        else
+            launch_mm<QT, GU_GATEUP, 2>(b, n_experts, s);
     } else {
         b.ns = a.N / 64;
         launch_mm<QT, GU_GATEUP, 1>(b, n_experts, s);
@@ -510,7 +528,7 @@ void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* 
         q.act = reinterpret_cast<const uint8_t*>(x);
         q.items = items + (size_t)(QT_Q2B - 1) * L.maxrec;
         q.wl_len = flags + 8 + QT_Q2B;
-        launch_gateup_mm<QT_Q2B>(q, records_bound(present[QT_Q2B], P), s);
+        launch_gateup_mm<QT_Q2B>(q, records_bound(present[QT_Q2B], P), s, false);
     }
     if (present[QT_T1]) {  // the split of x
         GuArgs q = b;
@@ -520,7 +538,7 @@ void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* 
         q.hsc = hsc;
         q.items = items + (size_t)(QT_T1 - 1) * L.maxrec;
         q.wl_len = flags + 8 + QT_T1;
-        launch_gateup_mm<QT_T1>(q, records_bound(present[QT_T1], P), s);
+        launch_gateup_mm<QT_T1>(q, records_bound(present[QT_T1], P), s, gateup_spans(ex, QT_T1));
     }
     mark(2);
 }

@@ -643,6 +643,40 @@ def test_prefill_graph_replay(rl, cases, name):
     log(f"prefill graph replays bit-identical ({name})")
 
 
+def test_gateup_matrices_far_apart(rl):
+    """T1 experts whose gate and up matrices lie more than 2 GiB apart in the arena take the
+    gate/up kernel whose windows use one buffer resource per matrix (the spanning resource needs
+    both within 2^31 bytes): same experts, same inputs, bit-identical output to the compact layout
+    (itself checked against the oracle by the other tests)."""
+    import torch
+
+    from workload import DESC_DTYPE
+
+    wl = make_workload("t1_2048", seed=71, T=80, E=4, H=1024, I=256, k=2)
+    x, ids, w, ex = to_device(wl)
+    near = rl.prefill(x, ids, w, ex)
+    e_np = wl.experts
+    mb = e_np.H * e_np.I // 256 * BLOCK_BYTES[QTYPE_T1]
+    far = 1 << 31
+    desc = np.zeros(e_np.E, DESC_DTYPE)
+    desc["qtype"] = QTYPE_T1
+    src = torch.from_numpy(np.ascontiguousarray(e_np.arena)).cuda()
+    arena = torch.zeros(far + 4 * e_np.E * mb + 64, dtype=torch.uint8, device="cuda")
+    for e in range(e_np.E):
+        g0 = 4 * e * mb
+        u0 = far + 4 * e * mb  # up more than 2 GiB after gate
+        d0 = g0 + 2 * mb
+        for (which, dst) in (("gate_off", g0), ("up_off", u0), ("down_off", d0)):
+            so = int(e_np.desc[which][e])
+            arena[dst:dst + mb].copy_(src[so:so + mb])
+            desc[which][e] = dst
+    ex_far = rl.DeviceExperts(arena, desc, e_np.E, e_np.H, e_np.I)
+    far_out = rl.prefill(x, ids, w, ex_far)
+    assert torch.equal(near, far_out)
+    log("gate/up with matrices 2 GiB apart: bit-identical")
+    del arena, ex_far
+
+
 def test_chunked_layer_bit_identical_to_one_call(orc, rl):
     """A layer taken as consecutive calls of at most 128 tokens (the 8,192-token workload runs as
     four 2,048-token calls) gives bit-identical outputs to one call over all its tokens: every
