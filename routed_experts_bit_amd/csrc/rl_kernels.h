@@ -716,19 +716,44 @@ __device__ __forceinline__ uint32_t win_lane_byte(int lane) {
 // per quarter, measured 10 us slower than the narrow layout).  In both layouts the 16 rows of a
 // strip read by one lane group fall on distinct banks: wide row 4q + j of strip t starts at
 // 1040q + 256t + 64j bytes, bank 4q + 16j.
+// Linear (Q2B, 4 strips from one resource): the 64 rows' 80-byte windows back to back (row 16t +
+// r at 80 (16t + r) bytes: 80 bytes = 20 banks, so 16 consecutive rows fall on distinct banks),
+// filled by 5 instructions of 64 lanes (slot s = 64i + L holds 16 bytes s % 5 of row s / 5).
 template <int QT, int NT, int NMAT, bool SPAN = true>
 struct WinLay {
     typedef WinGeo<QT> G;
-    static constexpr bool WIDE = QT == QT_T1 && NT == 4 && (NMAT == 1 || SPAN);
+    static constexpr bool ONE_RES = NT == 4 && (NMAT == 1 || SPAN);
+    static constexpr bool WIDE = QT == QT_T1 && ONE_RES;
+    static constexpr bool LINEAR = QT == QT_Q2B && ONE_RES;
     static constexpr int QS = NT * 256 + 16;  // wide: bytes per quarter
-    static constexpr int WAVE_BYTES = WIDE ? 4 * QS : NT * G::WS;
-    static constexpr int LOADS = WIDE ? 4 : 4 * NT;  // buffer-to-LDS instructions per block
+    static constexpr int WAVE_BYTES = WIDE ? 4 * QS : LINEAR ? NT * 16 * G::WIN : NT * G::WS;
+    // per-lane offsets per block (wide: one per quarter; linear: one per instruction; narrow: one per strip)
+    static constexpr int NOFF = LINEAR ? NT * 16 * G::WIN / 1024 : NT;
+    static constexpr int LOADS = WIDE ? 4 : LINEAR ? NOFF : 4 * NT;  // buffer-to-LDS instructions per block
+    static_assert(!LINEAR || (NT * 16 * G::WIN) % 1024 == 0, "whole 64-lane loads");
     __device__ static __forceinline__ const uint32_t* win(uint8_t* wave_base, int t, int r) {
         if constexpr (WIDE)
             return (const uint32_t*)(wave_base + QS * (r >> 2) + 256 * t + 64 * (r & 3));
+        else if constexpr (LINEAR)
+            return (const uint32_t*)(wave_base + (16 * t + r) * G::WIN);
         else
             return (const uint32_t*)(wave_base + t * G::WS + G::WQ * (r >> 2) + G::WIN * (r & 3));
     }
+    // one-resource layouts: the strip, row and 16-byte piece that `lane` fetches with load i, and
+    // that load's LDS offset in the wave's area
+    __device__ static __forceinline__ void lane_piece(int i, int lane, int& t, int& r, int& p) {
+        if constexpr (WIDE) {
+            t = lane >> 4;
+            r = 4 * i + ((lane >> 2) & 3);
+            p = lane & 3;
+        } else {
+            const int sl = 64 * i + lane, R = sl / 5;
+            t = R >> 4;
+            r = R & 15;
+            p = sl - 5 * R;
+        }
+    }
+    __device__ static __forceinline__ int load_lds_off(int i) { return WIDE ? QS * i : 1024 * i; }
 };
 
 // A staged step of an activation row is 256 bytes in 16 pieces of 16 bytes; piece 4g + j
@@ -977,11 +1002,11 @@ struct GuChunk {
     // lane L's offset in quarter q (see WinLay).
     __device__ __forceinline__ void wload_from(const BufSrc& sg, const BufSrc& su, const uint32_t* wo,
                                                const uint32_t* wxx, uint32_t blk) {
-        if constexpr (WLay::WIDE) {  // (one resource: sg; for gate/up it spans both matrices)
+        if constexpr (WLay::ONE_RES) {  // (one resource: sg; for gate/up it spans both matrices)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(sg.r, (lds_void*)(wbase() + WLay::QS * q), 16,
-                                                         (wo[q] + blk) & ~3u, 0, 0, 0);
+            for (int i = 0; i < WLay::NOFF; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(sg.r, (lds_void*)(wbase() + WLay::load_lds_off(i)), 16,
+                                                         (wo[i] + blk) & ~3u, 0, 0, 0);
         } else if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -1352,7 +1377,7 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
         const int rows_n = has_next ? min(64, recn.ne - mcn) : 1;
         // wide gate/up windows: one resource from the lower of the gate and up matrices to the end
         // of the higher one, each lane's offsets relative to it
-        constexpr bool COMB = WLay::WIDE && MODE == GU_GATEUP;
+        constexpr bool COMB = WLay::ONE_RES && MODE == GU_GATEUP;
         const uint64_t lo = COMB ? min(rec.off[0], rec.off[1]) : rec.off[MODE == GU_GATEUP ? 0 : 2];
         const uint64_t lo_n = COMB ? min(recn.off[0], recn.off[1]) : recn.off[MODE == GU_GATEUP ? 0 : 2];
         const uint32_t span = COMB ? (uint32_t)(max(rec.off[0], rec.off[1]) - lo) + mat_bytes : mat_bytes;
@@ -1366,21 +1391,27 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
         // weight row of output position c; quarter 3 of a strip starting at position c0 begins
         // at row col(c0 + 12), which for t1_hcol's tail tiles is not col(c0) + 12
         auto col = [&](int c) { return HCOL ? t1_hcol(c, a.N) : c; };
-        uint32_t roff[NT], woff[NT], woff_n[NT], wx[NT], wx_n[NT];
+        uint32_t roff[NT], woff[WLay::NOFF], woff_n[WLay::NOFF], wx[NT], wx_n[NT];
+        if constexpr (WLay::ONE_RES) {  // entry i: the lane's piece of load i (see WinLay)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int c0 = colw + 16 * (t % NTI), c0n = colw_n + 16 * (t % NTI);
-            roff[t] = (uint32_t)col(c0 + n) * row_bytes;
-            if constexpr (WLay::WIDE) {  // entry t: quarter t of the lane's own strip (lane >> 4)
-                const int tl = lane >> 4, j = (lane >> 2) & 3;
+            for (int i = 0; i < WLay::NOFF; ++i) {
+                int tl, r, pc;
+                WLay::lane_piece(i, lane, tl, r, pc);
                 const int l0 = colw + 16 * (tl % NTI), l0n = colw_n + 16 * (tl % NTI);
                 uint32_t mo = 0, mo_n = 0;  // the lane's matrix within the combined resource
                 if constexpr (COMB) {
                     mo = (uint32_t)(rec.off[tl < NTI ? 0 : 1] - lo);
                     mo_n = (uint32_t)(recn.off[tl < NTI ? 0 : 1] - lo_n);
                 }
-                woff[t] = mo + (uint32_t)col(l0 + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
-                woff_n[t] = mo_n + (uint32_t)col(l0n + 4 * t + j) * row_bytes + 16u * (uint32_t)(lane & 3);
+                woff[i] = mo + (uint32_t)col(l0 + r) * row_bytes + 16u * (uint32_t)pc;
+                woff_n[i] = mo_n + (uint32_t)col(l0n + r) * row_bytes + 16u * (uint32_t)pc;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int c0 = colw + 16 * (t % NTI), c0n = colw_n + 16 * (t % NTI);
+            roff[t] = (uint32_t)col(c0 + n) * row_bytes;
+            if constexpr (WLay::ONE_RES) {
                 wx[t] = wx_n[t] = 0u;
             } else {
                 woff[t] = (uint32_t)col(c0 + win_lane_row<QT>(lane)) * row_bytes + win_lane_byte<QT>(lane);
@@ -1422,9 +1453,9 @@ __global__ __launch_bounds__(64 * GU_NW, 2) void k_t1_f8(GuArgs a) {
     gu_kernel<QT_T1, MODE, NTI, SPAN>(a);
 }
 // Q2B experts on the 16-bit MFMA: the same two uses
-template <int MODE, int NTI>
+template <int MODE, int NTI, bool SPAN>
 __global__ __launch_bounds__(64 * GU_NW, 2) void k_q2_mm(GuArgs a) {
-    gu_kernel<QT_Q2B, MODE, NTI, false>(a);
+    gu_kernel<QT_Q2B, MODE, NTI, SPAN>(a);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1465,13 +1496,13 @@ struct DnSweep {
     typedef WinLay<QT, NT, 1> WLay;
     __device__ __forceinline__ uint8_t* wbase() const { return sh.wts + wave * WLay::WAVE_BYTES; }
     __device__ __forceinline__ const uint32_t* win(int t, int r) const { return WLay::win(wbase(), t, r); }
-    // narrow: wo[t] is the lane's offset in quarter 0 of strip t; wide: wo[q] its offset in quarter q
+    // narrow: wo[t] is the lane's offset in quarter 0 of strip t; wide / linear: wo[i] its offset for load i
     __device__ __forceinline__ void wload_from(const BufSrc& sw, const uint32_t* wo, uint32_t blk) {
-        if constexpr (WLay::WIDE) {
+        if constexpr (WLay::ONE_RES) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wbase() + WLay::QS * q), 16,
-                                                         (wo[q] + blk) & ~3u, 0, 0, 0);
+            for (int i = 0; i < WLay::NOFF; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(sw.r, (lds_void*)(wbase() + WLay::load_lds_off(i)), 16,
+                                                         (wo[i] + blk) & ~3u, 0, 0, 0);
         } else if ((threadIdx.x & 63) < 4 * G::WL) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -1546,14 +1577,21 @@ __device__ __forceinline__ void dn_chunk(const GuArgs& a, const GuShared& sh, co
         const int col0 = cbase + s * DN_SW + wave * (16 * DN_NT);
         const bool last = s + 1 == nsw;
         const int col0n = last ? cbase_next + wave * (16 * DN_NT) : col0 + DN_SW;
-        uint32_t roff[DN_NT], woff[DN_NT], woff_n[DN_NT];
+        typedef WinLay<QT, DN_NT, 1> WLay;
+        uint32_t roff[DN_NT], woff[WLay::NOFF], woff_n[WLay::NOFF];
+        if constexpr (WLay::ONE_RES) {  // entry i: the lane's piece of load i
+#pragma unroll
+            for (int i = 0; i < WLay::NOFF; ++i) {
+                int tl, r, pc;
+                WLay::lane_piece(i, lane, tl, r, pc);
+                woff[i] = ((uint32_t)col0 + (uint32_t)(16 * tl + r)) * rowb + 16u * (uint32_t)pc;
+                woff_n[i] = ((uint32_t)col0n + (uint32_t)(16 * tl + r)) * rowb + 16u * (uint32_t)pc;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < DN_NT; ++t) {
             roff[t] = (uint32_t)(col0 + 16 * t + n) * rowb;
-            if constexpr (WinLay<QT, DN_NT, 1>::WIDE) {  // entry t: quarter t of the lane's strip
-                const uint32_t r = (uint32_t)(16 * (lane >> 4) + 4 * t + ((lane >> 2) & 3));
-                woff[t] = ((uint32_t)col0 + r) * rowb + 16u * (uint32_t)(lane & 3);
-                woff_n[t] = ((uint32_t)col0n + r) * rowb + 16u * (uint32_t)(lane & 3);
+            if constexpr (WLay::ONE_RES) {
             } else {
                 woff[t] = ((uint32_t)(col0 + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
                 woff_n[t] = ((uint32_t)(col0n + 16 * t) + win_lane_row<QT>(lane)) * rowb + win_lane_byte<QT>(lane);
@@ -1649,12 +1687,14 @@ __device__ __forceinline__ void dn_kernel(const GuArgs& a) {
         if (first) {  // the first sweep's windows (later ones are loaded by the sweep before)
             const int col0 = cbase + wave * (16 * DN_NT);
             uint8_t* wb = wts + wave * WLay::WAVE_BYTES;
-            if constexpr (WLay::WIDE) {
+            if constexpr (WLay::ONE_RES) {
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const uint32_t r = (uint32_t)(16 * (lane >> 4) + 4 * qq + ((lane >> 2) & 3));
-                    const uint32_t wo = ((uint32_t)col0 + r) * rowb + 16u * (uint32_t)(lane & 3);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wb + WLay::QS * qq), 16, wo & ~3u, 0, 0, 0);
+                for (int i = 0; i < WLay::NOFF; ++i) {
+                    int tl, r, pc;
+                    WLay::lane_piece(i, lane, tl, r, pc);
+                    const uint32_t wo = ((uint32_t)col0 + (uint32_t)(16 * tl + r)) * rowb + 16u * (uint32_t)pc;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(srcw.r, (lds_void*)(wb + WLay::load_lds_off(i)), 16, wo & ~3u,
+                                                             0, 0, 0);
                 }
             } else if ((lane & 63) < 4 * G::WL) {
 #pragma unroll

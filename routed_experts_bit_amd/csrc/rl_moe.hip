@@ -281,7 +281,7 @@ constexpr auto mm_kernel() {
     if constexpr (QT == QT_T1)
         return &k_t1_f8<MODE, NTI, SPAN>;
     else
-        return &k_q2_mm<MODE, NTI>;
+        return &k_q2_mm<MODE, NTI, SPAN>;
 }
 template <int QT>
 constexpr auto dn_kernel_of() {
@@ -320,7 +320,7 @@ void launch_gateup_mm(const GuArgs& a, int n_experts, hipStream_t s, bool span) 
     GuArgs b = a;
     if (a.N % 128 == 0) {
         b.ns = a.N / 128;
-        if (QT == QT_T1 && span)
+        if (span)
             launch_mm<QT, GU_GATEUP, 2, true>(b, n_experts, s);
         else
             launch_mm<QT, GU_GATEUP, 2>(b, n_experts, s);
@@ -528,7 +528,7 @@ void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* 
         q.act = reinterpret_cast<const uint8_t*>(x);
         q.items = items + (size_t)(QT_Q2B - 1) * L.maxrec;
         q.wl_len = flags + 8 + QT_Q2B;
-        launch_gateup_mm<QT_Q2B>(q, records_bound(present[QT_Q2B], P), s, false);
+        launch_gateup_mm<QT_Q2B>(q, records_bound(present[QT_Q2B], P), s, gateup_spans(ex, QT_Q2B));
     }
     if (present[QT_T1]) {  // the split of x
         GuArgs q = b;
