@@ -95,7 +95,7 @@ def test_dequant_real_matrix(orc, rl, qtype):
     "T,k,E,kind",
     [(1, 1, 1, "uniform"), (64, 2, 8, "uniform"), (2048, 10, 512, "uniform"), (1090, 10, 512, "skewed"),
      (300, 16, 1024, "dup"), (4096, 8, 64, "uniform"), (5, 3, 1024, "uniform"), (8192, 10, 512, "skewed"),
-     (777, 13, 3, "uniform")],
+     (777, 13, 3, "uniform"), (3277, 10, 1000, "uniform"), (4095, 8, 1024, "skewed")],
 )
 def test_group_pairs_bit_exact(orc, rl, T, k, E, kind):
     import torch
