@@ -89,14 +89,19 @@ struct PairIds {
     }
 };
 
-// Work records: an expert's pairs are cut into records of at most REC_PAIRS sorted pairs, so that
-// a hot expert (the shared expert has a pair for every token) is spread over many work items.  96
-// pairs = two down chunks of 48 (or a 64-row and a 32-row gate/up chunk): every expert up to 96
-// pairs stays one record, so no chunk of the down kernel is cut short by a record boundary
-// (records of 64 pairs made a 74-pair expert three down chunks, 48 + 16 + 10, and the Zipf-routed
-// Q2B layer's down 17 us slower).
+// Work records: an expert's sorted pairs as one record when it has at most REC_PAIRS of them,
+// else cut into records of REC_HOT, so that a hot expert (the shared expert has a pair for every
+// token) is spread over many work items of about the size of the others.  96 pairs = two down
+// chunks of 48 (or a 64-row and a 32-row gate/up chunk): every expert up to 96 pairs stays one
+// record, so no chunk of the down kernel is cut short by a record boundary (records of 64 pairs
+// made a 74-pair expert three down chunks, 48 + 16 + 10, and the Zipf-routed Q2B layer's down
+// 17 us slower).  Above 96 pairs, records of 48 decode the expert's weights as often as records
+// of 96 do (one 48-row chunk each, against 64 + 32 rows) in items half as long (the MoE block of
+// the 2048-token T1 layer, whose shared expert has 2,048 pairs: ~19 us shorter).
 constexpr int REC_PAIRS = 96;
-__host__ __device__ constexpr int max_records(int E, int P) { return E + (P + REC_PAIRS - 1) / REC_PAIRS; }
+constexpr int REC_HOT = REC_PAIRS / 2;
+__host__ __device__ constexpr int rec_size(int pairs) { return pairs > REC_PAIRS ? REC_HOT : REC_PAIRS; }
+__host__ __device__ constexpr int max_records(int E, int P) { return E + (P + REC_HOT - 1) / REC_HOT; }
 
 struct GroupArgs {
     PairIds pid;
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
     __syncthreads();
     if (tid == 0 && bad_sh) atomicOr(&a.flags[0], FLAG_BAD_ID);
 
-    // per-type work lists of records (at most REC_PAIRS pairs each), binned by record size,
+    // per-type work lists of records (rec_size pairs at most), binned by record size,
     // larger records first
     if (lister && a.desc != nullptr) {
         static_assert(REC_PAIRS < NBIN, "record sizes are bins");
@@ -293,8 +298,9 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
                 atomicOr(&bad_sh, 2);
                 continue;
             }
-            if (c >= REC_PAIRS) atomicAdd(&bins[q - 1][REC_PAIRS], c / REC_PAIRS);
-            if (c % REC_PAIRS) atomicAdd(&bins[q - 1][c % REC_PAIRS], 1);
+            const int rp = rec_size(c);
+            if (c >= rp) atomicAdd(&bins[q - 1][rp], c / rp);
+            if (c % rp) atomicAdd(&bins[q - 1][c % rp], 1);
         }
         __syncthreads();
         if (tid < 128) {  // start of each bin in the type's list, high counts first: wave q scans type q
@@ -332,8 +338,9 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             r.off[1] = dl[i].up_off;
             r.off[2] = dl[i].down_off;
             const int first = scan[e] - c;
-            for (int p = 0; p < c; p += REC_PAIRS) {
-                const int sz = min(REC_PAIRS, c - p);
+            const int rp = rec_size(c);
+            for (int p = 0; p < c; p += rp) {
+                const int sz = min(rp, c - p);
                 r.p0 = first + p;
                 r.ne = sz;
                 a.items[(size_t)(q - 1) * a.maxrec + atomicAdd(&bins[q - 1][sz], 1)] = r;

@@ -366,7 +366,10 @@ void launch_hsplit(const GuArgs& a, int P, hipStream_t s) {
     launch_split<SPLIT_H>(sa, s);
 }
 // Columns of H per work item of the LDS-held down kernel (I a multiple of 256, at most 512).
-int down_item_cols(int32_t H) { return H % 1024 == 0 ? 1024 : (H % 512 == 0 ? 512 : 256); }
+// (512 columns: four items per work-group at 2048 columns and 512 experts, so records of
+// different sizes even out; with items of 1024 columns the down kernel of the mixed-type layer
+// took 117 against 102 us, of the Zipf-routed Q2B layer 86 against 81 us)
+int down_item_cols(int32_t H) { return H % 512 == 0 ? 512 : 256; }
 
 // Down on the LDS-window kernels (I a multiple of 256): for I <= 512 the activations are held in
 // LDS, items of up to 1024 columns; else 4 waves x 4 tiles = 256 output columns per item.
@@ -483,8 +486,8 @@ void launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t*
 #undef RL_RT
 }
 
-// Upper bound of the work records of one block type (its experts, plus one per REC_PAIRS pairs).
-int records_bound(int n_experts, int64_t P) { return n_experts + (int)((P + REC_PAIRS - 1) / REC_PAIRS); }
+// Upper bound of the work records of one block type (its experts, plus one per REC_HOT pairs).
+int records_bound(int n_experts, int64_t P) { return n_experts + (int)((P + REC_HOT - 1) / REC_HOT); }
 
 // grouping + gate/up for every present type; returns the layout used.  With h8 (T1, I <= 512)
 // the T1 gate/up writes its h rows split for the fp8 down kernel (h8, with k-group scales hsc)
