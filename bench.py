@@ -255,7 +255,9 @@ def main():
             rl.prefill(x[c0:c1], ids_r[c0:c1], w_r[c0:c1], exps, out=out[c0:c1], ws=ws)
 
     def time_layer(fn, sets_):
-        for i in range(5):
+        # 40 untimed calls first: after the short 1-2 row kernels the clocks need tens of ms of
+        # load to settle (5 calls left the MoE block ~40 us slower than on a warm GPU)
+        for i in range(40):
             fn(sets_[i % len(sets_)])
         torch.cuda.synchronize()
         e0.record(stream)
