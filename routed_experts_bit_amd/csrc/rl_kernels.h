@@ -837,17 +837,29 @@ struct GuTables {
 // work-groups of the XCD (blockIdx = 8*j + xcd: work-groups are dealt round-robin over the
 // XCDs) take the items in snake order, round q taking item q*nw + j (q even) or
 // q*nw + nw-1-j (q odd), which balances a longest-first list without atomics; every item of
-// an expert stays on one XCD (one L2 for its activation rows).
+// an expert stays on one XCD (one L2 for its activation rows).  HALVES: the first half of the
+// XCD's work-groups (j < nw/2, one per CU) takes the first, longer half of every round and the
+// second half the rest, each half in its own snake order.  The second work-group dispatched to
+// a CU issues behind the first one's waves: per-work-group time stamps of the gate/up kernel put
+// j < nw/2 at ~121 us and j >= nw/2 at ~137 us for the same work (a reversed assignment keeps
+// the gap with the position, not the items); with the halves the kernel is 0.5-4 us shorter
+// (the down kernel, whose halves differ less, gains nothing).
 struct StaticSched {
     int xcd, j, nw, ns, nitems;
-    __device__ inline StaticSched(int n_ranks, int ns_) {
+    bool halves;
+    __device__ inline StaticSched(int n_ranks, int ns_, bool halves_ = false) {
         xcd = blockIdx.x & 7;
         j = blockIdx.x >> 3;
         nw = gridDim.x >> 3;
         ns = ns_;
         nitems = (n_ranks > xcd ? (n_ranks - xcd + 7) / 8 : 0) * ns;
+        halves = halves_ && nw >= 2 && (nw & 1) == 0;
     }
-    __device__ inline int item(int q) const { return q * nw + ((q & 1) ? nw - 1 - j : j); }
+    __device__ inline int item(int q) const {
+        if (!halves) return q * nw + ((q & 1) ? nw - 1 - j : j);
+        const int h = nw >> 1, m = j >= h ? 1 : 0, jj = j - m * h;
+        return q * nw + m * h + ((q & 1) ? h - 1 - jj : jj);
+    }
     __device__ inline int rank(int ix) const { return (ix / ns) * 8 + xcd; }
     __device__ inline int slice(int ix) const { return ix % ns; }
 };
@@ -1339,7 +1351,7 @@ __device__ __forceinline__ void gu_kernel(const GuArgs& a) {
     constexpr bool HCOL = QT == QT_T1 && MODE == GU_GATEUP;  // output columns in t1_hcol order
     __shared__ float hred[HCOL ? GU_NW * 64 : 1];
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63, n = lane & 15, g = lane >> 4;
-    const StaticSched sc(uni(*a.wl_len), a.ns);
+    const StaticSched sc(uni(*a.wl_len), a.ns, MODE == GU_GATEUP);
     if (sc.item(0) >= sc.nitems) return;  // uniform over the work-group
     Tab::build(t64, tbl8, tid, NTHR);
     GuShared sh0 = Tab::shared(ring0, ring1, wts, t64, tbl8, rscale, rdst);
