@@ -2090,8 +2090,9 @@ __device__ __forceinline__ void gv_load_pairs(const GvArgs& a, GvPair* sp) {
 // of gv_xs_bytes(R, H) bytes.
 __host__ __device__ constexpr int gv_xs_row(int H) { return H + 16 * 8; }  // halfwords per staged row
 __host__ __device__ constexpr size_t gv_xs_bytes(int R, int H) { return (size_t)R * gv_xs_row(H) * 2; }
-template <int QMASK, int S1, int MAXS>
-__global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
+template <int QMASK, int S1, int MAXS, int NTHR>
+__global__ __launch_bounds__(NTHR) void k_gv_gateup(GvArgs a) {
+    constexpr int NW = NTHR / 64;
     __shared__ GvTables<QMASK, false> tb;
     __shared__ GvPair sp[GV_MAX_PAIRS];
     extern __shared__ u32x4 gv_xs[];
@@ -2099,12 +2100,12 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
     gv_load_pairs(a, sp);  // the pair table first: its loads are in flight while the rest is staged
     {
         const int units = a.H / 8, run = a.H / 128;  // 16-byte units per row and per lane run
-        for (int i = tid; i < a.R * units; i += 256) {
+        for (int i = tid; i < a.R * units; i += NTHR) {
             const int r = i / units, u = i - r * units;
             gv_xs[r * (gv_xs_row(a.H) / 8) + u + u / run] = reinterpret_cast<const u32x4*>(a.x)[i];
         }
     }
-    tb.load(tid, 256);
+    tb.load(tid, NTHR);
     if (blockIdx.x == 0 && tid < FLAGS_WORDS) a.flags[tid] = 0;
     __syncthreads();
     if (blockIdx.x == 0 && tid < a.R * a.k) {
@@ -2116,7 +2117,7 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
     const int half_i = a.I >> 1;
     const int total = a.R * a.k * half_i;
     const int span = a.H >> 4;
-    for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < total; wv += gridDim.x * 4) {
+    for (int wv = blockIdx.x * NW + (threadIdx.x >> 6); wv < total; wv += gridDim.x * NW) {
         const int pr = wv / half_i;
         const int i0 = 2 * (wv % half_i);
         const int r = pr / a.k;
@@ -2142,8 +2143,9 @@ __global__ __launch_bounds__(256) void k_gv_gateup(GvArgs a) {
 // each lane I/16 values of row c of that expert's W_down; after the 16-lane reduction the slot
 // outputs are added to the accumulator in selection order j = 0..k-1.  The weights of all
 // rounds are loaded before the first is decoded.
-template <int QMASK, int S2, int MAXS>
-__global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
+template <int QMASK, int S2, int MAXS, int NTHR>
+__global__ __launch_bounds__(NTHR) void k_gv_down(GvArgs a) {
+    constexpr int NW = NTHR / 64;
     __shared__ GvTables<QMASK, true> tb;
     __shared__ GvPair sp[GV_MAX_PAIRS];
     __shared__ float wsh[GV_MAX_PAIRS];
@@ -2151,13 +2153,13 @@ __global__ __launch_bounds__(256) void k_gv_down(GvArgs a) {
         sp[threadIdx.x] = a.pairs[threadIdx.x];  // resolved by the gate/up kernel
         wsh[threadIdx.x] = a.weight(threadIdx.x);
     }
-    tb.load(threadIdx.x, 256);
+    tb.load(threadIdx.x, NTHR);
     __syncthreads();
     const int lane = threadIdx.x & 63, gq = lane >> 4, q = lane & 15;
     const int span = a.I >> 4;
     const int nst = span / S2;
     constexpr int MAXR = GV_MAX_PAIRS / 2 / 4;  // rounds of 4 slots (k <= 16)
-    for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < a.R * a.H; wv += gridDim.x * 4) {
+    for (int wv = blockIdx.x * NW + (threadIdx.x >> 6); wv < a.R * a.H; wv += gridDim.x * NW) {
         const int r = wv / a.H, c = wv % a.H;
         // loads of every round
         StripRaw<QT_T1, S2> rt[MAXR][MAXS];
