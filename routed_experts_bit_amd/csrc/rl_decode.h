@@ -305,6 +305,22 @@ struct Strip {
         r[3] = (uint32_t)(hi >> 32);
         return r;
     }
+
+    // the same operand divided by its sub-scale, from the unit row (s = 1) of the value table
+    // (val1 = 256 entries); sub(f / FPS) is the factor that restores it
+    __host__ __device__ inline u32x4 frag1(int f, const uint64_t* val1) const {
+        const uint32_t w = code[f >> 1] >> (16 * (f & 1));
+        const uint64_t lo = val1[w & 255u];
+        const uint64_t hi = val1[(w >> 8) & 255u];
+        u32x4 r;
+        r[0] = (uint32_t)lo;
+        r[1] = (uint32_t)(lo >> 32);
+        r[2] = (uint32_t)hi;
+        r[3] = (uint32_t)(hi >> 32);
+        return r;
+    }
+    // sub-scale i of the strip (0 when the block scale is 0)
+    __host__ __device__ inline float sub(int i) const { return (float)(sb[i] >> 8); }
 };
 
 // ------------------------------------------------------------------ T1 strips for the fp8 MFMA

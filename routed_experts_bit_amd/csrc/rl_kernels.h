@@ -1963,42 +1963,77 @@ __global__ __launch_bounds__(256) void k_combine(YSlots ys, CombineW cw, float* 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Decode tables of the 1-2 row kernels: the unit row (s = 1) of the value table, i.e. the
+// operands (c - 1) (T1) or (2c - 3) (Q2B) of every byte of four codes, and the T1 digit table;
+// the sub-scale multiplies each sub-scale group's partial sum instead (2 KB of values instead of
+// 16 KB for T1 and 32 KB for Q2B, so a work-group's copy is short).
+template <int QT, bool F16>
+struct alignas(16) GvUnitTables {
+    uint64_t val[256];
+    uint32_t tern[QT == QT_T1 ? 256 : 4];  // (Q2B: padding to whole 16-byte units)
+};
+template <int QT, bool F16>
+constexpr GvUnitTables<QT, F16> make_unit_tables() {
+    GvUnitTables<QT, F16> t{};
+    for (int i = 0; i < 256; ++i) t.val[i] = val_entry<QT, F16>(256 + i);
+    if constexpr (QT == QT_T1)
+        for (int i = 0; i < 256; ++i) t.tern[i] = tern_entry((uint32_t)i);
+    return t;
+}
+template <int QT, bool F16>
+__device__ constexpr GvUnitTables<QT, F16> kGvUnitTables = make_unit_tables<QT, F16>();
+template <int QT, bool F16>
+__device__ __forceinline__ void copy_unit_tables(GvUnitTables<QT, F16>& dst, int tid, int nthr) {
+    static_assert(sizeof(GvUnitTables<QT, F16>) % 16 == 0, "whole 16-byte units");
+    constexpr int N = (int)(sizeof(GvUnitTables<QT, F16>) / 16);
+    const u32x4* s = reinterpret_cast<const u32x4*>(&kGvUnitTables<QT, F16>);
+    u32x4* d = reinterpret_cast<u32x4*>(&dst);
+    for (int i = tid; i < N; i += nthr) d[i] = s[i];
+}
+
 struct NoTables {};
-// only the tables of the types present take LDS (T1 alone: 17 KB, Q2B alone: 32 KB)
+// only the tables of the types present take LDS (T1 alone: 3 KB, Q2B alone: 2 KB)
 template <int QMASK, bool F16>
 struct GvTables {
-    std::conditional_t<(QMASK & 1) != 0, DecodeTables<QT_Q2B, F16>, NoTables> q2b;
-    std::conditional_t<(QMASK & 2) != 0, DecodeTables<QT_T1, F16>, NoTables> t1;
+    std::conditional_t<(QMASK & 1) != 0, GvUnitTables<QT_Q2B, F16>, NoTables> q2b;
+    std::conditional_t<(QMASK & 2) != 0, GvUnitTables<QT_T1, F16>, NoTables> t1;
     __device__ inline void load(int tid, int nthr) {
-        if constexpr (QMASK & 1) copy_tables(q2b, tid, nthr);
-        if constexpr (QMASK & 2) copy_tables(t1, tid, nthr);
+        if constexpr (QMASK & 1) copy_unit_tables(q2b, tid, nthr);
+        if constexpr (QMASK & 2) copy_unit_tables(t1, tid, nthr);
     }
 };
 
 // sum over the S values of one strip (inside one block) of w_i * xs[i], times the block scale;
 // xs is bf16 bits (XS_BF16, weights decoded to bf16) or fp16 bits (weights decoded to fp16).
-// Fixed order: pairs (2i, 2i+1) ascending, then the scale.
+// Fixed order: per sub-scale group, pairs (2i, 2i+1) ascending of the unit operands, times the
+// sub-scale, groups ascending, then the block scale.
 template <int QT, int S, bool XS_BF16>
 __device__ __forceinline__ float strip_dot_raw(const StripRaw<QT, S>& raw, const uint16_t* xs,
-                                               const DecodeTables<QT, !XS_BF16>& tb) {
-    Strip<QT, S> st;
+                                               const GvUnitTables<QT, !XS_BF16>& tb) {
+    typedef Strip<QT, S> St;
+    St st;
     st.prepare(raw, tb.tern);
     float part = 0.f;
 #pragma unroll
-    for (int f = 0; f < S / 8; ++f) {
-        const u32x4 fr = st.frag(f, tb.val);
-        const u32x4 xv = *(const u32x4*)(xs + 8 * f);
+    for (int gi = 0; gi < St::NSB; ++gi) {
+        float pg = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // through scalars: a bit_cast straight from a vector element reads element 0 only
-            // with this compiler
-            const uint32_t fw = fr[i], xw = xv[i];
-            if constexpr (XS_BF16)
-                part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, fw), __builtin_bit_cast(bf16x2, xw), part,
-                                                       false);
-            else
-                part = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, fw), __builtin_bit_cast(f16x2, xw), part, false);
+        for (int f = gi * St::FPS; f < (gi + 1) * St::FPS && f < S / 8; ++f) {
+            const u32x4 fr = st.frag1(f, tb.val);
+            const u32x4 xv = *(const u32x4*)(xs + 8 * f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // through scalars: a bit_cast straight from a vector element reads element 0 only
+                // with this compiler
+                const uint32_t fw = fr[i], xw = xv[i];
+                if constexpr (XS_BF16)
+                    pg = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, fw), __builtin_bit_cast(bf16x2, xw), pg,
+                                                         false);
+                else
+                    pg = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, fw), __builtin_bit_cast(f16x2, xw), pg, false);
+            }
         }
+        part = __fmaf_rn(st.sub(gi), pg, part);
     }
     return part * st.d;
 }
@@ -2008,7 +2043,7 @@ __device__ __forceinline__ float strip_dot_raw(const StripRaw<QT, S>& raw, const
 // is decoded, so a lane waits for memory once.
 template <int QT, int S, int MAXS, bool XS_BF16>
 __device__ __forceinline__ float row_dot_t(const BufSrc& src, int C, int row, int c0, int nst, const uint16_t* xs,
-                                           const DecodeTables<QT, !XS_BF16>& tb) {
+                                           const GvUnitTables<QT, !XS_BF16>& tb) {
     StripRaw<QT, S> raw[MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)

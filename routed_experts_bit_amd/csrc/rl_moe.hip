@@ -427,12 +427,11 @@ bool gv_dim_ok(int d) { return d == 256 || d == 512 || (d % 1024 == 0); }
 
 template <int QMASK>
 void launch_gv(const GvArgs& a, hipStream_t s) {
-    // Work-groups of 512 threads when Q2B tables are in LDS (32 KB, 49 KB with T1's): every
-    // work-group copies its tables, and halving their number measured 2-row Q2B steps 26.5 ->
-    // 22.7 us and mixed-type steps 23.9 -> 19.8 us (1 row) and 36.1 -> 31.5 us (2 rows); the T1
-    // tables (17 KB) copy fast enough that 256 threads (more, smaller work-groups) are better.
-    // (The down kernels for I >= 2048 hold more than 256 registers per lane: 256 threads.)
-    constexpr int NT = QMASK == 2 ? 256 : 512, NW = NT / 64;
+    // Work-groups of 256 threads.  Every work-group copies its decode tables into LDS; with the
+    // full value tables (T1 17 KB, Q2B 32 KB, both 49 KB) work-groups of 512 threads had been
+    // faster for Q2B and mixed layers, with the unit rows (3-5 KB) 256 threads are as fast or
+    // faster for every type mask.
+    constexpr int NT = 256, NW = NT / 64;
     const int waves1 = a.R * a.k * (a.I / 2);
     const int waves2 = a.R * a.H;
     dim3 g1((waves1 + NW - 1) / NW < 1024 ? (waves1 + NW - 1) / NW : 1024);
@@ -455,9 +454,7 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
         RL_GV1(16, 1);
     }
 #undef RL_GV1
-#define RL_GV2(S, M)                                                                                  \
-    hipLaunchKernelGGL((k_gv_down<QMASK, S, M, (M >= 2 ? 256 : NT)>), g2((M >= 2 ? 256 : NT) / 64), \
-                       dim3(M >= 2 ? 256 : NT), 0, s, a)
+#define RL_GV2(S, M) hipLaunchKernelGGL((k_gv_down<QMASK, S, M, NT>), g2(NW), dim3(NT), 0, s, a)
     if (a.I >= 1024) {
         if (a.I <= 1024)
             RL_GV2(64, 1);
