@@ -177,8 +177,11 @@ int rl_moe_noalloc_status(int32_t* flags_out);
 /* The same layer for 1 or 2 rows (decode and 2-row verify; dev75 "Decode", dev72 "2-row
  * verify"): matrix-vector kernels, gate/up + SwiGLU then down + the ordered combine in one
  * dispatch.  T (= rows) must be 1 or 2.  Each row's result is bit-identical to a call with
- * that row alone.  Arguments as rl_moe_prefill; additionally H and I must each be 256, 512 or
- * a multiple of 1024. */
+ * that row alone.  Arguments as rl_moe_prefill; additionally H and I must be multiples of 256
+ * whose D/16 columns per lane (16 lanes per row) make few strips of 64, 32 or 16 columns (the
+ * largest that divides D/16): H at most 8 strips (any multiple of 1024 up to 8192,
+ * 512 x odd up to 3584, 256 x odd up to 1792), I at most 4 (multiples of 1024 up to 4096, 256,
+ * 512, 768, 1536); other sizes return RL_ESHAPE. */
 int rl_moe_decode(const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                   const rl_expert_blobs* experts, float* out, int32_t T, int32_t k,
                   void* workspace, size_t ws_bytes, void* stream);

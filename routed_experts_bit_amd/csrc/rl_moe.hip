@@ -423,7 +423,13 @@ void launch_combine(const YSlots& ys, const CombineW& cw, float* out, int T, int
     }
 }
 
-bool gv_dim_ok(int d) { return d == 256 || d == 512 || (d % 1024 == 0); }
+// 1-2 row kernels: each of the 16 lanes of a row takes d/16 consecutive values in strips of the
+// widest of 64, 32 and 16 values that divides them (a strip stays inside one block and one
+// sub-scale group); gate/up holds up to 8 strips per lane (H), down up to 4 per round (I).
+constexpr int gv_strip(int d) { return (d / 16) % 64 == 0 ? 64 : ((d / 16) % 32 == 0 ? 32 : 16); }
+constexpr int gv_nst(int d) { return d / 16 / gv_strip(d); }
+bool gv_dim_ok(int d, int max_nst) { return d >= 256 && d % 256 == 0 && gv_nst(d) <= max_nst; }
+constexpr int gv_maxs(int nst) { return nst <= 1 ? 1 : (nst <= 2 ? 2 : (nst <= 4 ? 4 : 8)); }
 
 template <int QMASK>
 void launch_gv(const GvArgs& a, hipStream_t s) {
@@ -436,37 +442,39 @@ void launch_gv(const GvArgs& a, hipStream_t s) {
     const int waves2 = a.R * a.H;
     dim3 g1((waves1 + NW - 1) / NW < 1024 ? (waves1 + NW - 1) / NW : 1024);
     auto g2 = [&](int nw) { return dim3((waves2 + nw - 1) / nw < 1024 ? (waves2 + nw - 1) / nw : 1024); };
-    // strips of S values per lane: S = 64 for dimensions >= 1024 (then H/1024 or I/1024 strips)
     const size_t xs_bytes = gv_xs_bytes(a.R, a.H);  // x staged in LDS (at most 32.5 KB)
 #define RL_GV1(S, M) hipLaunchKernelGGL((k_gv_gateup<QMASK, S, M, NT>), g1, dim3(NT), xs_bytes, s, a)
-    if (a.H >= 1024) {
-        if (a.H <= 1024)
-            RL_GV1(64, 1);
-        else if (a.H <= 2048)
-            RL_GV1(64, 2);
-        else if (a.H <= 4096)
-            RL_GV1(64, 4);
-        else
-            RL_GV1(64, 8);
-    } else if (a.H == 512) {
-        RL_GV1(32, 1);
-    } else {
-        RL_GV1(16, 1);
+#define RL_GV1S(S)                      \
+    switch (gv_maxs(gv_nst(a.H))) {     \
+        case 1: RL_GV1(S, 1); break;    \
+        case 2: RL_GV1(S, 2); break;    \
+        case 4: RL_GV1(S, 4); break;    \
+        default: RL_GV1(S, 8); break;   \
     }
+    if (gv_strip(a.H) == 64) {
+        RL_GV1S(64)
+    } else if (gv_strip(a.H) == 32) {
+        RL_GV1S(32)
+    } else {
+        RL_GV1S(16)
+    }
+#undef RL_GV1S
 #undef RL_GV1
 #define RL_GV2(S, M) hipLaunchKernelGGL((k_gv_down<QMASK, S, M, NT>), g2(NW), dim3(NT), 0, s, a)
-    if (a.I >= 1024) {
-        if (a.I <= 1024)
-            RL_GV2(64, 1);
-        else if (a.I <= 2048)
-            RL_GV2(64, 2);
-        else
-            RL_GV2(64, 4);
-    } else if (a.I == 512) {
-        RL_GV2(32, 1);
-    } else {
-        RL_GV2(16, 1);
+#define RL_GV2S(S)                      \
+    switch (gv_maxs(gv_nst(a.I))) {     \
+        case 1: RL_GV2(S, 1); break;    \
+        case 2: RL_GV2(S, 2); break;    \
+        default: RL_GV2(S, 4); break;   \
     }
+    if (gv_strip(a.I) == 64) {
+        RL_GV2S(64)
+    } else if (gv_strip(a.I) == 32) {
+        RL_GV2S(32)
+    } else {
+        RL_GV2S(16)
+    }
+#undef RL_GV2S
 #undef RL_GV2
 }
 
@@ -726,7 +734,7 @@ int rl_moe_gate_up(const uint16_t* x, const int32_t* topk_ids, const float* topk
 static int decode_impl(const uint16_t* x, const Route& r, const rl_expert_blobs* experts, float* out, int32_t T,
                        void* workspace, size_t ws_bytes, void* stream) {
     int present[3] = {0, 0, 0};
-    if (experts && (T < 1 || T > 2 || !gv_dim_ok(experts->H) || !gv_dim_ok(experts->I))) return RL_ESHAPE;
+    if (experts && (T < 1 || T > 2 || !gv_dim_ok(experts->H, 8) || !gv_dim_ok(experts->I, 4))) return RL_ESHAPE;
     int rc = check_layer(x, r, experts, out, T, workspace, ws_bytes, present);
     if (rc != RL_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);

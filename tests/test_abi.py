@@ -177,8 +177,11 @@ def test_decode_rows_and_dims(L):
     b, _ = _blobs(H=2048, I=512)
     assert _call(L, "rl_moe_decode", b, T=3, k=10) == RL_ESHAPE
     assert _call(L, "rl_moe_decode", b, T=0, k=10) == RL_ESHAPE
-    b2, _ = _blobs(H=768, I=512)
-    assert _call(L, "rl_moe_decode", b2, T=1, k=10) == RL_ESHAPE
+    # more strips per lane than the 1-2 row kernels take (H 256 x 9, 512 x 9; I 256 x 5,
+    # 512 x 5) and I below 256: refused on the host
+    for H, I in ((2304, 512), (4608, 512), (1024, 1280), (1024, 2560), (1024, 128)):
+        b2, _ = _blobs(H=H, I=I)
+        assert _call(L, "rl_moe_decode", b2, T=1, k=10) == RL_ESHAPE, (H, I)
 
 
 def test_prefill_empty_is_ok(L):

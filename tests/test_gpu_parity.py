@@ -481,9 +481,10 @@ def test_decode_rows_parity_and_bit_identity(orc, rl, types):
     assert rel_l2(two.cpu().numpy(), pre.cpu().numpy()) <= TOL
 
 
-@pytest.mark.parametrize("H,I", [(8192, 256), (256, 4096)])
+@pytest.mark.parametrize("H,I", [(8192, 256), (256, 4096), (1280, 768), (3584, 1536), (1792, 512), (3072, 3072)])
 def test_decode_rows_max_dims(orc, rl, H, I):
-    """The 1-2 row path at the largest hidden and intermediate sizes (mixed block types)."""
+    """The 1-2 row path at the largest hidden and intermediate sizes and at sizes whose columns
+    per lane make an odd number of strips of 16 or 32 (mixed block types)."""
     import torch
 
     ex_np = make_experts(6, H, I, [QTYPE_Q2B] * 3 + [QTYPE_T1] * 3, seed=42)
@@ -497,6 +498,18 @@ def test_decode_rows_max_dims(orc, rl, H, I):
     log(f"  rel_l2={err:.3e}")
     assert err <= TOL
 
+
+
+@pytest.mark.parametrize("H,I", [(2304, 512), (4608, 256), (1024, 1280), (1024, 2560), (1024, 128)])
+def test_decode_rows_refuses_sizes(rl, H, I):
+    """Sizes outside the 1-2 row kernels' strip counts (H > 8 strips per lane, I > 4, I < 256)
+    are refused on the host before any launch."""
+    ex_np = make_experts(2, H, I, [QTYPE_Q2B, QTYPE_T1], seed=44)
+    wl = make_workload("decode_t1", seed=45, T=1, experts=ex_np, E=2, H=H, I=I, k=2)
+    x, ids, w, ex = to_device(wl)
+    log(f"decode refuses H={H} I={I}")
+    with pytest.raises(rl.RlError, match="size outside"):
+        rl.decode(x, ids, w, ex)
 
 # ----------------------------------------------------------------------------- full size
 FULL = {
