@@ -209,18 +209,25 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
 /* Block decode alone (parity hook for the in-kernel weight decode): n_values (a multiple of
  * 256) consecutive values of `blocks` [dev] (any byte address) as float d * s * c into out [dev].
  * `decoder` picks which of the library's device decoders runs, exactly as the kernels run it:
- *   RL_DEC_STRIP        the strip decoder of the 1-2 row kernels and of the down kernel for
- *                       I < 256 (64-value strips, bf16 operand table)
+ *   RL_DEC_STRIP        the full-table strip decoder of the down kernel for I < 256 (64-value
+ *                       strips; operand table with every sub-scale, here in bf16)
  *   RL_DEC_MFMA_GATEUP  the MFMA operand decoder of the gate/up GEMMs (T1: fp8 operands, digit
  *                       selector and fp8 scale tables built on the device; Q2B: bf16 operands);
  *                       value k of a block is written where its operand byte / half stands for
  *   RL_DEC_MFMA_DOWN    the same for the down GEMMs (T1: identical to gate/up; Q2B: fp16 operands)
+ *   RL_DEC_ROWS_GATEUP  the decoder of the 1-2 row gate/up kernel: unit operands (bf16) from the
+ *                       s = 1 row of the value table, times the strip's sub-scale, times the block
+ *                       scale; block b is cut into strips of 64, 32 or 16 values by b % 3 (the
+ *                       three strip widths those kernels use)
+ *   RL_DEC_ROWS_DOWN    the same with the fp16 unit operands of the 1-2 row down kernel
  * Every such product is exact in fp32, so any correct decode is bit-identical to the format's
  * definition.  RL_EINVAL for an unknown qtype or decoder; RL_ESHAPE if the blocks span more than
  * 2^32 - 16 bytes. */
 #define RL_DEC_STRIP 0
 #define RL_DEC_MFMA_GATEUP 1
 #define RL_DEC_MFMA_DOWN 2
+#define RL_DEC_ROWS_GATEUP 3
+#define RL_DEC_ROWS_DOWN 4
 int rl_moe_dequant(int32_t qtype, int32_t decoder, const void* blocks, int64_t n_values, float* out, void* stream);
 
 /* Grouping + fused dequant/gate/up/SwiGLU alone (parity hook): the launches rl_moe_prefill makes

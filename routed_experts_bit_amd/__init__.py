@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     RL_DEC_STRIP,
     RL_DEC_MFMA_GATEUP,
     RL_DEC_MFMA_DOWN,
+    RL_DEC_ROWS_GATEUP,
+    RL_DEC_ROWS_DOWN,
     t1_splits_h,
     RlError,
     DeviceExperts,

@@ -15,6 +15,8 @@ RL_QTYPE_T1 = 2
 RL_DEC_STRIP = 0
 RL_DEC_MFMA_GATEUP = 1
 RL_DEC_MFMA_DOWN = 2
+RL_DEC_ROWS_GATEUP = 3
+RL_DEC_ROWS_DOWN = 4
 _BLOCK_BYTES = {RL_QTYPE_Q2B: 74, RL_QTYPE_T1: 57}
 
 # every entry point declared in include/rl_moe.h

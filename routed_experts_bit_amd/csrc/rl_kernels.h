@@ -1991,6 +1991,68 @@ __device__ __forceinline__ void copy_unit_tables(GvUnitTables<QT, F16>& dst, int
     for (int i = tid; i < N; i += nthr) d[i] = s[i];
 }
 
+// The decoder of the 1-2 row kernels, run as they run it: the unit-row tables copied from the
+// initialised device data, a strip's raw bytes through the buffer loads of StripRaw, the unit
+// operands of frag1 (bf16 for gate/up, F16 = false; fp16 for down, F16 = true), then the strip's
+// sub-scale and the block scale.  Block b is cut into strips of 64, 32 or 16 values by b % 3, so
+// that one call covers the three strip widths; thread j of a block's 16 decodes its strip j (when
+// the block has that many).  (unit * sub) * d is exact in fp32.
+template <int QT, int S, bool F16>
+__device__ __forceinline__ void dequant_rows_strip(const BufSrc& src, uint32_t mis, int j,
+                                                   const GvUnitTables<QT, F16>& tb, float* o) {
+    typedef Strip<QT, S> St;
+    StripRaw<QT, S> raw;
+    raw.load(src, mis, S * j);
+    St st;
+    st.prepare(raw, tb.tern);
+#pragma unroll
+    for (int f = 0; f < S / 8; ++f) {
+        const u32x4 fr = st.frag1(f, tb.val);
+        const float sc = st.sub(f / St::FPS);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = fr[i];
+            float u0, u1;
+            if constexpr (F16) {
+                u0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+                u1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+            } else {
+                u0 = __uint_as_float(w << 16);
+                u1 = __uint_as_float(w & 0xFFFF0000u);
+            }
+            o[S * j + 8 * f + 2 * i] = (u0 * sc) * st.d;
+            o[S * j + 8 * f + 2 * i + 1] = (u1 * sc) * st.d;
+        }
+    }
+}
+
+template <int QT, bool F16>
+__global__ __launch_bounds__(256) void k_dequant_rows(const uint8_t* __restrict__ blocks, int64_t n_blocks,
+                                                      float* __restrict__ out) {
+    __shared__ GvUnitTables<QT, F16> tb;
+    copy_unit_tables(tb, threadIdx.x, 256);
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_blocks * 16) return;
+    const int64_t b = t >> 4;
+    const int j = (int)(t & 15);
+    const uintptr_t base = (uintptr_t)(blocks + b * Fmt<QT>::BYTES);
+    const uint32_t mis = (uint32_t)(base & 3);
+    const BufSrc src((const uint8_t*)(base - mis), mis + Fmt<QT>::BYTES);
+    float* o = out + b * 256;
+    switch ((int)(b % 3)) {
+        case 0:
+            if (j < 4) dequant_rows_strip<QT, 64, F16>(src, mis, j, tb, o);
+            break;
+        case 1:
+            if (j < 8) dequant_rows_strip<QT, 32, F16>(src, mis, j, tb, o);
+            break;
+        default:
+            dequant_rows_strip<QT, 16, F16>(src, mis, j, tb, o);
+            break;
+    }
+}
+
 struct NoTables {};
 // only the tables of the types present take LDS (T1 alone: 3 KB, Q2B alone: 2 KB)
 template <int QMASK, bool F16>

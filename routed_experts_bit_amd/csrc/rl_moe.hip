@@ -805,7 +805,7 @@ int rl_moe_group_pairs(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
 
 int rl_moe_dequant(int32_t qtype, int32_t decoder, const void* blocks, int64_t n_values, float* out, void* stream) {
     if (qtype != QT_Q2B && qtype != QT_T1) return RL_EINVAL;
-    if (decoder < RL_DEC_STRIP || decoder > RL_DEC_MFMA_DOWN) return RL_EINVAL;
+    if (decoder < RL_DEC_STRIP || decoder > RL_DEC_ROWS_DOWN) return RL_EINVAL;
     if (n_values < 0 || n_values % 256) return RL_ESHAPE;
     if (n_values == 0) return RL_OK;
     if (!blocks || !out) return RL_EINVAL;
@@ -818,6 +818,19 @@ int rl_moe_dequant(int32_t qtype, int32_t decoder, const void* blocks, int64_t n
             hipLaunchKernelGGL(k_dequant<QT_Q2B>, grid, dim3(256), 0, s, b, n_blocks, out);
         else
             hipLaunchKernelGGL(k_dequant<QT_T1>, grid, dim3(256), 0, s, b, n_blocks, out);
+        return hip_status();
+    }
+    if (decoder == RL_DEC_ROWS_GATEUP || decoder == RL_DEC_ROWS_DOWN) {
+        dim3 grid((unsigned)((n_blocks * 16 + 255) / 256));
+        const bool f16 = decoder == RL_DEC_ROWS_DOWN;
+        if (qtype == QT_Q2B && !f16)
+            hipLaunchKernelGGL((k_dequant_rows<QT_Q2B, false>), grid, dim3(256), 0, s, b, n_blocks, out);
+        else if (qtype == QT_Q2B)
+            hipLaunchKernelGGL((k_dequant_rows<QT_Q2B, true>), grid, dim3(256), 0, s, b, n_blocks, out);
+        else if (!f16)
+            hipLaunchKernelGGL((k_dequant_rows<QT_T1, false>), grid, dim3(256), 0, s, b, n_blocks, out);
+        else
+            hipLaunchKernelGGL((k_dequant_rows<QT_T1, true>), grid, dim3(256), 0, s, b, n_blocks, out);
         return hip_status();
     }
     // the blocks' bytes must be addressable by 32-bit buffer offsets from their dword base

@@ -192,7 +192,7 @@ def test_prefill_empty_is_ok(L):
 def test_dequant_and_group_codes(L):
     v = C.c_void_p
     assert L.rl_moe_dequant(3, 0, v(0x100), 256, v(0x200), None) == -1
-    assert L.rl_moe_dequant(1, 3, v(0x100), 256, v(0x200), None) == -1   # unknown decoder
+    assert L.rl_moe_dequant(1, 5, v(0x100), 256, v(0x200), None) == -1   # unknown decoder
     assert L.rl_moe_dequant(1, -1, v(0x100), 256, v(0x200), None) == -1
     assert L.rl_moe_dequant(1, 0, v(0x100), 255, v(0x200), None) == -2
     assert L.rl_moe_dequant(2, 1, None, 0, None, None) == 0

@@ -53,25 +53,32 @@ def _decode_blocks(qtype, nb=3159):
 
 
 @pytest.mark.parametrize("qtype", [QTYPE_Q2B, QTYPE_T1])
-@pytest.mark.parametrize("decoder", ["strip", "mfma_gateup", "mfma_down"])
+@pytest.mark.parametrize("decoder", ["strip", "mfma_gateup", "mfma_down", "rows_gateup", "rows_down"])
 def test_dequant_bit_exact(orc, rl, qtype, decoder):
     """Each of the library's device decoders, run as the kernels run it (the MFMA ones with their
     selector and fp8 / 16-bit tables built on the device, windows cut at the block's byte
-    misalignment, operands written at their k-map positions), equals the oracle's decode bit for
+    misalignment, operands written at their k-map positions; the 1-2 row ones with their unit
+    tables copied from device data, at the three strip widths), equals the oracle's decode bit for
     bit: every product d * s * c is exact in fp32.  Blocks at all four byte misalignments."""
     import torch
 
-    dec = {"strip": rl.RL_DEC_STRIP, "mfma_gateup": rl.RL_DEC_MFMA_GATEUP, "mfma_down": rl.RL_DEC_MFMA_DOWN}[decoder]
+    dec = {"strip": rl.RL_DEC_STRIP, "mfma_gateup": rl.RL_DEC_MFMA_GATEUP, "mfma_down": rl.RL_DEC_MFMA_DOWN,
+           "rows_gateup": rl.RL_DEC_ROWS_GATEUP, "rows_down": rl.RL_DEC_ROWS_DOWN}[decoder]
     blk = _decode_blocks(qtype)
     nb = blk.shape[0]
-    flat = blk.reshape(-1)
-    ref = orc.dequant(qtype, flat, nb * 256)
-    for mis in range(4):
-        log(f"dequant qtype={qtype} decoder={decoder} blocks={nb} misalignment={mis}")
-        buf = torch.zeros(flat.size + 8, dtype=torch.uint8, device="cuda")
-        buf[mis:mis + flat.size].copy_(torch.from_numpy(flat))
-        got = rl.dequant(qtype, buf[mis:mis + flat.size], nb * 256, decoder=dec).cpu().numpy()
-        assert np.array_equal(got.astype(np.float64), ref), f"misalignment {mis}"
+    ref_all = orc.dequant(qtype, blk.reshape(-1), nb * 256)
+    # the 1-2 row decoders cut block b of a call into strips of 64, 32 or 16 values by b % 3:
+    # three calls starting one block apart give every block every strip width
+    shifts = range(3) if decoder.startswith("rows") else range(1)
+    for sh in shifts:
+        flat = blk[sh:].reshape(-1)
+        ref = ref_all[256 * sh:]
+        for mis in range(4):
+            log(f"dequant qtype={qtype} decoder={decoder} blocks={nb - sh} misalignment={mis}")
+            buf = torch.zeros(flat.size + 8, dtype=torch.uint8, device="cuda")
+            buf[mis:mis + flat.size].copy_(torch.from_numpy(flat))
+            got = rl.dequant(qtype, buf[mis:mis + flat.size], (nb - sh) * 256, decoder=dec).cpu().numpy()
+            assert np.array_equal(got.astype(np.float64), ref), f"first block {sh}, misalignment {mis}"
 
 
 @pytest.mark.parametrize("qtype", [QTYPE_Q2B, QTYPE_T1])
@@ -85,7 +92,8 @@ def test_dequant_real_matrix(orc, rl, qtype):
         n = 2048 * 512
         ref = orc.dequant(qtype, ex.matrix(1, which), n)
         mb = n // 256 * BLOCK_BYTES[qtype]
-        for dec in (rl.RL_DEC_STRIP, rl.RL_DEC_MFMA_GATEUP, rl.RL_DEC_MFMA_DOWN):
+        for dec in (rl.RL_DEC_STRIP, rl.RL_DEC_MFMA_GATEUP, rl.RL_DEC_MFMA_DOWN, rl.RL_DEC_ROWS_GATEUP,
+                    rl.RL_DEC_ROWS_DOWN):
             got = rl.dequant(qtype, arena[off:off + mb], n, decoder=dec).cpu().numpy()
             assert np.array_equal(got.astype(np.float64), ref)
 
