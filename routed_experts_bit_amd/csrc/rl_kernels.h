@@ -656,7 +656,7 @@ struct GuArgs {
     int32_t* flags;           // status words (flags[0])
     int K, N, ns;
     int k;                    // pairs per token (gate/up: token of pair index q is q / k)
-    int P;                    // pairs (down: y has a spare row P for padding rows)
+    int P;                    // pairs: the length of pair_src (down: y has a spare row P for padding rows)
 };
 
 // Work item of the gate/up kernel: GU_NW waves, each with NTI 16-column tiles of gate and the

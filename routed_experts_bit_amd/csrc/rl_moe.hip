@@ -534,6 +534,7 @@ void run_group_gateup(const uint16_t* x, const Route& r, const rl_expert_blobs* 
     GuArgs b = {};
     b.pair_src = pair_src;
     b.k = kk;
+    b.P = (int)P;
     b.arena = static_cast<const uint8_t*>(ex->arena);
     b.hbuf = hdst;
     b.K = ex->H;
