@@ -72,7 +72,9 @@ def main():
                          "first, so the GPU is already under load)")
     ap.add_argument("--config", default="t1_2048")
     ap.add_argument("--seed", type=int, default=1234)
-    ap.add_argument("--rotate", type=int, default=3, help="distinct arena copies cycled through")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="distinct arena copies cycled through (0: at least 3 and at least 1 GiB in all, so that "
+                         "the weights come from HBM, not the memory-side cache)")
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--oracle-threads", type=int, default=0)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -101,6 +103,8 @@ def main():
         f"pairs/expert min={counts.min()} mean={counts.mean():.1f} max={counts.max()} (gen {time.time() - t0:.1f}s)")
 
     dev = rl.DeviceExperts.from_workload(ex0)
+    if args.rotate <= 0:
+        args.rotate = max(3, -(-(1 << 30) // ex0.arena.nbytes))
     sets = [dev] + [dev.with_arena(dev.arena.clone()) for _ in range(max(args.rotate, 1) - 1)]
     x = torch.from_numpy(wl.x.view(np.int16).copy()).cuda()
     ids = torch.from_numpy(wl.ids).cuda()

@@ -89,18 +89,22 @@ struct PairIds {
     }
 };
 
-// Work records: an expert's sorted pairs as one record when it has at most REC_PAIRS of them,
-// else cut into records of REC_HOT, so that a hot expert (the shared expert has a pair for every
-// token) is spread over many work items of about the size of the others.  96 pairs = two down
-// chunks of 48 (or a 64-row and a 32-row gate/up chunk): every expert up to 96 pairs stays one
-// record, so no chunk of the down kernel is cut short by a record boundary (records of 64 pairs
-// made a 74-pair expert three down chunks, 48 + 16 + 10, and the Zipf-routed Q2B layer's down
-// 17 us slower).  Above 96 pairs, records of 48 decode the expert's weights as often as records
-// of 96 do (one 48-row chunk each, against 64 + 32 rows) in items half as long (the MoE block of
-// the 2048-token T1 layer, whose shared expert has 2,048 pairs: ~19 us shorter).
+// Work records: an expert's sorted pairs in records of REC_PAIRS, except that an expert far above
+// the layer's mean (more than REC_PAIRS pairs and more than 4x P / E: the shared expert has a
+// pair for every token) is cut into records of REC_HOT, so that it is spread over many work items
+// of about the size of the others.  96 pairs = two down chunks of 48 (or a 64-row and a 32-row
+// gate/up chunk): no chunk of the down kernel is cut short by a record boundary (records of 64
+// pairs made a 74-pair expert three down chunks, 48 + 16 + 10, and the Zipf-routed Q2B layer's
+// down 17 us slower).  Records of 48 decode the weights as often as records of 96 do (one 48-row
+// chunk each, against 64 + 32 rows) in items half as long: the MoE block of the 2048-token T1
+// layer, whose shared expert has 2,048 pairs, ~19 us shorter; but where every expert has some
+// hundreds of pairs (one GPU's share of experts), the 64-row gate/up chunks of 96-pair records
+// are ~6 us faster.
 constexpr int REC_PAIRS = 96;
 constexpr int REC_HOT = REC_PAIRS / 2;
-__host__ __device__ constexpr int rec_size(int pairs) { return pairs > REC_PAIRS ? REC_HOT : REC_PAIRS; }
+__host__ __device__ constexpr int rec_size(int pairs, int P, int E) {
+    return pairs > REC_PAIRS && (int64_t)pairs * E > 4 * (int64_t)P ? REC_HOT : REC_PAIRS;
+}
 __host__ __device__ constexpr int max_records(int E, int P) { return E + (P + REC_HOT - 1) / REC_HOT; }
 
 struct GroupArgs {
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
                 atomicOr(&bad_sh, 2);
                 continue;
             }
-            const int rp = rec_size(c);
+            const int rp = rec_size(c, a.P, E);
             if (c >= rp) atomicAdd(&bins[q - 1][rp], c / rp);
             if (c % rp) atomicAdd(&bins[q - 1][c % rp], 1);
         }
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(GROUP_NTHR) void k_group_scatter(GroupArgs a) {
             r.off[1] = dl[i].up_off;
             r.off[2] = dl[i].down_off;
             const int first = scan[e] - c;
-            const int rp = rec_size(c);
+            const int rp = rec_size(c, a.P, E);
             for (int p = 0; p < c; p += rp) {
                 const int sz = min(rp, c - p);
                 r.p0 = first + p;

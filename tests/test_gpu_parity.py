@@ -524,6 +524,7 @@ FULL = {
     "q2b_1090": dict(),
     "t1_2048": dict(),
     "mixed_2048": dict(),
+    "ep8_2048": dict(),  # one GPU's expert share: 64 experts x ~320 pairs
 }
 
 

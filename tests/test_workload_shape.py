@@ -37,8 +37,14 @@ def test_t1_2048_is_uniform():
     assert abs(np.median(c) - 40) <= 2 and c.max() <= 2 * 40
 
 
+def test_ep8_share_has_320_pairs_per_expert():
+    c = _counts("ep8_2048")
+    assert c.sum() == 20480 and CONFIGS["ep8_2048"]["E"] == 64
+    assert abs(np.median(c) - 320) <= 20 and c.min() >= 240 and c.max() <= 400
+
+
 def test_rows_select_distinct_experts_in_descending_weight():
-    for name in ("q2b_1090", "t1_2048", "tiny"):
+    for name in ("q2b_1090", "t1_2048", "tiny", "ep8_2048"):
         ids, w = _route(name)
         assert all(len(set(r)) == CONFIGS[name]["k"] for r in ids.tolist())
         assert np.all(np.diff(w, axis=1) <= 0)

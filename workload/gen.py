@@ -279,6 +279,10 @@ CONFIGS = {
     # 8,192 tokens taken as four consecutive 2,048-token calls (chunk: tokens per call)
     "mixed_8192": dict(T=8192, H=2048, E=512, I=512, k=10, types="mixed", bias=None, chunk=2048),
     "decode_t1": dict(T=2, H=2048, E=512, I=512, k=10, types="t1", bias=None),
+    # one GPU's share of the 512-expert T1 layer sharded by expert over 8 GPUs with 2,048 tokens
+    # per GPU: 64 experts, ~320 pairs each (the received rows stand in as 2,048 tokens x top-10 of
+    # the 64 local experts)
+    "ep8_2048": dict(T=2048, H=2048, E=64, I=512, k=10, types="t1", bias=None),
 }
 
 
