@@ -314,3 +314,32 @@ def test_t1_digit_bytes_checked_on_load():
     ok = ex.arena.copy()
     ok[int(ex.desc["gate_off"][0]) + 20] = 255
     rl.DeviceExperts(ok, ex.desc, ex.E, ex.H, ex.I, device="cpu")
+
+
+def test_kernel_resource_rules():
+    """The build's check of the compiler's kernel-resource-usage remarks: the tuned matrix kernels
+    (hand-counted load waits, two waves per SIMD) and the 1-2 row kernels may not use scratch, and
+    the tuned ones must keep two waves per SIMD; other kernels are only reported."""
+    from routed_experts_bit_amd import build as hb
+
+    def remark(fn, scratch, occ, vgprs=256):
+        loc = "/x/rl_kernels.h:1:1: remark: "
+        tail = " [-Rpass-analysis=kernel-resource-usage]"
+        return "\n".join([loc + f"Function Name: {fn}" + tail, " 1 | __global__ void k() {", "   | ^",
+                          loc + f"    VGPRs: {vgprs}" + tail, loc + f"    ScratchSize [bytes/lane]: {scratch}" + tail,
+                          loc + f"    Occupancy [waves/SIMD]: {occ}" + tail])
+
+    text = "\n".join([
+        remark("_ZN2rl7k_t1_f8ILi0ELi2ELb1EEEvNS_6GuArgsE", 0, 2),
+        remark("_ZN2rl7k_t1_dnENS_6GuArgsE", 0, 2, 226),
+        remark("_ZN2rl9k_gv_downILi2ELi32ELi1ELi256EEEvNS_6GvArgsE", 0, 5, 84),
+        remark("_ZN2rl6k_downILi1ELi256ELi4ELi4EEEvNS_8DownArgsE", 1404, 2),  # untuned path: reported only
+    ])
+    res = hb.kernel_resources(text)
+    assert res["_ZN2rl7k_t1_dnENS_6GuArgsE"] == {"vgprs": 226, "scratch": 0, "occupancy": 2}
+    assert len(res) == 4 and hb.check_resources(res) == []
+    bad = hb.kernel_resources("\n".join([remark("_ZN2rl7k_q2_mmILi0ELi2ELb1EEEvNS_6GuArgsE", 84, 2),
+                                         remark("_ZN2rl7k_t1_f8ILi0ELi2ELb0EEEvNS_6GuArgsE", 0, 1),
+                                         remark("_ZN2rl11k_gv_gateupILi1ELi64ELi2ELi256EEEvNS_6GvArgsE", 8, 4)]))
+    msgs = hb.check_resources(bad)
+    assert len(msgs) == 3 and "84 bytes" in msgs[0] and "1 wave" in msgs[1] and "8 bytes" in msgs[2]
