@@ -2240,12 +2240,18 @@ __global__ __launch_bounds__(NTHR) void k_gv_gateup(GvArgs a) {
     }
 }
 
+// Work-groups per CU the down kernel below is built for: with both block types and one strip of
+// at most 32 values per lane it needs just over 128 VGPRs; held to 128 (four waves per SIMD) a
+// 2-row call's 4,096 waves (H = 2048) are resident at once instead of in two rounds.
+template <int QMASK, int S2, int MAXS>
+constexpr int gv_down_wgs() { return QMASK == 3 && MAXS == 1 && S2 <= 32 ? 4 : 1; }
+
 // One wave per (row r, output column c): lane group gq = lane/16 takes slot j = 4*round + gq,
 // each lane I/16 values of row c of that expert's W_down; after the 16-lane reduction the slot
 // outputs are added to the accumulator in selection order j = 0..k-1.  The weights of all
 // rounds are loaded before the first is decoded.
 template <int QMASK, int S2, int MAXS, int NTHR>
-__global__ __launch_bounds__(NTHR) void k_gv_down(GvArgs a) {
+__global__ __launch_bounds__(NTHR, (gv_down_wgs<QMASK, S2, MAXS>())) void k_gv_down(GvArgs a) {
     constexpr int NW = NTHR / 64;
     __shared__ GvTables<QMASK, true> tb;
     __shared__ GvPair sp[GV_MAX_PAIRS];
